@@ -49,8 +49,12 @@ def _load():
 
 
 def default_threads() -> int:
-    """Host cores this process may run on."""
-    return len(os.sched_getaffinity(0))
+    """Host cores this process may run on, capped by OMP_NUM_THREADS if set."""
+    n = len(os.sched_getaffinity(0))
+    cap = os.environ.get("OMP_NUM_THREADS", "")
+    if cap.isdigit() and int(cap) > 0:
+        n = min(n, int(cap))
+    return n
 
 
 def e2m1_table() -> np.ndarray:

@@ -1,0 +1,36 @@
+"""NVFP4 block-scaled batched GEMV for MI355X (gfx950).
+
+The computation runs in the hand-written HIP kernels of ``libnvfp4_gemv.so``
+(``csrc/nvfp4_gemv.hip``, C ABI in ``include/nvfp4_gemv.h``).  This package
+only marshals arguments to that library; it raises if the library is not
+built and never computes anything on the CPU.
+"""
+from ._binding import (  # noqa: F401
+    EXPORTED,
+    LIB_PATH,
+    NVFP4_GEMV_ERR_ALIAS,
+    NVFP4_GEMV_ERR_ALIGNMENT,
+    NVFP4_GEMV_ERR_BAD_SHAPE,
+    NVFP4_GEMV_ERR_BAD_TUNING,
+    NVFP4_GEMV_ERR_DEVICE,
+    NVFP4_GEMV_ERR_LAUNCH,
+    NVFP4_GEMV_ERR_NULL_POINTER,
+    NVFP4_GEMV_ERR_WORKSPACE,
+    NVFP4_GEMV_OK,
+    NVFP4_GEMV_PATH_AUTO,
+    NVFP4_GEMV_PATH_FAST,
+    NVFP4_GEMV_PATH_GENERIC,
+    Nvfp4GemvError,
+    Tuning,
+    gemv,
+    load,
+    nvfp4_gemv_launch,
+    nvfp4_gemv_launch_ws,
+    nvfp4_gemv_launch_tuned,
+    nvfp4_gemv_num_variants,
+    nvfp4_gemv_plan,
+    nvfp4_gemv_status_string,
+    nvfp4_gemv_variant_info,
+    nvfp4_gemv_workspace_size,
+    nvfp4_hbm_read_probe,
+)

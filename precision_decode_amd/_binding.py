@@ -1,0 +1,212 @@
+"""ctypes binding of ``libnvfp4_gemv.so`` (argument marshalling only).
+
+Each C entry point of ``include/nvfp4_gemv.h`` has a Python function of the
+same name.  Pointer arguments accept a torch tensor (its ``data_ptr()``), a raw
+integer device address, or None where the C side allows NULL; ``stream``
+accepts None (torch's current stream), a ``torch.cuda.Stream`` or a raw
+``hipStream_t`` integer.  A negative status raises :class:`Nvfp4GemvError`.
+All arithmetic happens in the HIP kernels; nothing here falls back to the CPU.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libnvfp4_gemv.so")
+
+NVFP4_GEMV_OK = 0
+NVFP4_GEMV_ERR_NULL_POINTER = -1
+NVFP4_GEMV_ERR_BAD_SHAPE = -2
+NVFP4_GEMV_ERR_WORKSPACE = -3
+NVFP4_GEMV_ERR_LAUNCH = -4
+NVFP4_GEMV_ERR_ALIAS = -5
+NVFP4_GEMV_ERR_ALIGNMENT = -6
+NVFP4_GEMV_ERR_DEVICE = -7
+NVFP4_GEMV_ERR_BAD_TUNING = -8
+
+NVFP4_GEMV_PATH_AUTO = 0
+NVFP4_GEMV_PATH_FAST = 1
+NVFP4_GEMV_PATH_GENERIC = 2
+
+# Every symbol the header declares.
+EXPORTED = (
+    "nvfp4_gemv_status_string",
+    "nvfp4_gemv_launch",
+    "nvfp4_gemv_workspace_size",
+    "nvfp4_gemv_launch_ws",
+    "nvfp4_gemv_num_variants",
+    "nvfp4_gemv_variant_info",
+    "nvfp4_gemv_plan",
+    "nvfp4_gemv_launch_tuned",
+    "nvfp4_hbm_read_probe",
+)
+
+
+class Nvfp4GemvError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: status {status} ({nvfp4_gemv_status_string(status)})")
+
+
+class Tuning(ctypes.Structure):
+    """Mirror of ``nvfp4_gemv_tuning_t``."""
+    _fields_ = [("path", ctypes.c_int32), ("variant", ctypes.c_int32),
+                ("ksplit", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+    def __repr__(self):
+        return f"Tuning(path={self.path}, variant={self.variant}, ksplit={self.ksplit})"
+
+
+_lib = None
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+
+
+def load():
+    """Load the built library; raise if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m precision_decode_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    lib.nvfp4_gemv_status_string.restype = ctypes.c_char_p
+    lib.nvfp4_gemv_status_string.argtypes = [ctypes.c_int]
+    gemv_args = [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64]
+    lib.nvfp4_gemv_launch.restype = ctypes.c_int
+    lib.nvfp4_gemv_launch.argtypes = gemv_args + [_P]
+    lib.nvfp4_gemv_workspace_size.restype = ctypes.c_size_t
+    lib.nvfp4_gemv_workspace_size.argtypes = [_I64, _I64, _I64]
+    lib.nvfp4_gemv_launch_ws.restype = ctypes.c_int
+    lib.nvfp4_gemv_launch_ws.argtypes = gemv_args + [_P, ctypes.c_size_t, _P]
+    lib.nvfp4_gemv_num_variants.restype = ctypes.c_int
+    lib.nvfp4_gemv_num_variants.argtypes = []
+    lib.nvfp4_gemv_variant_info.restype = ctypes.c_int
+    lib.nvfp4_gemv_variant_info.argtypes = [ctypes.c_int] + [ctypes.POINTER(ctypes.c_int32)] * 3
+    lib.nvfp4_gemv_plan.restype = ctypes.c_int
+    lib.nvfp4_gemv_plan.argtypes = [_I64, _I64, _I64, ctypes.c_int, ctypes.POINTER(Tuning),
+                                    ctypes.POINTER(Tuning), ctypes.POINTER(ctypes.c_size_t)]
+    lib.nvfp4_gemv_launch_tuned.restype = ctypes.c_int
+    lib.nvfp4_gemv_launch_tuned.argtypes = gemv_args + [ctypes.POINTER(Tuning), _P, ctypes.c_size_t, _P]
+    lib.nvfp4_hbm_read_probe.restype = ctypes.c_int
+    lib.nvfp4_hbm_read_probe.argtypes = [_P, ctypes.c_size_t, _P, _P]
+    _lib = lib
+    return lib
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    if not getattr(t, "is_cuda", False):
+        raise ValueError("device pointer expected: pass a CUDA/HIP tensor or an integer address")
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(status: int, where: str):
+    if status != NVFP4_GEMV_OK:
+        raise Nvfp4GemvError(status, where)
+
+
+def nvfp4_gemv_status_string(status: int) -> str:
+    return load().nvfp4_gemv_status_string(int(status)).decode()
+
+
+def nvfp4_gemv_launch(A_packed, sfA, x_packed, sfx, alpha, c, l, m, k, stream=None):
+    st = load().nvfp4_gemv_launch(_ptr(A_packed), _ptr(sfA), _ptr(x_packed), _ptr(sfx),
+                                  _ptr(alpha), _ptr(c), l, m, k, _stream(stream))
+    _check(st, "nvfp4_gemv_launch")
+
+
+def nvfp4_gemv_workspace_size(l, m, k) -> int:
+    return int(load().nvfp4_gemv_workspace_size(l, m, k))
+
+
+def nvfp4_gemv_launch_ws(A_packed, sfA, x_packed, sfx, alpha, c, l, m, k, workspace,
+                         workspace_bytes, stream=None):
+    st = load().nvfp4_gemv_launch_ws(_ptr(A_packed), _ptr(sfA), _ptr(x_packed), _ptr(sfx),
+                                     _ptr(alpha), _ptr(c), l, m, k, _ptr(workspace),
+                                     int(workspace_bytes), _stream(stream))
+    _check(st, "nvfp4_gemv_launch_ws")
+
+
+def nvfp4_gemv_num_variants() -> int:
+    return int(load().nvfp4_gemv_num_variants())
+
+
+def nvfp4_gemv_variant_info(v: int):
+    r, u, w = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+    _check(load().nvfp4_gemv_variant_info(v, ctypes.byref(r), ctypes.byref(u), ctypes.byref(w)),
+           "nvfp4_gemv_variant_info")
+    return r.value, u.value, w.value
+
+
+def _tuning(t):
+    if t is None:
+        return None
+    if isinstance(t, Tuning):
+        return ctypes.byref(t)
+    return ctypes.byref(Tuning(int(t.get("path", 0)), int(t.get("variant", 0)),
+                               int(t.get("ksplit", 0)), 0))
+
+
+def nvfp4_gemv_plan(l, m, k, aligned=True, tuning=None):
+    """Returns (Tuning actually used, workspace bytes)."""
+    out = Tuning()
+    ws = ctypes.c_size_t()
+    _check(load().nvfp4_gemv_plan(l, m, k, int(bool(aligned)), _tuning(tuning), ctypes.byref(out),
+                                  ctypes.byref(ws)), "nvfp4_gemv_plan")
+    return out, int(ws.value)
+
+
+def nvfp4_gemv_launch_tuned(A_packed, sfA, x_packed, sfx, alpha, c, l, m, k, tuning, workspace,
+                            workspace_bytes, stream=None):
+    st = load().nvfp4_gemv_launch_tuned(_ptr(A_packed), _ptr(sfA), _ptr(x_packed), _ptr(sfx),
+                                        _ptr(alpha), _ptr(c), l, m, k, _tuning(tuning),
+                                        _ptr(workspace), int(workspace_bytes), _stream(stream))
+    _check(st, "nvfp4_gemv_launch_tuned")
+
+
+def nvfp4_hbm_read_probe(buffer, nbytes, sink, stream=None):
+    _check(load().nvfp4_hbm_read_probe(_ptr(buffer), int(nbytes), _ptr(sink), _stream(stream)),
+           "nvfp4_hbm_read_probe")
+
+
+def gemv(A_packed, sfA, x_packed, sfx, alpha=None, out=None, stream=None):
+    """Tensor-level call: shapes (l,m,k/2), (l,m,k/16), (l,k/2), (l,k/16), (l,).
+
+    Checks dtypes, shapes, contiguity and device, allocates ``out`` (uint16
+    fp16 bits, (l, m)) if not given, and calls :func:`nvfp4_gemv_launch`.
+    """
+    import torch
+
+    if A_packed.dim() != 3:
+        raise ValueError("A_packed must be (l, m, k/2)")
+    l, m, half = A_packed.shape
+    k = 2 * half
+    want = {"A_packed": (A_packed, (l, m, half)), "sfA": (sfA, (l, m, k // 16)),
+            "x_packed": (x_packed, (l, half)), "sfx": (sfx, (l, k // 16))}
+    for name, (t, shape) in want.items():
+        if t.dtype != torch.uint8 or tuple(t.shape) != shape or not t.is_contiguous() or not t.is_cuda:
+            raise ValueError(f"{name} must be a contiguous uint8 device tensor of shape {shape}")
+    if alpha is not None and (alpha.dtype != torch.float32 or tuple(alpha.shape) != (l,)
+                              or not alpha.is_cuda):
+        raise ValueError("alpha must be a float32 device tensor of shape (l,)")
+    if out is None:
+        out = torch.empty((l, m), dtype=torch.uint16, device=A_packed.device)
+    elif (out.dtype not in (torch.uint16, torch.float16, torch.int16) or tuple(out.shape) != (l, m)
+          or not out.is_contiguous() or not out.is_cuda):
+        raise ValueError("out must be a contiguous 16-bit device tensor of shape (l, m)")
+    nvfp4_gemv_launch(A_packed, sfA, x_packed, sfx, alpha, out, l, m, k, stream)
+    return out

@@ -1,0 +1,654 @@
+// NVFP4 block-scaled batched GEMV for MI355X (gfx950, CDNA4).
+//
+//   c[b,r] = f16( f32( alpha[b] * sum_kk e2m1(A[b,r,kk]) e4m3(sfA[b,r,kk/16])
+//                                      * e2m1(x[b,kk])   e4m3(sfx[b,kk/16]) ) )
+//
+// The operation is the NVFP4 batched GEMV of "nvFP4 Batch GEMV算子系列(下)"
+// (section "NVFP4 Batched GEMV 概念阐述"): blocks of 16 K-elements share an FP8
+// E4M3 scale, E2M1 elements are packed two per byte with the even element in
+// the low nibble (as the CuTeDSL bridge page's quantisers pack them).
+//
+// A GEMV reads every weight byte once and does 2 flops per 9/16 byte, so the
+// kernel is bound by HBM bandwidth, not by compute; it uses no MFMA.  Design:
+//
+//  * the workgroup first decodes its K-range of x into x~ = e2m1(x) * e4m3(sfx)
+//    as fp16 in LDS (exact: 2 + 4 significant bits, |x~| <= 2688, smallest
+//    nonzero 2^-10 is a normal fp16), laid out so that each lane's reads are
+//    consecutive across lanes (no bank conflicts);
+//  * each wave streams R rows at once, lanes along K: one 16-byte
+//    non-temporal load per lane per row covers 32 elements (two scale blocks),
+//    a wave instruction reads 1 KiB of one row; U such iterations are kept in
+//    flight per row;
+//  * A is decoded with gfx950's packed E2M1 -> fp16 conversion (2 elements
+//    per instruction, exact), multiplied by x~ with v_dot2_f32_f16 (2 products
+//    per instruction, fp32 accumulate), each 16-element block sum is scaled by
+//    its E4M3 sfA once (fp32 FMA);
+//  * lane partial sums are reduced across the wave; the epilogue is one fp32
+//    multiply by alpha and one fp32 -> fp16 round-to-nearest-even conversion;
+//  * when there are too few rows to fill the GPU, or K is longer than one
+//    workgroup's LDS staging, K is split across workgroups: they write fp32
+//    partial sums to a workspace and a second kernel adds them in split order.
+//
+// Every accumulator starts at +0.0, so an exactly-zero result is +0.  With the
+// integer-coded inputs (E2M1 values times scales 0, 1, 2) every partial sum is
+// a multiple of 1/4 below 2^22 and therefore exact in fp32, whatever the
+// summation order.
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cstddef>
+#include <cstdint>
+#include <map>
+#include <mutex>
+#include <utility>
+
+#include "nvfp4_gemv.h"
+
+namespace {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+constexpr int64_t kIterElems = 2048;    // K elements one wave covers per row per iteration
+constexpr int64_t kMaxChunk = 16384;    // K elements staged in LDS per workgroup (32 KiB)
+constexpr int64_t kMinSplitChunk = 2048;
+constexpr int64_t kTargetGroups = 512;  // workgroups wanted before splitting K
+constexpr int kReduceThreads = 256;
+constexpr int kGenericWaves = 4;
+constexpr int kProbeThreads = 256;
+constexpr int kProbeMaxGroups = 4096;
+
+// ---------------------------------------------------------------- decode
+// Two E2M1 codes (byte SEL of w) -> two fp16, exact.  The scale operand of the
+// gfx950 conversion is a power of two carried in a float; 1.0 leaves values
+// unscaled.
+template <int SEL>
+__device__ __forceinline__ f16x2 e2m1x2_f16(uint32_t w) {
+    return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, SEL);
+}
+
+// Two E4M3 codes (bytes 0 and 1 of w) -> two fp32, exact.
+__device__ __forceinline__ f32x2 e4m3x2_f32(uint32_t w) {
+    return __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w), false);
+}
+
+__device__ __forceinline__ uint32_t bits(f16x2 v) { return __builtin_bit_cast(uint32_t, v); }
+__device__ __forceinline__ f16x2 halves(uint32_t w) { return __builtin_bit_cast(f16x2, w); }
+
+// acc + sum over the 8 codes of `a` of e2m1(code) * x~ (8 fp16 in xq).
+__device__ __forceinline__ float dot8(uint32_t a, u32x4 xq, float acc) {
+    acc = __builtin_amdgcn_fdot2(e2m1x2_f16<0>(a), halves(xq.x), acc, false);
+    acc = __builtin_amdgcn_fdot2(e2m1x2_f16<1>(a), halves(xq.y), acc, false);
+    acc = __builtin_amdgcn_fdot2(e2m1x2_f16<2>(a), halves(xq.z), acc, false);
+    acc = __builtin_amdgcn_fdot2(e2m1x2_f16<3>(a), halves(xq.w), acc, false);
+    return acc;
+}
+
+// One lane's 32 elements (two scale blocks): 16 bytes of A, their two sfA
+// codes in the low half of s2, and x~ for the same 32 positions.
+__device__ __forceinline__ float chunk32(u32x4 a, uint32_t s2, const u32x4 (&xq)[4], float acc) {
+    float b0 = dot8(a.x, xq[0], 0.0f);
+    b0 = dot8(a.y, xq[1], b0);
+    float b1 = dot8(a.z, xq[2], 0.0f);
+    b1 = dot8(a.w, xq[3], b1);
+    const f32x2 s = e4m3x2_f32(s2);
+    acc = __builtin_fmaf(b0, s.x, acc);
+    acc = __builtin_fmaf(b1, s.y, acc);
+    return acc;
+}
+
+// x~ for 32 elements: 16 bytes of x and their two sfx codes -> 32 fp16.
+__device__ __forceinline__ void decode_x32(u32x4 xv, uint32_t s2, u32x4 (&out)[4]) {
+    const f32x2 s = e4m3x2_f32(s2);
+    const _Float16 h0 = static_cast<_Float16>(s.x);
+    const _Float16 h1 = static_cast<_Float16>(s.y);
+    const f16x2 v0 = {h0, h0};
+    const f16x2 v1 = {h1, h1};
+    out[0] = u32x4{bits(e2m1x2_f16<0>(xv.x) * v0), bits(e2m1x2_f16<1>(xv.x) * v0),
+                   bits(e2m1x2_f16<2>(xv.x) * v0), bits(e2m1x2_f16<3>(xv.x) * v0)};
+    out[1] = u32x4{bits(e2m1x2_f16<0>(xv.y) * v0), bits(e2m1x2_f16<1>(xv.y) * v0),
+                   bits(e2m1x2_f16<2>(xv.y) * v0), bits(e2m1x2_f16<3>(xv.y) * v0)};
+    out[2] = u32x4{bits(e2m1x2_f16<0>(xv.z) * v1), bits(e2m1x2_f16<1>(xv.z) * v1),
+                   bits(e2m1x2_f16<2>(xv.z) * v1), bits(e2m1x2_f16<3>(xv.z) * v1)};
+    out[3] = u32x4{bits(e2m1x2_f16<0>(xv.w) * v1), bits(e2m1x2_f16<1>(xv.w) * v1),
+                   bits(e2m1x2_f16<2>(xv.w) * v1), bits(e2m1x2_f16<3>(xv.w) * v1)};
+}
+
+__device__ __forceinline__ u32x4 load_nt16(const uint8_t *p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+}
+__device__ __forceinline__ uint32_t load_nt2(const uint8_t *p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const unsigned short *>(p));
+}
+
+// Butterfly sum over the 64 lanes; every lane ends with the same value.
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int o = kWave / 2; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+    return v;
+}
+
+__device__ __forceinline__ uint16_t f16_bits(float v) {
+    return __builtin_bit_cast(uint16_t, static_cast<_Float16>(v));
+}
+
+// ---------------------------------------------------------------- fast kernel
+// Workgroup = W waves; wave w streams rows rb*W*R + w*R .. +R-1 of batch b over
+// the K-range [split*kchunk, min(k, (split+1)*kchunk)).  blockIdx.x enumerates
+// (split, batch, row block) with the row block fastest.
+//
+// LDS holds x~ of the K-range: for iteration `it` (2048 elements) and lane i,
+// the 32 fp16 of elements it*2048 + 32*i .. +31 sit in four 16-byte slots
+// xs[(it*4 + j)*64 + i], j = 0..3, so a wave's reads of slot j are 1 KiB
+// contiguous.  Slots past the end of K hold zeros.
+template <int R, int U, int W>
+__global__ void __launch_bounds__(W * kWave)
+gemv_fast(const uint8_t *__restrict__ A, const uint8_t *__restrict__ sfA,
+          const uint8_t *__restrict__ x, const uint8_t *__restrict__ sfx,
+          const float *__restrict__ alpha, uint16_t *__restrict__ c,
+          float *__restrict__ part, int64_t l, int64_t m, int64_t k,
+          int64_t kchunk, int64_t row_blocks) {
+    extern __shared__ u32x4 xs[];
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = tid / kWave;
+
+    int64_t g = blockIdx.x;
+    const int64_t rb = g % row_blocks;
+    g /= row_blocks;
+    const int64_t b = g % l;
+    const int64_t split = g / l;
+
+    const int64_t kb0 = split * kchunk;
+    const int64_t klen = (k - kb0 < kchunk) ? (k - kb0) : kchunk;
+    const int nit = static_cast<int>((klen + kIterElems - 1) / kIterElems);
+    const int64_t row0 = rb * (W * R) + wave * R;
+
+    const uint8_t *arow[R];
+    const uint8_t *srow[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int64_t row = (row0 + r < m) ? row0 + r : m - 1;   // rows past m: read row m-1, never written
+        arow[r] = A + (b * m + row) * (k / 2) + kb0 / 2;
+        srow[r] = sfA + (b * m + row) * (k / 16) + kb0 / 16;
+    }
+
+    u32x4 abuf[U][R];
+    uint32_t sbuf[U][R];
+    auto issue = [&](int it, int u) {
+        const int64_t off = static_cast<int64_t>(it) * (kIterElems / 2) + lane * 16;   // byte offset in the K-range
+        const bool ok = (it < nit) && (2 * off < klen);
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            if (ok) {
+                abuf[u][r] = load_nt16(arow[r] + off);
+                sbuf[u][r] = load_nt2(srow[r] + off / 8);
+            } else {
+                abuf[u][r] = u32x4{0u, 0u, 0u, 0u};
+                sbuf[u][r] = 0u;
+            }
+        }
+    };
+
+    // Put the first U iterations of A in flight before staging x~.
+#pragma unroll
+    for (int u = 0; u < U; ++u) issue(u, u);
+
+    const uint8_t *xb = x + b * (k / 2) + kb0 / 2;
+    const uint8_t *sxb = sfx + b * (k / 16) + kb0 / 16;
+    for (int q = tid; q < nit * kWave; q += W * kWave) {
+        const int64_t e = static_cast<int64_t>(q) * 32;
+        u32x4 xv = {0u, 0u, 0u, 0u};
+        uint32_t s2 = 0u;
+        if (e < klen) {
+            xv = *reinterpret_cast<const u32x4 *>(xb + e / 2);
+            s2 = *reinterpret_cast<const unsigned short *>(sxb + e / 16);
+        }
+        u32x4 out[4];
+        decode_x32(xv, s2, out);
+        const int it = q / kWave, i = q % kWave;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) xs[(it * 4 + j) * kWave + i] = out[j];
+    }
+    __syncthreads();
+
+    float acc[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) acc[r] = 0.0f;
+
+    for (int it0 = 0; it0 < nit; it0 += U) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int it = it0 + u;
+            if (it < nit) {
+                u32x4 xq[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) xq[j] = xs[(it * 4 + j) * kWave + lane];
+#pragma unroll
+                for (int r = 0; r < R; ++r) acc[r] = chunk32(abuf[u][r], sbuf[u][r], xq, acc[r]);
+                issue(it + U, u);
+            }
+        }
+    }
+
+    float sum[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) sum[r] = wave_sum(acc[r]);
+
+    if (lane < R) {
+        float v = sum[0];
+#pragma unroll
+        for (int r = 1; r < R; ++r)
+            if (lane == r) v = sum[r];
+        const int64_t row = row0 + lane;
+        if (row < m) {
+            if (part != nullptr) {
+                part[(split * l + b) * m + row] = v;
+            } else {
+                const float al = alpha ? alpha[b] : 1.0f;
+                c[b * m + row] = f16_bits(al * v);
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------- generic kernel
+// Any k % 16 == 0 and any byte alignment of A, sfA, x, sfx.  One wave per
+// (split, batch, row); lanes take 16-element blocks; bytes are loaded singly
+// and x~ is decoded on the fly.
+__device__ __forceinline__ uint32_t load_u32_bytes(const uint8_t *p) {
+    return static_cast<uint32_t>(p[0]) | (static_cast<uint32_t>(p[1]) << 8) |
+           (static_cast<uint32_t>(p[2]) << 16) | (static_cast<uint32_t>(p[3]) << 24);
+}
+
+__device__ __forceinline__ float dot8_generic(uint32_t a, uint32_t xw, f16x2 sx, float acc) {
+    acc = __builtin_amdgcn_fdot2(e2m1x2_f16<0>(a), e2m1x2_f16<0>(xw) * sx, acc, false);
+    acc = __builtin_amdgcn_fdot2(e2m1x2_f16<1>(a), e2m1x2_f16<1>(xw) * sx, acc, false);
+    acc = __builtin_amdgcn_fdot2(e2m1x2_f16<2>(a), e2m1x2_f16<2>(xw) * sx, acc, false);
+    acc = __builtin_amdgcn_fdot2(e2m1x2_f16<3>(a), e2m1x2_f16<3>(xw) * sx, acc, false);
+    return acc;
+}
+
+__global__ void __launch_bounds__(kGenericWaves * kWave)
+gemv_generic(const uint8_t *__restrict__ A, const uint8_t *__restrict__ sfA,
+             const uint8_t *__restrict__ x, const uint8_t *__restrict__ sfx,
+             const float *__restrict__ alpha, uint16_t *__restrict__ c,
+             float *__restrict__ part, int64_t l, int64_t m, int64_t k, int64_t kchunk,
+             int64_t row_blocks) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    int64_t g = blockIdx.x;
+    const int64_t rb = g % row_blocks;
+    g /= row_blocks;
+    const int64_t b = g % l;
+    const int64_t split = g / l;
+    const int64_t row = rb * kGenericWaves + wave;
+    if (row >= m) return;
+
+    const int64_t kb0 = split * kchunk;
+    const int64_t klen = (k - kb0 < kchunk) ? (k - kb0) : kchunk;
+    const uint8_t *arow = A + (b * m + row) * (k / 2) + kb0 / 2;
+    const uint8_t *srow = sfA + (b * m + row) * (k / 16) + kb0 / 16;
+    const uint8_t *xrow = x + b * (k / 2) + kb0 / 2;
+    const uint8_t *sxrow = sfx + b * (k / 16) + kb0 / 16;
+
+    float acc = 0.0f;
+    for (int64_t blk = lane; blk < klen / 16; blk += kWave) {
+        const uint32_t a0 = load_u32_bytes(arow + blk * 8);
+        const uint32_t a1 = load_u32_bytes(arow + blk * 8 + 4);
+        const uint32_t x0 = load_u32_bytes(xrow + blk * 8);
+        const uint32_t x1 = load_u32_bytes(xrow + blk * 8 + 4);
+        const float sa = e4m3x2_f32(srow[blk]).x;
+        const _Float16 hs = static_cast<_Float16>(e4m3x2_f32(sxrow[blk]).x);
+        const f16x2 sx = {hs, hs};
+        float bs = dot8_generic(a0, x0, sx, 0.0f);
+        bs = dot8_generic(a1, x1, sx, bs);
+        acc = __builtin_fmaf(bs, sa, acc);
+    }
+    const float v = wave_sum(acc);
+    if (lane == 0) {
+        if (part != nullptr) {
+            part[(split * l + b) * m + row] = v;
+        } else {
+            const float al = alpha ? alpha[b] : 1.0f;
+            c[b * m + row] = f16_bits(al * v);
+        }
+    }
+}
+
+// ---------------------------------------------------------------- split-K second pass
+// c[i] = f16(alpha * (((0 + p[0][i]) + p[1][i]) + ...)), splits in order.
+__global__ void __launch_bounds__(kReduceThreads)
+gemv_splitk_reduce(const float *__restrict__ part, const float *__restrict__ alpha,
+                   uint16_t *__restrict__ c, int64_t l, int64_t m, int64_t ksplit) {
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * kReduceThreads + threadIdx.x;
+    const int64_t n = l * m;
+    if (i >= n) return;
+    float s = 0.0f;
+    for (int64_t j = 0; j < ksplit; ++j) s += part[j * n + i];
+    const float al = alpha ? alpha[i / m] : 1.0f;
+    c[i] = f16_bits(al * s);
+}
+
+// ---------------------------------------------------------------- read probe
+__global__ void __launch_bounds__(kProbeThreads)
+hbm_read_probe(const uint8_t *__restrict__ buf, int64_t n16, uint32_t *__restrict__ sink) {
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * kProbeThreads;
+    int64_t i = static_cast<int64_t>(blockIdx.x) * kProbeThreads + threadIdx.x;
+    u32x4 acc = {0u, 0u, 0u, 0u};
+    for (; i + 3 * stride < n16; i += 4 * stride) {
+        const u32x4 v0 = load_nt16(buf + i * 16);
+        const u32x4 v1 = load_nt16(buf + (i + stride) * 16);
+        const u32x4 v2 = load_nt16(buf + (i + 2 * stride) * 16);
+        const u32x4 v3 = load_nt16(buf + (i + 3 * stride) * 16);
+        acc ^= v0 ^ v1 ^ v2 ^ v3;
+    }
+    for (; i < n16; i += stride) acc ^= load_nt16(buf + i * 16);
+    uint32_t w = acc.x ^ acc.y ^ acc.z ^ acc.w;
+    for (int o = kWave / 2; o >= 1; o >>= 1) w ^= __shfl_xor(w, o, kWave);
+    if (threadIdx.x == 0) sink[blockIdx.x] = w;
+}
+
+// ---------------------------------------------------------------- host side
+struct Variant {
+    int R, U, W;
+};
+// Index 0 is the default.  Listed as {rows per wave, iterations in flight, waves}.
+constexpr Variant kVariants[] = {
+    {2, 4, 4}, {1, 8, 4}, {1, 4, 4}, {2, 2, 4}, {4, 2, 4},
+    {4, 4, 4}, {2, 4, 8}, {1, 8, 8}, {4, 2, 8}, {2, 2, 8},
+};
+constexpr int kNumVariants = static_cast<int>(sizeof(kVariants) / sizeof(kVariants[0]));
+
+typedef void (*FastKernel)(const uint8_t *, const uint8_t *, const uint8_t *, const uint8_t *,
+                           const float *, uint16_t *, float *, int64_t, int64_t, int64_t,
+                           int64_t, int64_t);
+
+FastKernel fast_kernel(int v) {
+    switch (v) {
+    case 0: return gemv_fast<2, 4, 4>;
+    case 1: return gemv_fast<1, 8, 4>;
+    case 2: return gemv_fast<1, 4, 4>;
+    case 3: return gemv_fast<2, 2, 4>;
+    case 4: return gemv_fast<4, 2, 4>;
+    case 5: return gemv_fast<4, 4, 4>;
+    case 6: return gemv_fast<2, 4, 8>;
+    case 7: return gemv_fast<1, 8, 8>;
+    case 8: return gemv_fast<4, 2, 8>;
+    case 9: return gemv_fast<2, 2, 8>;
+    default: return nullptr;
+    }
+}
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+struct Plan {
+    int path;          // NVFP4_GEMV_PATH_FAST or _GENERIC
+    int variant;       // 0-based fast variant
+    int64_t ksplit;
+    int64_t kchunk;
+    int64_t row_blocks;
+    int64_t groups;
+    int threads;
+    size_t lds_bytes;
+    size_t ws_bytes;
+};
+
+int check_shape(int64_t l, int64_t m, int64_t k) {
+    if (l < 1 || m < 1 || k < 16 || k % 16 != 0) return NVFP4_GEMV_ERR_BAD_SHAPE;
+    if (k >= (int64_t(1) << 31) || l > INT64_MAX / m || l * m >= (int64_t(1) << 31))
+        return NVFP4_GEMV_ERR_BAD_SHAPE;
+    if (l * m > INT64_MAX / (k / 2)) return NVFP4_GEMV_ERR_BAD_SHAPE;
+    return NVFP4_GEMV_OK;
+}
+
+// Resolves the launch plan; shape must already be valid.
+int make_plan(int64_t l, int64_t m, int64_t k, bool aligned, const nvfp4_gemv_tuning_t *t,
+              Plan *p) {
+    nvfp4_gemv_tuning_t tun = {NVFP4_GEMV_PATH_AUTO, 0, 0, 0};
+    if (t) tun = *t;
+    if (tun.reserved != 0 || tun.path < 0 || tun.path > 2 || tun.variant < 0 ||
+        tun.variant > kNumVariants || tun.ksplit < 0)
+        return NVFP4_GEMV_ERR_BAD_TUNING;
+    const bool fast_ok = aligned && (k % 32 == 0);
+    if (tun.path == NVFP4_GEMV_PATH_FAST && !fast_ok) return NVFP4_GEMV_ERR_BAD_TUNING;
+    p->path = (tun.path == NVFP4_GEMV_PATH_GENERIC || !fast_ok) ? NVFP4_GEMV_PATH_GENERIC
+                                                                  : NVFP4_GEMV_PATH_FAST;
+    p->variant = tun.variant > 0 ? tun.variant - 1 : 0;
+
+    int64_t rows_per_group;
+    if (p->path == NVFP4_GEMV_PATH_FAST) {
+        const Variant &v = kVariants[p->variant];
+        rows_per_group = static_cast<int64_t>(v.R) * v.W;
+        p->threads = v.W * kWave;
+    } else {
+        rows_per_group = kGenericWaves;
+        p->threads = kGenericWaves * kWave;
+    }
+    p->row_blocks = ceil_div(m, rows_per_group);
+    const int64_t groups1 = l * p->row_blocks;
+    const int64_t granule = (p->path == NVFP4_GEMV_PATH_FAST) ? 32 : 16;
+
+    int64_t ks;
+    if (tun.ksplit > 0) {
+        ks = tun.ksplit;
+        if (ks > k / granule) return NVFP4_GEMV_ERR_BAD_TUNING;
+    } else {
+        ks = (p->path == NVFP4_GEMV_PATH_FAST) ? ceil_div(k, kMaxChunk) : 1;
+        if (groups1 * ks < kTargetGroups) {
+            const int64_t want = ceil_div(kTargetGroups, groups1);
+            int64_t most = k / kMinSplitChunk;
+            if (most < 1) most = 1;
+            const int64_t pick = want < most ? want : most;
+            if (pick > ks) ks = pick;
+        }
+    }
+    int64_t kchunk = ceil_div(ceil_div(k, ks), granule) * granule;
+    if (p->path == NVFP4_GEMV_PATH_FAST && kchunk > kMaxChunk) {
+        if (tun.ksplit > 0) return NVFP4_GEMV_ERR_BAD_TUNING;
+        kchunk = kMaxChunk;
+    }
+    ks = ceil_div(k, kchunk);
+    p->ksplit = ks;
+    p->kchunk = kchunk;
+    p->groups = groups1 * ks;
+    if (p->groups >= (int64_t(1) << 31)) return NVFP4_GEMV_ERR_BAD_SHAPE;
+    p->lds_bytes = (p->path == NVFP4_GEMV_PATH_FAST)
+                       ? static_cast<size_t>(ceil_div(kchunk, kIterElems)) * 4 * kWave * 16
+                       : 0;
+    p->ws_bytes = ks > 1 ? static_cast<size_t>(ks) * l * m * sizeof(float) : 0;
+    return NVFP4_GEMV_OK;
+}
+
+bool aligned_for_fast(const void *A, const void *sfA, const void *x, const void *sfx) {
+    auto a = [](const void *p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; };
+    return a(A, 16) && a(x, 16) && a(sfA, 2) && a(sfx, 2);
+}
+
+bool overlaps(const void *p, size_t pn, const void *q, size_t qn) {
+    if (!p || !q || pn == 0 || qn == 0) return false;
+    const uintptr_t a = reinterpret_cast<uintptr_t>(p), b = reinterpret_cast<uintptr_t>(q);
+    return a < b + qn && b < a + pn;
+}
+
+int validate(const uint8_t *A, const uint8_t *sfA, const uint8_t *x, const uint8_t *sfx,
+             const float *alpha, uint16_t *c, int64_t l, int64_t m, int64_t k) {
+    if (!A || !sfA || !x || !sfx || !c) return NVFP4_GEMV_ERR_NULL_POINTER;
+    const int s = check_shape(l, m, k);
+    if (s != NVFP4_GEMV_OK) return s;
+    if (reinterpret_cast<uintptr_t>(c) % 2 != 0 || reinterpret_cast<uintptr_t>(alpha) % 4 != 0)
+        return NVFP4_GEMV_ERR_ALIGNMENT;
+    const size_t cn = static_cast<size_t>(l * m) * 2;
+    if (overlaps(c, cn, A, static_cast<size_t>(l * m) * (k / 2)) ||
+        overlaps(c, cn, sfA, static_cast<size_t>(l * m) * (k / 16)) ||
+        overlaps(c, cn, x, static_cast<size_t>(l) * (k / 2)) ||
+        overlaps(c, cn, sfx, static_cast<size_t>(l) * (k / 16)) ||
+        overlaps(c, cn, alpha, static_cast<size_t>(l) * 4))
+        return NVFP4_GEMV_ERR_ALIAS;
+    return NVFP4_GEMV_OK;
+}
+
+int run(const Plan &p, const uint8_t *A, const uint8_t *sfA, const uint8_t *x,
+        const uint8_t *sfx, const float *alpha, uint16_t *c, int64_t l, int64_t m, int64_t k,
+        void *ws, hipStream_t stream) {
+    float *part = p.ksplit > 1 ? static_cast<float *>(ws) : nullptr;
+    int64_t kchunk = p.kchunk, row_blocks = p.row_blocks;
+    void *args[] = {&A, &sfA, &x, &sfx, &alpha, &c, &part, &l, &m, &k, &kchunk, &row_blocks};
+    const void *fn = (p.path == NVFP4_GEMV_PATH_FAST)
+                         ? reinterpret_cast<const void *>(fast_kernel(p.variant))
+                         : reinterpret_cast<const void *>(gemv_generic);
+    hipError_t e = hipLaunchKernel(fn, dim3(static_cast<uint32_t>(p.groups)), dim3(p.threads),
+                                   args, p.lds_bytes, stream);
+    if (e != hipSuccess) return NVFP4_GEMV_ERR_LAUNCH;
+    if (p.ksplit > 1) {
+        const float *cpart = part;
+        int64_t ks = p.ksplit;
+        void *rargs[] = {&cpart, &alpha, &c, &l, &m, &ks};
+        const int64_t n = l * m;
+        e = hipLaunchKernel(reinterpret_cast<const void *>(gemv_splitk_reduce),
+                            dim3(static_cast<uint32_t>(ceil_div(n, kReduceThreads))),
+                            dim3(kReduceThreads), rargs, 0, stream);
+        if (e != hipSuccess) return NVFP4_GEMV_ERR_LAUNCH;
+    }
+    return NVFP4_GEMV_OK;
+}
+
+// Library-owned split-K workspaces, one per (device, stream).
+std::mutex g_ws_mutex;
+std::map<std::pair<int, void *>, std::pair<void *, size_t>> g_ws;
+
+void *owned_workspace(int dev, void *stream, size_t need) {
+    std::lock_guard<std::mutex> lock(g_ws_mutex);
+    auto &slot = g_ws[std::make_pair(dev, stream)];
+    if (slot.second >= need) return slot.first;
+    if (slot.first) {
+        // Earlier work on this stream may still read the old buffer.
+        if (hipStreamSynchronize(static_cast<hipStream_t>(stream)) != hipSuccess) return nullptr;
+        (void)hipFree(slot.first);
+        slot = std::make_pair(nullptr, size_t(0));
+    }
+    void *ptr = nullptr;
+    if (hipMalloc(&ptr, need) != hipSuccess) return nullptr;
+    slot = std::make_pair(ptr, need);
+    return ptr;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *nvfp4_gemv_status_string(int status) {
+    switch (status) {
+    case NVFP4_GEMV_OK: return "ok";
+    case NVFP4_GEMV_ERR_NULL_POINTER: return "a required pointer is NULL";
+    case NVFP4_GEMV_ERR_BAD_SHAPE:
+        return "bad shape: need l, m >= 1, k >= 16, k % 16 == 0, l*m < 2^31, k < 2^31";
+    case NVFP4_GEMV_ERR_WORKSPACE: return "workspace missing, too small or not allocatable";
+    case NVFP4_GEMV_ERR_LAUNCH: return "the HIP runtime rejected a kernel launch";
+    case NVFP4_GEMV_ERR_ALIAS: return "the output c overlaps an input";
+    case NVFP4_GEMV_ERR_ALIGNMENT: return "c must be 2-byte, alpha and workspace 4-byte aligned";
+    case NVFP4_GEMV_ERR_DEVICE: return "no current HIP device";
+    case NVFP4_GEMV_ERR_BAD_TUNING: return "invalid tuning request for this shape";
+    default: return "unknown status";
+    }
+}
+
+int nvfp4_gemv_num_variants(void) { return kNumVariants; }
+
+int nvfp4_gemv_variant_info(int v, int32_t *rows_per_wave, int32_t *iters_in_flight,
+                            int32_t *waves_per_group) {
+    if (v < 1 || v > kNumVariants) return NVFP4_GEMV_ERR_BAD_TUNING;
+    if (!rows_per_wave || !iters_in_flight || !waves_per_group) return NVFP4_GEMV_ERR_NULL_POINTER;
+    *rows_per_wave = kVariants[v - 1].R;
+    *iters_in_flight = kVariants[v - 1].U;
+    *waves_per_group = kVariants[v - 1].W;
+    return NVFP4_GEMV_OK;
+}
+
+int nvfp4_gemv_plan(int64_t l, int64_t m, int64_t k, int aligned, const nvfp4_gemv_tuning_t *in,
+                    nvfp4_gemv_tuning_t *out, size_t *workspace_bytes) {
+    if (!out || !workspace_bytes) return NVFP4_GEMV_ERR_NULL_POINTER;
+    const int s = check_shape(l, m, k);
+    if (s != NVFP4_GEMV_OK) return s;
+    Plan p;
+    const int st = make_plan(l, m, k, aligned != 0, in, &p);
+    if (st != NVFP4_GEMV_OK) return st;
+    out->path = p.path;
+    out->variant = p.path == NVFP4_GEMV_PATH_FAST ? p.variant + 1 : 0;
+    out->ksplit = static_cast<int32_t>(p.ksplit);
+    out->reserved = 0;
+    *workspace_bytes = p.ws_bytes;
+    return NVFP4_GEMV_OK;
+}
+
+size_t nvfp4_gemv_workspace_size(int64_t l, int64_t m, int64_t k) {
+    if (check_shape(l, m, k) != NVFP4_GEMV_OK) return 0;
+    Plan p;
+    if (make_plan(l, m, k, true, nullptr, &p) != NVFP4_GEMV_OK) return 0;
+    return p.ws_bytes;
+}
+
+int nvfp4_gemv_launch_tuned(const uint8_t *A_packed, const uint8_t *sfA, const uint8_t *x_packed,
+                            const uint8_t *sfx, const float *alpha, uint16_t *c, int64_t l,
+                            int64_t m, int64_t k, const nvfp4_gemv_tuning_t *tuning,
+                            void *workspace, size_t workspace_bytes, void *stream) {
+    int s = validate(A_packed, sfA, x_packed, sfx, alpha, c, l, m, k);
+    if (s != NVFP4_GEMV_OK) return s;
+    Plan p;
+    s = make_plan(l, m, k, aligned_for_fast(A_packed, sfA, x_packed, sfx), tuning, &p);
+    if (s != NVFP4_GEMV_OK) return s;
+    if (p.ws_bytes > 0) {
+        if (!workspace || workspace_bytes < p.ws_bytes) return NVFP4_GEMV_ERR_WORKSPACE;
+        if (reinterpret_cast<uintptr_t>(workspace) % 4 != 0) return NVFP4_GEMV_ERR_ALIGNMENT;
+    }
+    return run(p, A_packed, sfA, x_packed, sfx, alpha, c, l, m, k, workspace,
+               static_cast<hipStream_t>(stream));
+}
+
+int nvfp4_gemv_launch_ws(const uint8_t *A_packed, const uint8_t *sfA, const uint8_t *x_packed,
+                         const uint8_t *sfx, const float *alpha, uint16_t *c, int64_t l,
+                         int64_t m, int64_t k, void *workspace, size_t workspace_bytes,
+                         void *stream) {
+    return nvfp4_gemv_launch_tuned(A_packed, sfA, x_packed, sfx, alpha, c, l, m, k, nullptr,
+                                   workspace, workspace_bytes, stream);
+}
+
+int nvfp4_gemv_launch(const uint8_t *A_packed, const uint8_t *sfA, const uint8_t *x_packed,
+                      const uint8_t *sfx, const float *alpha, uint16_t *c, int64_t l, int64_t m,
+                      int64_t k, void *stream) {
+    int s = validate(A_packed, sfA, x_packed, sfx, alpha, c, l, m, k);
+    if (s != NVFP4_GEMV_OK) return s;
+    Plan p;
+    s = make_plan(l, m, k, aligned_for_fast(A_packed, sfA, x_packed, sfx), nullptr, &p);
+    if (s != NVFP4_GEMV_OK) return s;
+    void *ws = nullptr;
+    if (p.ws_bytes > 0) {
+        int dev = -1;
+        if (hipGetDevice(&dev) != hipSuccess) return NVFP4_GEMV_ERR_DEVICE;
+        ws = owned_workspace(dev, stream, p.ws_bytes);
+        if (!ws) return NVFP4_GEMV_ERR_WORKSPACE;
+    }
+    return run(p, A_packed, sfA, x_packed, sfx, alpha, c, l, m, k, ws,
+               static_cast<hipStream_t>(stream));
+}
+
+int nvfp4_hbm_read_probe(const void *buffer, size_t bytes, uint32_t *sink, void *stream) {
+    if (!buffer || !sink) return NVFP4_GEMV_ERR_NULL_POINTER;
+    if (bytes == 0 || bytes % 16 != 0 || bytes > static_cast<size_t>(INT64_MAX))
+        return NVFP4_GEMV_ERR_BAD_SHAPE;
+    if (reinterpret_cast<uintptr_t>(buffer) % 16 != 0 || reinterpret_cast<uintptr_t>(sink) % 4 != 0)
+        return NVFP4_GEMV_ERR_ALIGNMENT;
+    const int64_t n16 = static_cast<int64_t>(bytes / 16);
+    int64_t groups = ceil_div(n16, int64_t(kProbeThreads) * 4);
+    if (groups > kProbeMaxGroups) groups = kProbeMaxGroups;
+    const uint8_t *buf = static_cast<const uint8_t *>(buffer);
+    void *args[] = {&buf, const_cast<int64_t *>(&n16), &sink};
+    hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(hbm_read_probe),
+                                   dim3(static_cast<uint32_t>(groups)), dim3(kProbeThreads), args,
+                                   0, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? NVFP4_GEMV_OK : NVFP4_GEMV_ERR_LAUNCH;
+}
+
+}  // extern "C"

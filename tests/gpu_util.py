@@ -1,0 +1,63 @@
+"""Helpers shared by the GPU tests: move inputs to the device, call the HIP
+library through its C ABI, compare fp16 bit patterns."""
+import numpy as np
+import torch
+
+import precision_decode_amd as pd
+
+
+def to_device(ops):
+    return {k: torch.from_numpy(np.ascontiguousarray(v)).cuda() for k, v in ops.items()}
+
+
+def run_gpu(dops, l, m, k, tuning=None, use_alpha=True, mode="launch", stream=None):
+    """Runs one GEMV on the GPU and returns the fp16 bits as a uint16 numpy array."""
+    c = torch.full((l, m), -1, dtype=torch.int16, device="cuda")   # 0xFFFF: a NaN pattern
+    alpha = dops["alpha"] if use_alpha else None
+    args = (dops["A"], dops["sfA"], dops["x"], dops["sfx"], alpha, c, l, m, k)
+    if mode == "launch" and tuning is None:
+        pd.nvfp4_gemv_launch(*args, stream=stream)
+    else:
+        _, ws_bytes = pd.nvfp4_gemv_plan(l, m, k, aligned=True, tuning=tuning)
+        ws = torch.empty(max(ws_bytes, 4), dtype=torch.uint8, device="cuda")
+        if mode == "ws" and tuning is None:
+            pd.nvfp4_gemv_launch_ws(*args, ws, ws_bytes, stream=stream)
+        else:
+            pd.nvfp4_gemv_launch_tuned(*args, tuning, ws, ws_bytes, stream=stream)
+    torch.cuda.synchronize()
+    return c.cpu().numpy().view(np.uint16)
+
+
+def f16_ordered(bits):
+    """Map fp16 bit patterns to integers whose difference counts ulps."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.int64)
+    mag = b & 0x7FFF
+    return np.where(b & 0x8000, -mag, mag)
+
+
+def assert_bits_equal(got, want, what=""):
+    got = np.asarray(got, dtype=np.uint16)
+    want = np.asarray(want, dtype=np.uint16)
+    gnan = np.isnan(got.view(np.float16))
+    wnan = np.isnan(want.view(np.float16))
+    assert np.array_equal(gnan, wnan), f"{what}: NaN positions differ"
+    diff = (got != want) & ~gnan
+    if diff.any():
+        idx = np.argwhere(diff)[:5]
+        details = [(tuple(i), hex(int(got[tuple(i)])), hex(int(want[tuple(i)]))) for i in idx]
+        raise AssertionError(f"{what}: {int(diff.sum())} of {got.size} outputs differ, e.g. {details}")
+
+
+def assert_within_tolerance(got, want, ulps=2, rel=1e-3, what=""):
+    """|got - want| <= max(ulps fp16 ulps, rel * |want|), NaN where the oracle has NaN."""
+    got = np.asarray(got, dtype=np.uint16)
+    want = np.asarray(want, dtype=np.uint16)
+    g = got.view(np.float16).astype(np.float64)
+    w = want.view(np.float16).astype(np.float64)
+    assert np.array_equal(np.isnan(g), np.isnan(w)), f"{what}: NaN positions differ"
+    fin = ~np.isnan(w)
+    ulp_ok = np.abs(f16_ordered(got) - f16_ordered(want)) <= ulps
+    with np.errstate(invalid="ignore"):
+        rel_ok = np.abs(g - w) <= rel * np.abs(w)
+    ok = ulp_ok | rel_ok | ~fin
+    assert ok.all(), f"{what}: {int((~ok).sum())} outputs outside tolerance"

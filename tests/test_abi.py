@@ -1,0 +1,154 @@
+"""The C-ABI library without a GPU: it loads, exports every symbol the header
+declares, and rejects invalid calls with the documented status before any HIP
+call (only failing calls are made here, so nothing is ever launched)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import precision_decode_amd as pd
+from precision_decode_amd import _binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "nvfp4_gemv.h")
+
+# Fake, never dereferenced device addresses (validation fails before any use).
+A, SA, X, SX, AL, C = 0x10000000, 0x20000000, 0x30000000, 0x40000000, 0x50000000, 0x60000000
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(nvfp4_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_binding.LIB_PATH):
+        from precision_decode_amd import build
+        build.build()
+    return pd.load()
+
+
+def test_header_declares_the_exported_list():
+    assert header_functions() == sorted(_binding.EXPORTED)
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in header_functions():
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", _binding.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (nvfp4_\w+)", out))
+    assert set(header_functions()) <= exported
+
+
+def test_status_strings(lib):
+    for st in range(0, -9, -1):
+        s = pd.nvfp4_gemv_status_string(st)
+        assert s and s != "unknown status"
+    assert pd.nvfp4_gemv_status_string(-99) == "unknown status"
+
+
+def call(l=1, m=8, k=64, a=A, sa=SA, x=X, sx=SX, al=AL, c=C):
+    return pd.load().nvfp4_gemv_launch(a, sa, x, sx, al, c, l, m, k, None)
+
+
+def test_null_pointers(lib):
+    for kw in ("a", "sa", "x", "sx", "c"):
+        assert call(**{kw: None}) == pd.NVFP4_GEMV_ERR_NULL_POINTER
+
+
+@pytest.mark.parametrize("l,m,k", [(0, 8, 64), (1, 0, 64), (1, 8, 0), (1, 8, 8), (1, 8, 40),
+                                   (-1, 8, 64), (1, 8, 1 << 31), (1 << 20, 1 << 12, 64)])
+def test_bad_shapes(lib, l, m, k):
+    assert call(l=l, m=m, k=k) == pd.NVFP4_GEMV_ERR_BAD_SHAPE
+
+
+def test_alias_detected(lib):
+    # c overlapping A's (l*m*k/2)-byte range
+    assert call(c=A + 100) == pd.NVFP4_GEMV_ERR_ALIAS
+    assert call(c=SX) == pd.NVFP4_GEMV_ERR_ALIAS
+    assert call(c=AL - 2) == pd.NVFP4_GEMV_ERR_ALIAS
+
+
+def test_output_and_alpha_alignment(lib):
+    assert call(c=C + 1) == pd.NVFP4_GEMV_ERR_ALIGNMENT
+    assert call(al=AL + 2) == pd.NVFP4_GEMV_ERR_ALIGNMENT
+
+
+def test_workspace_required_before_launch(lib):
+    l, m, k = 1, 64, 16384
+    need = pd.nvfp4_gemv_workspace_size(l, m, k)
+    assert need > 0
+    st = lib.nvfp4_gemv_launch_ws(A, SA, X, SX, AL, C, l, m, k, None, 0, None)
+    assert st == pd.NVFP4_GEMV_ERR_WORKSPACE
+    st = lib.nvfp4_gemv_launch_ws(A, SA, X, SX, AL, C, l, m, k, 0x70000000, need - 4, None)
+    assert st == pd.NVFP4_GEMV_ERR_WORKSPACE
+    st = lib.nvfp4_gemv_launch_ws(A, SA, X, SX, AL, C, l, m, k, 0x70000002, need, None)
+    assert st == pd.NVFP4_GEMV_ERR_ALIGNMENT
+
+
+def test_plan_defaults(lib):
+    t, ws = pd.nvfp4_gemv_plan(1, 7168, 16384)
+    assert t.path == pd.NVFP4_GEMV_PATH_FAST and t.ksplit == 1 and ws == 0
+    t, ws = pd.nvfp4_gemv_plan(1, 896, 16384)            # one eighth of the rows: split K
+    assert t.path == pd.NVFP4_GEMV_PATH_FAST and t.ksplit > 1 and ws == t.ksplit * 896 * 4
+    t, ws = pd.nvfp4_gemv_plan(1, 64, 65536)             # K longer than one LDS stage
+    assert t.ksplit >= 4
+    t, _ = pd.nvfp4_gemv_plan(2, 100, 48)                # k % 32 != 0
+    assert t.path == pd.NVFP4_GEMV_PATH_GENERIC
+    t, _ = pd.nvfp4_gemv_plan(2, 100, 64, aligned=False)
+    assert t.path == pd.NVFP4_GEMV_PATH_GENERIC
+    assert pd.nvfp4_gemv_workspace_size(1, 896, 16384) == pd.nvfp4_gemv_plan(1, 896, 16384)[1]
+
+
+def test_plan_rejects_bad_tuning(lib):
+    with pytest.raises(pd.Nvfp4GemvError) as e:
+        pd.nvfp4_gemv_plan(1, 64, 48, tuning={"path": pd.NVFP4_GEMV_PATH_FAST})
+    assert e.value.status == pd.NVFP4_GEMV_ERR_BAD_TUNING
+    with pytest.raises(pd.Nvfp4GemvError):
+        pd.nvfp4_gemv_plan(1, 64, 64, tuning={"variant": pd.nvfp4_gemv_num_variants() + 1})
+    with pytest.raises(pd.Nvfp4GemvError):
+        pd.nvfp4_gemv_plan(1, 64, 64, tuning={"ksplit": 3})   # 64/3 < one 32-element chunk each
+    with pytest.raises(pd.Nvfp4GemvError):
+        pd.nvfp4_gemv_plan(1, 64, 65536, tuning={"ksplit": 1})  # exceeds one LDS stage
+    t = _binding.Tuning(0, 0, 0, 1)
+    with pytest.raises(pd.Nvfp4GemvError):
+        pd.nvfp4_gemv_plan(1, 64, 64, tuning=t)
+
+
+def test_plan_explicit_choices(lib):
+    for v in range(1, pd.nvfp4_gemv_num_variants() + 1):
+        r, u, w = pd.nvfp4_gemv_variant_info(v)
+        assert r >= 1 and u >= 1 and w in (4, 8)
+        t, _ = pd.nvfp4_gemv_plan(3, 100, 4096, tuning={"variant": v, "ksplit": 2})
+        assert t.variant == v and t.ksplit == 2
+    t, ws = pd.nvfp4_gemv_plan(3, 100, 4096, tuning={"path": pd.NVFP4_GEMV_PATH_GENERIC, "ksplit": 5})
+    assert t.path == pd.NVFP4_GEMV_PATH_GENERIC and t.ksplit == 5 and ws == 5 * 300 * 4
+
+
+def test_probe_validation(lib):
+    assert lib.nvfp4_hbm_read_probe(None, 1024, C, None) == pd.NVFP4_GEMV_ERR_NULL_POINTER
+    assert lib.nvfp4_hbm_read_probe(A, 1000, C, None) == pd.NVFP4_GEMV_ERR_BAD_SHAPE
+    assert lib.nvfp4_hbm_read_probe(A + 8, 1024, C, None) == pd.NVFP4_GEMV_ERR_ALIGNMENT
+
+
+def test_binding_fails_loudly_without_library(monkeypatch):
+    monkeypatch.setattr(_binding, "LIB_PATH", "/nonexistent/libnvfp4_gemv.so")
+    monkeypatch.setattr(_binding, "_lib", None)
+    with pytest.raises(RuntimeError, match="missing"):
+        _binding.load()
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+    with pytest.raises(ValueError):
+        _binding._ptr(torch.zeros(4, dtype=torch.uint8))
+
+
+def test_binding_exports_same_names():
+    for name in _binding.EXPORTED:
+        assert callable(getattr(pd, name))
