@@ -161,7 +161,7 @@ def main(argv=None) -> int:
     warm_gbs = nbytes / (warm_ms / min(args.steps, 500) * 1e-3) / 1e9
     print(f"[bench] cache-resident (same buffers every step): {warm_gbs:.1f} GB/s", flush=True)
 
-    probe_gbs = None
+    probe_gbs = probe_ws_gbs = None
     if not args.no_probe:
         pbytes = 1 << 30
         pbuf = torch.empty(pbytes, dtype=torch.uint8, device="cuda")
@@ -174,6 +174,14 @@ def main(argv=None) -> int:
         probe_gbs = pbytes / (pms / pn * 1e-3) / 1e9
         del pbuf
         print(f"[bench] streaming-read probe (1 GiB): {probe_gbs:.1f} GB/s", flush=True)
+        # the same probe over each copy's A in turn: the achievable read rate
+        # for a read of this workload's size, operands in HBM
+        abytes = replicas[0]["A"].numel()
+        pn = 4 * reps
+        pms, _ = timed(pn, lambda i: pd.nvfp4_hbm_read_probe(replicas[i % reps]["A"], abytes, sink, sptr))
+        probe_ws_gbs = abytes / (pms / pn * 1e-3) / 1e9
+        print(f"[bench] streaming-read probe over A ({abytes / 1e6:.1f} MB, rotated): "
+              f"{probe_ws_gbs:.1f} GB/s", flush=True)
 
     if args.copy_mib:
         src = torch.ones(args.copy_mib << 20, dtype=torch.uint8, device="cuda")
@@ -226,6 +234,7 @@ def main(argv=None) -> int:
                      "frac": round(gbs / HBM_PEAK_GBS, 4),
                      "traffic": traffic,
                      "probe_read_gbs": round(probe_gbs, 2) if probe_gbs else None,
+                     "probe_read_same_size_gbs": round(probe_ws_gbs, 2) if probe_ws_gbs else None,
                      "cache_resident_gbs": round(warm_gbs, 2)},
         "cpu_baseline": cpu,
     }

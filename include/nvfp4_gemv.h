@@ -86,8 +86,9 @@ int nvfp4_gemv_launch(const uint8_t *A_packed, const uint8_t *sfA,
 
 /*
  * Bytes of workspace nvfp4_gemv_launch_ws needs for this shape with the
- * default launch plan (0 when the plan does not split K; then the workspace
- * may be NULL).  Returns 0 for invalid shapes as well.
+ * default launch plan, whatever the alignment of the operands (0 when no plan
+ * splits K; then the workspace may be NULL).  Returns 0 for invalid shapes as
+ * well.
  */
 size_t nvfp4_gemv_workspace_size(int64_t l, int64_t m, int64_t k);
 

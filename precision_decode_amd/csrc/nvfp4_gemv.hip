@@ -123,15 +123,39 @@ __device__ __forceinline__ uint32_t load_nt2(const uint8_t *p) {
     return __builtin_nontemporal_load(reinterpret_cast<const unsigned short *>(p));
 }
 
-// Butterfly sum over the 64 lanes; every lane ends with the same value.
+// Sum over the 64 lanes, the same value in every lane, without LDS: DPP
+// exchanges inside 16-lane rows (neighbour, pair, mirror of 8, mirror of 16),
+// then swaps of 16-lane rows and of 32-lane halves.  Each step adds two values
+// that every lane of a pair adds in the same order, so all lanes agree bit
+// for bit.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL,
+                                                              0xF, 0xF, false));
+}
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int o = kWave / 2; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
-    return v;
+    v += dpp<0xB1>(v);    // quad_perm [1,0,3,2]
+    v += dpp<0x4E>(v);    // quad_perm [2,3,0,1]
+    v += dpp<0x141>(v);   // row_half_mirror
+    v += dpp<0x140>(v);   // row_mirror
+    const unsigned u = __builtin_bit_cast(unsigned, v);
+    const auto r16 = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    v = __builtin_bit_cast(float, static_cast<unsigned>(r16[0])) +
+        __builtin_bit_cast(float, static_cast<unsigned>(r16[1]));
+    const unsigned w = __builtin_bit_cast(unsigned, v);
+    const auto r32 = __builtin_amdgcn_permlane32_swap(w, w, false, false);
+    return __builtin_bit_cast(float, static_cast<unsigned>(r32[0])) +
+           __builtin_bit_cast(float, static_cast<unsigned>(r32[1]));
 }
 
-__device__ __forceinline__ uint16_t f16_bits(float v) {
-    return __builtin_bit_cast(uint16_t, static_cast<_Float16>(v));
+// fp16 bits of f16(f32(al * v)): the product is rounded to fp32 first.  The
+// empty asm keeps that rounding: without it the compiler folds the multiply
+// and the conversion into one mixed-precision FMA that rounds only once, to
+// fp16, which differs on a few outputs.
+__device__ __forceinline__ uint16_t f16_of_product(float al, float v) {
+    float p = al * v;
+    __asm__ volatile("" : "+v"(p));
+    return __builtin_bit_cast(uint16_t, static_cast<_Float16>(p));
 }
 
 // ---------------------------------------------------------------- fast kernel
@@ -142,7 +166,36 @@ __device__ __forceinline__ uint16_t f16_bits(float v) {
 // LDS holds x~ of the K-range: for iteration `it` (2048 elements) and lane i,
 // the 32 fp16 of elements it*2048 + 32*i .. +31 sit in four 16-byte slots
 // xs[(it*4 + j)*64 + i], j = 0..3, so a wave's reads of slot j are 1 KiB
-// contiguous.  Slots past the end of K hold zeros.
+// contiguous.  The iteration count is rounded up to a multiple of U and the
+// slots past the end of K hold zeros.
+//
+// All global reads are buffer loads through a descriptor that covers exactly
+// one row's K-range (or x's): a lane whose offset lies past the end gets
+// zeros from the hardware range check (E2M1 code 0, E4M3 code 0), which
+// contributes +0.  So no load sits under a per-lane branch, the compiler can
+// count outstanding loads, and U iterations of every row stay in flight.
+constexpr int kMaxIters = static_cast<int>(kMaxChunk / kIterElems);   // 8
+
+// Word 3 of a buffer descriptor: 32-bit data format, untyped (raw) access.
+constexpr int kRawBufferFlags = 0x00020000;
+// Cache-policy operand of a buffer load: non-temporal (streamed, read once).
+constexpr int kNonTemporal = 2;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_of(const uint8_t *base, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(base), 0, bytes, kRawBufferFlags);
+}
+
+// Keeps the compiler's scheduler from moving any instruction across this
+// point (the phases below rely on issue order for the load counters).
+__device__ __forceinline__ void phase_fence() { __builtin_amdgcn_sched_barrier(0); }
+
+// Makes a loaded value available here, so its load cannot be sunk into a
+// later branch.
+__device__ __forceinline__ void keep(u32x4 v) {
+    __asm__ volatile("" ::"v"(v.x), "v"(v.y), "v"(v.z), "v"(v.w));
+}
+__device__ __forceinline__ void keep(uint16_t v) { __asm__ volatile("" ::"v"(v)); }
+
 template <int R, int U, int W>
 __global__ void __launch_bounds__(W * kWave)
 gemv_fast(const uint8_t *__restrict__ A, const uint8_t *__restrict__ sfA,
@@ -150,10 +203,12 @@ gemv_fast(const uint8_t *__restrict__ A, const uint8_t *__restrict__ sfA,
           const float *__restrict__ alpha, uint16_t *__restrict__ c,
           float *__restrict__ part, int64_t l, int64_t m, int64_t k,
           int64_t kchunk, int64_t row_blocks) {
+    static_assert(kMaxIters % U == 0, "U must divide the staged iteration count");
+    constexpr int kXPerThread = (kMaxIters + W - 1) / W;   // x chunks of 32 elements per thread
     extern __shared__ u32x4 xs[];
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
-    const int wave = tid / kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
 
     int64_t g = blockIdx.x;
     const int64_t rb = g % row_blocks;
@@ -162,75 +217,95 @@ gemv_fast(const uint8_t *__restrict__ A, const uint8_t *__restrict__ sfA,
     const int64_t split = g / l;
 
     const int64_t kb0 = split * kchunk;
-    const int64_t klen = (k - kb0 < kchunk) ? (k - kb0) : kchunk;
-    const int nit = static_cast<int>((klen + kIterElems - 1) / kIterElems);
+    const int klen = static_cast<int>((k - kb0 < kchunk) ? (k - kb0) : kchunk);
+    const int nit = (klen + static_cast<int>(kIterElems) - 1) / static_cast<int>(kIterElems);
+    const int nstage = (nit + U - 1) / U;
+    const int nslot = nstage * U;
     const int64_t row0 = rb * (W * R) + wave * R;
 
-    const uint8_t *arow[R];
-    const uint8_t *srow[R];
+    // x and its scales for the K-range, issued before the A stream.
+    const __amdgpu_buffer_rsrc_t xbuf = buffer_of(x + b * (k / 2) + kb0 / 2, klen / 2);
+    const __amdgpu_buffer_rsrc_t sxbuf = buffer_of(sfx + b * (k / 16) + kb0 / 16, klen / 16);
+    u32x4 xv[kXPerThread];
+    uint16_t xs2[kXPerThread];
+#pragma unroll
+    for (int i = 0; i < kXPerThread; ++i) {
+        const int q = tid + i * W * kWave;
+        xv[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xbuf, 16 * q, 0, 0));
+        xs2[i] = __builtin_amdgcn_raw_buffer_load_b16(sxbuf, 2 * q, 0, 0);
+    }
+
+    __amdgpu_buffer_rsrc_t abuf_rs[R], sbuf_rs[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
         const int64_t row = (row0 + r < m) ? row0 + r : m - 1;   // rows past m: read row m-1, never written
-        arow[r] = A + (b * m + row) * (k / 2) + kb0 / 2;
-        srow[r] = sfA + (b * m + row) * (k / 16) + kb0 / 16;
+        abuf_rs[r] = buffer_of(A + (b * m + row) * (k / 2) + kb0 / 2, klen / 2);
+        sbuf_rs[r] = buffer_of(sfA + (b * m + row) * (k / 16) + kb0 / 16, klen / 16);
     }
 
     u32x4 abuf[U][R];
-    uint32_t sbuf[U][R];
+    uint16_t sbuf[U][R];   // widened only where used, so no instruction touches it early
     auto issue = [&](int it, int u) {
-        const int64_t off = static_cast<int64_t>(it) * (kIterElems / 2) + lane * 16;   // byte offset in the K-range
-        const bool ok = (it < nit) && (2 * off < klen);
+        const int off = it * static_cast<int>(kIterElems / 2) + lane * 16;
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-            if (ok) {
-                abuf[u][r] = load_nt16(arow[r] + off);
-                sbuf[u][r] = load_nt2(srow[r] + off / 8);
-            } else {
-                abuf[u][r] = u32x4{0u, 0u, 0u, 0u};
-                sbuf[u][r] = 0u;
-            }
+            abuf[u][r] = __builtin_bit_cast(
+                u32x4, __builtin_amdgcn_raw_buffer_load_b128(abuf_rs[r], off, 0, kNonTemporal));
+            sbuf[u][r] = __builtin_amdgcn_raw_buffer_load_b16(sbuf_rs[r], off / 8, 0, kNonTemporal);
         }
     };
-
-    // Put the first U iterations of A in flight before staging x~.
+    auto consume = [&](int it, int u, float (&acc)[R]) {
+        u32x4 xq[4];
 #pragma unroll
-    for (int u = 0; u < U; ++u) issue(u, u);
+        for (int j = 0; j < 4; ++j) xq[j] = xs[(it * 4 + j) * kWave + lane];
+#pragma unroll
+        for (int r = 0; r < R; ++r) acc[r] = chunk32(abuf[u][r], sbuf[u][r], xq, acc[r]);
+    };
 
-    const uint8_t *xb = x + b * (k / 2) + kb0 / 2;
-    const uint8_t *sxb = sfx + b * (k / 16) + kb0 / 16;
-    for (int q = tid; q < nit * kWave; q += W * kWave) {
-        const int64_t e = static_cast<int64_t>(q) * 32;
-        u32x4 xv = {0u, 0u, 0u, 0u};
-        uint32_t s2 = 0u;
-        if (e < klen) {
-            xv = *reinterpret_cast<const u32x4 *>(xb + e / 2);
-            s2 = *reinterpret_cast<const unsigned short *>(sxb + e / 16);
-        }
+    phase_fence();
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        issue(u, u);
+        phase_fence();   // same issue order as the refills in the loop below
+    }
+
+    // Decode the x chunks (waiting only for the x loads, which were issued
+    // first) and store the slots that exist.
+#pragma unroll
+    for (int i = 0; i < kXPerThread; ++i) {
+        keep(xv[i]);
+        keep(xs2[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < kXPerThread; ++i) {
+        const int q = tid + i * W * kWave;
         u32x4 out[4];
-        decode_x32(xv, s2, out);
-        const int it = q / kWave, i = q % kWave;
+        decode_x32(xv[i], xs2[i], out);
+        if (q < nslot * kWave) {
+            const int it = q / kWave, li = q % kWave;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) xs[(it * 4 + j) * kWave + i] = out[j];
+            for (int j = 0; j < 4; ++j) xs[(it * 4 + j) * kWave + li] = out[j];
+        }
     }
     __syncthreads();
+    phase_fence();
 
     float acc[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) acc[r] = 0.0f;
 
-    for (int it0 = 0; it0 < nit; it0 += U) {
+    for (int st = 0; st + 1 < nstage; ++st) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int it = it0 + u;
-            if (it < nit) {
-                u32x4 xq[4];
-#pragma unroll
-                for (int j = 0; j < 4; ++j) xq[j] = xs[(it * 4 + j) * kWave + lane];
-#pragma unroll
-                for (int r = 0; r < R; ++r) acc[r] = chunk32(abuf[u][r], sbuf[u][r], xq, acc[r]);
-                issue(it + U, u);
-            }
+            const int it = st * U + u;
+            consume(it, u, acc);
+            issue(it + U, u);
         }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int it = (nstage - 1) * U + u;
+        if (it < nit) consume(it, u, acc);   // wave-uniform: skip iterations past K
     }
 
     float sum[R];
@@ -248,7 +323,7 @@ gemv_fast(const uint8_t *__restrict__ A, const uint8_t *__restrict__ sfA,
                 part[(split * l + b) * m + row] = v;
             } else {
                 const float al = alpha ? alpha[b] : 1.0f;
-                c[b * m + row] = f16_bits(al * v);
+                c[b * m + row] = f16_of_product(al, v);
             }
         }
     }
@@ -313,7 +388,7 @@ gemv_generic(const uint8_t *__restrict__ A, const uint8_t *__restrict__ sfA,
             part[(split * l + b) * m + row] = v;
         } else {
             const float al = alpha ? alpha[b] : 1.0f;
-            c[b * m + row] = f16_bits(al * v);
+            c[b * m + row] = f16_of_product(al, v);
         }
     }
 }
@@ -329,7 +404,7 @@ gemv_splitk_reduce(const float *__restrict__ part, const float *__restrict__ alp
     float s = 0.0f;
     for (int64_t j = 0; j < ksplit; ++j) s += part[j * n + i];
     const float al = alpha ? alpha[i / m] : 1.0f;
-    c[i] = f16_bits(al * s);
+    c[i] = f16_of_product(al, s);
 }
 
 // ---------------------------------------------------------------- read probe
@@ -338,17 +413,24 @@ hbm_read_probe(const uint8_t *__restrict__ buf, int64_t n16, uint32_t *__restric
     const int64_t stride = static_cast<int64_t>(gridDim.x) * kProbeThreads;
     int64_t i = static_cast<int64_t>(blockIdx.x) * kProbeThreads + threadIdx.x;
     u32x4 acc = {0u, 0u, 0u, 0u};
-    for (; i + 3 * stride < n16; i += 4 * stride) {
-        const u32x4 v0 = load_nt16(buf + i * 16);
-        const u32x4 v1 = load_nt16(buf + (i + stride) * 16);
-        const u32x4 v2 = load_nt16(buf + (i + 2 * stride) * 16);
-        const u32x4 v3 = load_nt16(buf + (i + 3 * stride) * 16);
-        acc ^= v0 ^ v1 ^ v2 ^ v3;
+    for (; i + 7 * stride < n16; i += 8 * stride) {
+        u32x4 v[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] = load_nt16(buf + (i + j * stride) * 16);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc ^= v[j];
     }
     for (; i < n16; i += stride) acc ^= load_nt16(buf + i * 16);
     uint32_t w = acc.x ^ acc.y ^ acc.z ^ acc.w;
     for (int o = kWave / 2; o >= 1; o >>= 1) w ^= __shfl_xor(w, o, kWave);
-    if (threadIdx.x == 0) sink[blockIdx.x] = w;
+    __shared__ uint32_t per_wave[kProbeThreads / kWave];
+    if ((threadIdx.x & (kWave - 1)) == 0) per_wave[threadIdx.x / kWave] = w;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t all = 0u;
+        for (int i = 0; i < kProbeThreads / kWave; ++i) all ^= per_wave[i];
+        sink[blockIdx.x] = all;
+    }
 }
 
 // ---------------------------------------------------------------- host side
@@ -359,6 +441,8 @@ struct Variant {
 constexpr Variant kVariants[] = {
     {2, 4, 4}, {1, 8, 4}, {1, 4, 4}, {2, 2, 4}, {4, 2, 4},
     {4, 4, 4}, {2, 4, 8}, {1, 8, 8}, {4, 2, 8}, {2, 2, 8},
+    {4, 1, 4}, {8, 1, 4}, {8, 2, 4}, {2, 1, 8}, {4, 1, 8},
+    {1, 8, 7}, {1, 8, 14}, {2, 4, 7}, {1, 4, 14},
 };
 constexpr int kNumVariants = static_cast<int>(sizeof(kVariants) / sizeof(kVariants[0]));
 
@@ -378,11 +462,32 @@ FastKernel fast_kernel(int v) {
     case 7: return gemv_fast<1, 8, 8>;
     case 8: return gemv_fast<4, 2, 8>;
     case 9: return gemv_fast<2, 2, 8>;
+    case 10: return gemv_fast<4, 1, 4>;
+    case 11: return gemv_fast<8, 1, 4>;
+    case 12: return gemv_fast<8, 2, 4>;
+    case 13: return gemv_fast<2, 1, 8>;
+    case 14: return gemv_fast<4, 1, 8>;
+    case 15: return gemv_fast<1, 8, 7>;
+    case 16: return gemv_fast<1, 8, 14>;
+    case 17: return gemv_fast<2, 4, 7>;
+    case 18: return gemv_fast<1, 4, 14>;
     default: return nullptr;
     }
 }
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Default fast variant (0-based) by the number of 1 KiB K-iterations per row
+// of one workgroup's K-range: enough iterations in flight to cover the whole
+// row when it is short, more rows per wave when K is short (measured on
+// MI355X over the decode, batched and short-K workloads).
+int default_variant(int64_t k) {
+    const int64_t nit = ceil_div(k < kMaxChunk ? k : kMaxChunk, kIterElems);
+    if (nit >= 6) return 1;    // {1, 8, 4}
+    if (nit >= 3) return 6;    // {2, 4, 8}
+    if (nit == 2) return 3;    // {2, 2, 4}
+    return 10;                 // {4, 1, 4}
+}
 
 struct Plan {
     int path;          // NVFP4_GEMV_PATH_FAST or _GENERIC
@@ -416,7 +521,7 @@ int make_plan(int64_t l, int64_t m, int64_t k, bool aligned, const nvfp4_gemv_tu
     if (tun.path == NVFP4_GEMV_PATH_FAST && !fast_ok) return NVFP4_GEMV_ERR_BAD_TUNING;
     p->path = (tun.path == NVFP4_GEMV_PATH_GENERIC || !fast_ok) ? NVFP4_GEMV_PATH_GENERIC
                                                                   : NVFP4_GEMV_PATH_FAST;
-    p->variant = tun.variant > 0 ? tun.variant - 1 : 0;
+    p->variant = tun.variant > 0 ? tun.variant - 1 : default_variant(k);
 
     int64_t rows_per_group;
     if (p->path == NVFP4_GEMV_PATH_FAST) {
@@ -455,9 +560,13 @@ int make_plan(int64_t l, int64_t m, int64_t k, bool aligned, const nvfp4_gemv_tu
     p->kchunk = kchunk;
     p->groups = groups1 * ks;
     if (p->groups >= (int64_t(1) << 31)) return NVFP4_GEMV_ERR_BAD_SHAPE;
-    p->lds_bytes = (p->path == NVFP4_GEMV_PATH_FAST)
-                       ? static_cast<size_t>(ceil_div(kchunk, kIterElems)) * 4 * kWave * 16
-                       : 0;
+    if (p->path == NVFP4_GEMV_PATH_FAST) {
+        const int64_t u = kVariants[p->variant].U;
+        const int64_t slots = ceil_div(ceil_div(kchunk, kIterElems), u) * u;
+        p->lds_bytes = static_cast<size_t>(slots) * 4 * kWave * 16;
+    } else {
+        p->lds_bytes = 0;
+    }
     p->ws_bytes = ks > 1 ? static_cast<size_t>(ks) * l * m * sizeof(float) : 0;
     return NVFP4_GEMV_OK;
 }
@@ -585,9 +694,12 @@ int nvfp4_gemv_plan(int64_t l, int64_t m, int64_t k, int aligned, const nvfp4_ge
 
 size_t nvfp4_gemv_workspace_size(int64_t l, int64_t m, int64_t k) {
     if (check_shape(l, m, k) != NVFP4_GEMV_OK) return 0;
-    Plan p;
-    if (make_plan(l, m, k, true, nullptr, &p) != NVFP4_GEMV_OK) return 0;
-    return p.ws_bytes;
+    // the larger of the fast and generic plans, so the size holds whatever the
+    // operands' alignment turns out to be
+    Plan fast, generic;
+    if (make_plan(l, m, k, true, nullptr, &fast) != NVFP4_GEMV_OK) return 0;
+    if (make_plan(l, m, k, false, nullptr, &generic) != NVFP4_GEMV_OK) return 0;
+    return fast.ws_bytes > generic.ws_bytes ? fast.ws_bytes : generic.ws_bytes;
 }
 
 int nvfp4_gemv_launch_tuned(const uint8_t *A_packed, const uint8_t *sfA, const uint8_t *x_packed,

@@ -102,7 +102,7 @@ def test_plan_defaults(lib):
     assert t.path == pd.NVFP4_GEMV_PATH_GENERIC
     t, _ = pd.nvfp4_gemv_plan(2, 100, 64, aligned=False)
     assert t.path == pd.NVFP4_GEMV_PATH_GENERIC
-    assert pd.nvfp4_gemv_workspace_size(1, 896, 16384) == pd.nvfp4_gemv_plan(1, 896, 16384)[1]
+    assert pd.nvfp4_gemv_workspace_size(1, 896, 16384) >= pd.nvfp4_gemv_plan(1, 896, 16384)[1]
 
 
 def test_plan_rejects_bad_tuning(lib):
@@ -123,7 +123,7 @@ def test_plan_rejects_bad_tuning(lib):
 def test_plan_explicit_choices(lib):
     for v in range(1, pd.nvfp4_gemv_num_variants() + 1):
         r, u, w = pd.nvfp4_gemv_variant_info(v)
-        assert r >= 1 and u >= 1 and w in (4, 8)
+        assert r >= 1 and u >= 1 and 1 <= w <= 16
         t, _ = pd.nvfp4_gemv_plan(3, 100, 4096, tuning={"variant": v, "ksplit": 2})
         assert t.variant == v and t.ksplit == 2
     t, ws = pd.nvfp4_gemv_plan(3, 100, 4096, tuning={"path": pd.NVFP4_GEMV_PATH_GENERIC, "ksplit": 5})

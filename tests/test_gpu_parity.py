@@ -120,13 +120,15 @@ def test_edge_shapes_default_plan(l, m, k):
 @pytest.mark.parametrize("l,m,k", [(1, 1, 32), (3, 5, 48), (2, 9, 2080), (5, 129, 7168)])
 @pytest.mark.parametrize("ksplit", [1, 3])
 def test_generic_kernel(l, m, k, ksplit):
+    if ksplit > k // 16:
+        pytest.skip("fewer 16-element blocks than splits")
     ops = workloads.integer_coded(l, m, k, seed=7, alpha="uniform")
     want = oracle_out(ops, l, m, k)
     tun = {"path": pd.NVFP4_GEMV_PATH_GENERIC, "ksplit": ksplit}
     assert_bits_equal(run_gpu(to_device(ops), l, m, k, tuning=tun), want, "generic")
 
 
-@pytest.mark.parametrize("variant", range(1, 11))
+@pytest.mark.parametrize("variant", range(1, 20))
 @pytest.mark.parametrize("ksplit", [1, 2, 5])
 def test_every_variant_and_split(variant, ksplit):
     if variant > pd.nvfp4_gemv_num_variants():
