@@ -110,25 +110,27 @@ int nvfp4_gemv_launch_ws(const uint8_t *A_packed, const uint8_t *sfA,
 /* Kernel choice. */
 #define NVFP4_GEMV_PATH_AUTO 0     /* fast kernel when shape and alignment allow */
 #define NVFP4_GEMV_PATH_FAST 1     /* fast kernel; BAD_TUNING if not allowed     */
-#define NVFP4_GEMV_PATH_GENERIC 2  /* generic kernel                             */
+#define NVFP4_GEMV_PATH_GENERIC 2  /* generic kernel (any alignment, k % 32 == 16) */
 
 typedef struct nvfp4_gemv_tuning_t {
-    int32_t path;     /* NVFP4_GEMV_PATH_*                                         */
-    int32_t variant;  /* fast-kernel variant, 0 = default, 1..nvfp4_gemv_num_variants() */
-    int32_t ksplit;   /* K split across workgroups, 0 = default, >= 1 explicit     */
-    int32_t reserved; /* must be 0                                                 */
+    int32_t path;     /* NVFP4_GEMV_PATH_*                                          */
+    int32_t variant;  /* fast-kernel variant, 0 = default, 1..nvfp4_gemv_num_variants();
+                         must be 0 with NVFP4_GEMV_PATH_GENERIC                     */
+    int32_t ksplit;   /* K split across workgroups, 0 = default, >= 1 explicit      */
+    int32_t reserved; /* must be 0                                                  */
 } nvfp4_gemv_tuning_t;
 
-/* Number of fast-kernel variants (rows per wave x iterations in flight). */
+/* Number of fast-kernel variants. */
 int nvfp4_gemv_num_variants(void);
 
 /*
  * Describes fast-kernel variant v (1-based): rows each wave streams at once,
- * 1 KiB K-iterations kept in flight per row, waves per workgroup.  Returns a
+ * 1 KiB K-iterations kept in flight per row, waves per workgroup, and whether
+ * x is staged in LDS as packed codes (1) or as decoded fp16 (0).  Returns a
  * status.
  */
 int nvfp4_gemv_variant_info(int v, int32_t *rows_per_wave, int32_t *iters_in_flight,
-                            int32_t *waves_per_group);
+                            int32_t *waves_per_group, int32_t *packed_x);
 
 /*
  * The plan the library would use: fills `out` with the resolved path, variant

@@ -83,7 +83,7 @@ def load():
     lib.nvfp4_gemv_num_variants.restype = ctypes.c_int
     lib.nvfp4_gemv_num_variants.argtypes = []
     lib.nvfp4_gemv_variant_info.restype = ctypes.c_int
-    lib.nvfp4_gemv_variant_info.argtypes = [ctypes.c_int] + [ctypes.POINTER(ctypes.c_int32)] * 3
+    lib.nvfp4_gemv_variant_info.argtypes = [ctypes.c_int] + [ctypes.POINTER(ctypes.c_int32)] * 4
     lib.nvfp4_gemv_plan.restype = ctypes.c_int
     lib.nvfp4_gemv_plan.argtypes = [_I64, _I64, _I64, ctypes.c_int, ctypes.POINTER(Tuning),
                                     ctypes.POINTER(Tuning), ctypes.POINTER(ctypes.c_size_t)]
@@ -146,10 +146,11 @@ def nvfp4_gemv_num_variants() -> int:
 
 
 def nvfp4_gemv_variant_info(v: int):
-    r, u, w = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
-    _check(load().nvfp4_gemv_variant_info(v, ctypes.byref(r), ctypes.byref(u), ctypes.byref(w)),
-           "nvfp4_gemv_variant_info")
-    return r.value, u.value, w.value
+    """(rows per wave, iterations in flight, waves per group, packed x)."""
+    r, u, w, px = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+    _check(load().nvfp4_gemv_variant_info(v, ctypes.byref(r), ctypes.byref(u), ctypes.byref(w),
+                                          ctypes.byref(px)), "nvfp4_gemv_variant_info")
+    return r.value, u.value, w.value, px.value
 
 
 def _tuning(t):

@@ -119,9 +119,6 @@ __device__ __forceinline__ void decode_x32(u32x4 xv, uint32_t s2, u32x4 (&out)[4
 __device__ __forceinline__ u32x4 load_nt16(const uint8_t *p) {
     return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
 }
-__device__ __forceinline__ uint32_t load_nt2(const uint8_t *p) {
-    return __builtin_nontemporal_load(reinterpret_cast<const unsigned short *>(p));
-}
 
 // Sum over the 64 lanes, the same value in every lane, without LDS: DPP
 // exchanges inside 16-lane rows (neighbour, pair, mirror of 8, mirror of 16),
@@ -329,6 +326,159 @@ gemv_fast(const uint8_t *__restrict__ A, const uint8_t *__restrict__ sfA,
     }
 }
 
+// ---------------------------------------------------------------- packed-x fast kernel
+// The fast kernel with x staged raw: LDS holds x's packed codes (16 bytes per
+// 32 elements) and its scale pairs, about 10 KiB for a 16384-element K-range
+// instead of 32 KiB of fp16 x~, so staging is a copy, LDS reads per step are
+// 18 bytes per lane instead of 64, and LDS no longer limits how many
+// workgroups a compute unit holds.  Each wave decodes x's codes once per step
+// for its R rows and applies the combined scale sA*sx once per 16-element
+// block: Σ e2m1(a)·e2m1(x) over a block is exact, and sA*sx (4 + 4
+// significant bits) is exact, so the fp32 FMA rounds exactly as the fp16-x~
+// kernel does and the results are bit-identical.
+//
+// One lane's 32 elements: block sums of raw E2M1 products, then the scales.
+__device__ __forceinline__ float dot8_raw(uint32_t a, uint32_t xw, float acc) {
+    acc = __builtin_amdgcn_fdot2(e2m1x2_f16<0>(a), e2m1x2_f16<0>(xw), acc, false);
+    acc = __builtin_amdgcn_fdot2(e2m1x2_f16<1>(a), e2m1x2_f16<1>(xw), acc, false);
+    acc = __builtin_amdgcn_fdot2(e2m1x2_f16<2>(a), e2m1x2_f16<2>(xw), acc, false);
+    acc = __builtin_amdgcn_fdot2(e2m1x2_f16<3>(a), e2m1x2_f16<3>(xw), acc, false);
+    return acc;
+}
+__device__ __forceinline__ float chunk32_raw(u32x4 a, uint32_t sa2, u32x4 xr, f32x2 sx, float acc) {
+    float b0 = dot8_raw(a.x, xr.x, 0.0f);
+    b0 = dot8_raw(a.y, xr.y, b0);
+    float b1 = dot8_raw(a.z, xr.z, 0.0f);
+    b1 = dot8_raw(a.w, xr.w, b1);
+    const f32x2 sa = e4m3x2_f32(sa2);
+    acc = __builtin_fmaf(b0, sa.x * sx.x, acc);
+    acc = __builtin_fmaf(b1, sa.y * sx.y, acc);
+    return acc;
+}
+
+template <int R, int U, int W>
+__global__ void __launch_bounds__(W * kWave)
+gemv_fastp(const uint8_t *__restrict__ A, const uint8_t *__restrict__ sfA,
+           const uint8_t *__restrict__ x, const uint8_t *__restrict__ sfx,
+           const float *__restrict__ alpha, uint16_t *__restrict__ c,
+           float *__restrict__ part, int64_t l, int64_t m, int64_t k,
+           int64_t kchunk, int64_t row_blocks) {
+    static_assert(kMaxIters % U == 0, "U must divide the staged iteration count");
+    constexpr int kXPerThread = (kMaxIters + W - 1) / W;   // x chunks of 32 elements per thread
+    // LDS: codes as xr[it*64 + lane] (16 bytes), scale pairs as xsc[it*64 + lane]
+    extern __shared__ u32x4 xr[];
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+
+    int64_t g = blockIdx.x;
+    const int64_t rb = g % row_blocks;
+    g /= row_blocks;
+    const int64_t b = g % l;
+    const int64_t split = g / l;
+
+    const int64_t kb0 = split * kchunk;
+    const int klen = static_cast<int>((k - kb0 < kchunk) ? (k - kb0) : kchunk);
+    const int nit = (klen + static_cast<int>(kIterElems) - 1) / static_cast<int>(kIterElems);
+    const int nstage = (nit + U - 1) / U;
+    const int nslot = nstage * U;
+    uint32_t *xsc = reinterpret_cast<uint32_t *>(xr + nslot * kWave);
+    const int64_t row0 = rb * (W * R) + wave * R;
+
+    const __amdgpu_buffer_rsrc_t xbuf = buffer_of(x + b * (k / 2) + kb0 / 2, klen / 2);
+    const __amdgpu_buffer_rsrc_t sxbuf = buffer_of(sfx + b * (k / 16) + kb0 / 16, klen / 16);
+    u32x4 xv[kXPerThread];
+    uint16_t xs2[kXPerThread];
+#pragma unroll
+    for (int i = 0; i < kXPerThread; ++i) {
+        const int q = tid + i * W * kWave;
+        xv[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xbuf, 16 * q, 0, 0));
+        xs2[i] = __builtin_amdgcn_raw_buffer_load_b16(sxbuf, 2 * q, 0, 0);
+    }
+
+    __amdgpu_buffer_rsrc_t abuf_rs[R], sbuf_rs[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int64_t row = (row0 + r < m) ? row0 + r : m - 1;   // rows past m: read row m-1, never written
+        abuf_rs[r] = buffer_of(A + (b * m + row) * (k / 2) + kb0 / 2, klen / 2);
+        sbuf_rs[r] = buffer_of(sfA + (b * m + row) * (k / 16) + kb0 / 16, klen / 16);
+    }
+
+    u32x4 abuf[U][R];
+    uint16_t sbuf[U][R];
+    auto issue = [&](int it, int u) {
+        const int off = it * static_cast<int>(kIterElems / 2) + lane * 16;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            abuf[u][r] = __builtin_bit_cast(
+                u32x4, __builtin_amdgcn_raw_buffer_load_b128(abuf_rs[r], off, 0, kNonTemporal));
+            sbuf[u][r] = __builtin_amdgcn_raw_buffer_load_b16(sbuf_rs[r], off / 8, 0, kNonTemporal);
+        }
+    };
+    auto consume = [&](int it, int u, float (&acc)[R]) {
+        const u32x4 xq = xr[it * kWave + lane];
+        const f32x2 sx = e4m3x2_f32(xsc[it * kWave + lane]);
+#pragma unroll
+        for (int r = 0; r < R; ++r) acc[r] = chunk32_raw(abuf[u][r], sbuf[u][r], xq, sx, acc[r]);
+    };
+
+    float acc[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) acc[r] = 0.0f;
+
+    // One loop for the whole K-range.  Its first pass only issues loads and
+    // then stages x (waiting only for the x loads, which were issued before
+    // any A), so every pass issues the same loads in the same order and the
+    // load counter waits only for the oldest step.  `first` is 0, taken from
+    // an argument so the compiler cannot peel the first pass off the loop.
+    const int first = static_cast<int>(kchunk >> 62);
+    for (int t = first - U; t < first + nslot; t += U) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int it = t - first + u;
+            if (t >= first && it < nit) consume(it, u, acc);   // wave-uniform, no global memory
+            issue(it + U, u);   // past the K-range: zeros, no traffic
+            phase_fence();
+        }
+#pragma unroll
+        for (int i = 0; i < kXPerThread; ++i) {
+            __asm__ volatile("" : "+v"(xv[i].x), "+v"(xv[i].y), "+v"(xv[i].z), "+v"(xv[i].w),
+                             "+v"(xs2[i]));
+        }
+        if (t == first - U) {
+#pragma unroll
+            for (int i = 0; i < kXPerThread; ++i) {
+                const int q = tid + i * W * kWave;
+                if (q < nslot * kWave) {
+                    xr[q] = xv[i];
+                    xsc[q] = xs2[i];
+                }
+            }
+            __syncthreads();
+        }
+    }
+
+    float sum[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) sum[r] = wave_sum(acc[r]);
+
+    if (lane < R) {
+        float v = sum[0];
+#pragma unroll
+        for (int r = 1; r < R; ++r)
+            if (lane == r) v = sum[r];
+        const int64_t row = row0 + lane;
+        if (row < m) {
+            if (part != nullptr) {
+                part[(split * l + b) * m + row] = v;
+            } else {
+                const float al = alpha ? alpha[b] : 1.0f;
+                c[b * m + row] = f16_of_product(al, v);
+            }
+        }
+    }
+}
+
 // ---------------------------------------------------------------- generic kernel
 // Any k % 16 == 0 and any byte alignment of A, sfA, x, sfx.  One wave per
 // (split, batch, row); lanes take 16-element blocks; bytes are loaded singly
@@ -436,13 +586,14 @@ hbm_read_probe(const uint8_t *__restrict__ buf, int64_t n16, uint32_t *__restric
 // ---------------------------------------------------------------- host side
 struct Variant {
     int R, U, W;
+    bool packed_x;   // x staged raw (gemv_fastp) rather than as fp16 x~ (gemv_fast)
 };
-// Index 0 is the default.  Listed as {rows per wave, iterations in flight, waves}.
+// Listed as {rows per wave, iterations in flight, waves, packed x}.
 constexpr Variant kVariants[] = {
-    {2, 4, 4}, {1, 8, 4}, {1, 4, 4}, {2, 2, 4}, {4, 2, 4},
-    {4, 4, 4}, {2, 4, 8}, {1, 8, 8}, {4, 2, 8}, {2, 2, 8},
-    {4, 1, 4}, {8, 1, 4}, {8, 2, 4}, {2, 1, 8}, {4, 1, 8},
-    {1, 8, 7}, {1, 8, 14}, {2, 4, 7}, {1, 4, 14},
+    {2, 4, 7, false}, {1, 8, 4, false}, {2, 4, 4, false}, {2, 2, 4, false}, {4, 2, 4, false},
+    {2, 4, 8, false}, {1, 8, 8, false}, {4, 1, 4, false}, {2, 1, 8, false}, {1, 4, 4, false},
+    {2, 2, 4, true},  {4, 1, 4, true},  {4, 2, 4, true},  {2, 4, 8, true},  {4, 2, 8, true},
+    {1, 4, 8, true},
 };
 constexpr int kNumVariants = static_cast<int>(sizeof(kVariants) / sizeof(kVariants[0]));
 
@@ -452,25 +603,22 @@ typedef void (*FastKernel)(const uint8_t *, const uint8_t *, const uint8_t *, co
 
 FastKernel fast_kernel(int v) {
     switch (v) {
-    case 0: return gemv_fast<2, 4, 4>;
+    case 0: return gemv_fast<2, 4, 7>;
     case 1: return gemv_fast<1, 8, 4>;
-    case 2: return gemv_fast<1, 4, 4>;
+    case 2: return gemv_fast<2, 4, 4>;
     case 3: return gemv_fast<2, 2, 4>;
     case 4: return gemv_fast<4, 2, 4>;
-    case 5: return gemv_fast<4, 4, 4>;
-    case 6: return gemv_fast<2, 4, 8>;
-    case 7: return gemv_fast<1, 8, 8>;
-    case 8: return gemv_fast<4, 2, 8>;
-    case 9: return gemv_fast<2, 2, 8>;
-    case 10: return gemv_fast<4, 1, 4>;
-    case 11: return gemv_fast<8, 1, 4>;
-    case 12: return gemv_fast<8, 2, 4>;
-    case 13: return gemv_fast<2, 1, 8>;
-    case 14: return gemv_fast<4, 1, 8>;
-    case 15: return gemv_fast<1, 8, 7>;
-    case 16: return gemv_fast<1, 8, 14>;
-    case 17: return gemv_fast<2, 4, 7>;
-    case 18: return gemv_fast<1, 4, 14>;
+    case 5: return gemv_fast<2, 4, 8>;
+    case 6: return gemv_fast<1, 8, 8>;
+    case 7: return gemv_fast<4, 1, 4>;
+    case 8: return gemv_fast<2, 1, 8>;
+    case 9: return gemv_fast<1, 4, 4>;
+    case 10: return gemv_fastp<2, 2, 4>;
+    case 11: return gemv_fastp<4, 1, 4>;
+    case 12: return gemv_fastp<4, 2, 4>;
+    case 13: return gemv_fastp<2, 4, 8>;
+    case 14: return gemv_fastp<4, 2, 8>;
+    case 15: return gemv_fastp<1, 4, 8>;
     default: return nullptr;
     }
 }
@@ -478,23 +626,24 @@ FastKernel fast_kernel(int v) {
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Default fast variant (0-based) by the number of 1 KiB K-iterations per row
-// of one workgroup's K-range: enough iterations in flight to cover the whole
-// row when it is short, more rows per wave when K is short (measured on
-// MI355X over the decode, batched and short-K workloads).
+// of one workgroup's K-range, from MI355X measurements on the decode, batched,
+// Gaussian and short-K workloads: long rows want more rows in flight per
+// workgroup, short rows more rows per wave; with 2 to 5 iterations per row
+// the packed-x kernel's smaller LDS footprint wins.
 int default_variant(int64_t k) {
     const int64_t nit = ceil_div(k < kMaxChunk ? k : kMaxChunk, kIterElems);
-    if (nit >= 6) return 1;    // {1, 8, 4}
-    if (nit >= 3) return 6;    // {2, 4, 8}
-    if (nit == 2) return 3;    // {2, 2, 4}
-    return 10;                 // {4, 1, 4}
+    if (nit >= 6) return 0;    // {2, 4, 7}
+    if (nit >= 3) return 2;    // {2, 4, 4}
+    if (nit == 2) return 11;   // {4, 1, 4} packed x
+    return 7;                  // {4, 1, 4}
 }
 
 struct Plan {
     int path;          // NVFP4_GEMV_PATH_FAST or _GENERIC
-    int variant;       // 0-based fast variant
+    int variant;       // 0-based fast-kernel variant
     int64_t ksplit;
     int64_t kchunk;
-    int64_t row_blocks;
+    int64_t row_blocks;     // row blocks per batch
     int64_t groups;
     int threads;
     size_t lds_bytes;
@@ -509,16 +658,35 @@ int check_shape(int64_t l, int64_t m, int64_t k) {
     return NVFP4_GEMV_OK;
 }
 
+// K split: one LDS stage (16384 elements) per workgroup at most for the fast
+// kernel; an explicit split must leave every split at least one granule (32
+// elements for the fast kernel, 16 for the generic one) and fit one stage.
+int split_k(int64_t k, int64_t ks_req, int64_t ks_auto, int64_t granule, bool staged,
+            int64_t *ks_out, int64_t *kchunk_out) {
+    int64_t ks = ks_req > 0 ? ks_req : ks_auto;
+    if (ks_req > 0 && ks > k / granule) return NVFP4_GEMV_ERR_BAD_TUNING;
+    int64_t kchunk = ceil_div(ceil_div(k, ks), granule) * granule;
+    if (staged && kchunk > kMaxChunk) {
+        if (ks_req > 0) return NVFP4_GEMV_ERR_BAD_TUNING;
+        kchunk = kMaxChunk;
+    }
+    *ks_out = ceil_div(k, kchunk);
+    *kchunk_out = kchunk;
+    return NVFP4_GEMV_OK;
+}
+
 // Resolves the launch plan; shape must already be valid.
 int make_plan(int64_t l, int64_t m, int64_t k, bool aligned, const nvfp4_gemv_tuning_t *t,
               Plan *p) {
     nvfp4_gemv_tuning_t tun = {NVFP4_GEMV_PATH_AUTO, 0, 0, 0};
     if (t) tun = *t;
-    if (tun.reserved != 0 || tun.path < 0 || tun.path > 2 || tun.variant < 0 ||
-        tun.variant > kNumVariants || tun.ksplit < 0)
+    if (tun.reserved != 0 || tun.path < NVFP4_GEMV_PATH_AUTO || tun.path > NVFP4_GEMV_PATH_GENERIC ||
+        tun.variant < 0 || tun.ksplit < 0)
         return NVFP4_GEMV_ERR_BAD_TUNING;
     const bool fast_ok = aligned && (k % 32 == 0);
     if (tun.path == NVFP4_GEMV_PATH_FAST && !fast_ok) return NVFP4_GEMV_ERR_BAD_TUNING;
+    if (tun.path == NVFP4_GEMV_PATH_GENERIC && tun.variant != 0) return NVFP4_GEMV_ERR_BAD_TUNING;
+    if (tun.variant > kNumVariants) return NVFP4_GEMV_ERR_BAD_TUNING;
     p->path = (tun.path == NVFP4_GEMV_PATH_GENERIC || !fast_ok) ? NVFP4_GEMV_PATH_GENERIC
                                                                   : NVFP4_GEMV_PATH_FAST;
     p->variant = tun.variant > 0 ? tun.variant - 1 : default_variant(k);
@@ -529,41 +697,35 @@ int make_plan(int64_t l, int64_t m, int64_t k, bool aligned, const nvfp4_gemv_tu
         rows_per_group = static_cast<int64_t>(v.R) * v.W;
         p->threads = v.W * kWave;
     } else {
+        p->variant = 0;
         rows_per_group = kGenericWaves;
         p->threads = kGenericWaves * kWave;
     }
     p->row_blocks = ceil_div(m, rows_per_group);
     const int64_t groups1 = l * p->row_blocks;
-    const int64_t granule = (p->path == NVFP4_GEMV_PATH_FAST) ? 32 : 16;
+    const bool fast = p->path == NVFP4_GEMV_PATH_FAST;
+    const int64_t granule = fast ? 32 : 16;
 
-    int64_t ks;
-    if (tun.ksplit > 0) {
-        ks = tun.ksplit;
-        if (ks > k / granule) return NVFP4_GEMV_ERR_BAD_TUNING;
-    } else {
-        ks = (p->path == NVFP4_GEMV_PATH_FAST) ? ceil_div(k, kMaxChunk) : 1;
-        if (groups1 * ks < kTargetGroups) {
-            const int64_t want = ceil_div(kTargetGroups, groups1);
-            int64_t most = k / kMinSplitChunk;
-            if (most < 1) most = 1;
-            const int64_t pick = want < most ? want : most;
-            if (pick > ks) ks = pick;
-        }
+    int64_t ks_auto = fast ? ceil_div(k, kMaxChunk) : 1;
+    if (groups1 * ks_auto < kTargetGroups) {
+        const int64_t want = ceil_div(kTargetGroups, groups1);
+        int64_t most = k / kMinSplitChunk;
+        if (most < 1) most = 1;
+        const int64_t pick = want < most ? want : most;
+        if (pick > ks_auto) ks_auto = pick;
     }
-    int64_t kchunk = ceil_div(ceil_div(k, ks), granule) * granule;
-    if (p->path == NVFP4_GEMV_PATH_FAST && kchunk > kMaxChunk) {
-        if (tun.ksplit > 0) return NVFP4_GEMV_ERR_BAD_TUNING;
-        kchunk = kMaxChunk;
-    }
-    ks = ceil_div(k, kchunk);
+    int64_t ks, kchunk;
+    const int st = split_k(k, tun.ksplit, ks_auto, granule, fast, &ks, &kchunk);
+    if (st != NVFP4_GEMV_OK) return st;
     p->ksplit = ks;
     p->kchunk = kchunk;
     p->groups = groups1 * ks;
     if (p->groups >= (int64_t(1) << 31)) return NVFP4_GEMV_ERR_BAD_SHAPE;
-    if (p->path == NVFP4_GEMV_PATH_FAST) {
-        const int64_t u = kVariants[p->variant].U;
-        const int64_t slots = ceil_div(ceil_div(kchunk, kIterElems), u) * u;
-        p->lds_bytes = static_cast<size_t>(slots) * 4 * kWave * 16;
+    if (fast) {
+        const Variant &v = kVariants[p->variant];
+        const int64_t slots = ceil_div(ceil_div(kchunk, kIterElems), v.U) * v.U;
+        // per slot and lane: 64 bytes of fp16 x~, or 16 bytes of codes + 4 of scales
+        p->lds_bytes = static_cast<size_t>(slots) * kWave * (v.packed_x ? 20 : 64);
     } else {
         p->lds_bytes = 0;
     }
@@ -605,9 +767,11 @@ int run(const Plan &p, const uint8_t *A, const uint8_t *sfA, const uint8_t *x,
     float *part = p.ksplit > 1 ? static_cast<float *>(ws) : nullptr;
     int64_t kchunk = p.kchunk, row_blocks = p.row_blocks;
     void *args[] = {&A, &sfA, &x, &sfx, &alpha, &c, &part, &l, &m, &k, &kchunk, &row_blocks};
-    const void *fn = (p.path == NVFP4_GEMV_PATH_FAST)
-                         ? reinterpret_cast<const void *>(fast_kernel(p.variant))
-                         : reinterpret_cast<const void *>(gemv_generic);
+    const void *fn;
+    if (p.path == NVFP4_GEMV_PATH_FAST)
+        fn = reinterpret_cast<const void *>(fast_kernel(p.variant));
+    else
+        fn = reinterpret_cast<const void *>(gemv_generic);
     hipError_t e = hipLaunchKernel(fn, dim3(static_cast<uint32_t>(p.groups)), dim3(p.threads),
                                    args, p.lds_bytes, stream);
     if (e != hipSuccess) return NVFP4_GEMV_ERR_LAUNCH;
@@ -667,12 +831,14 @@ const char *nvfp4_gemv_status_string(int status) {
 int nvfp4_gemv_num_variants(void) { return kNumVariants; }
 
 int nvfp4_gemv_variant_info(int v, int32_t *rows_per_wave, int32_t *iters_in_flight,
-                            int32_t *waves_per_group) {
+                            int32_t *waves_per_group, int32_t *packed_x) {
+    if (!rows_per_wave || !iters_in_flight || !waves_per_group || !packed_x)
+        return NVFP4_GEMV_ERR_NULL_POINTER;
     if (v < 1 || v > kNumVariants) return NVFP4_GEMV_ERR_BAD_TUNING;
-    if (!rows_per_wave || !iters_in_flight || !waves_per_group) return NVFP4_GEMV_ERR_NULL_POINTER;
     *rows_per_wave = kVariants[v - 1].R;
     *iters_in_flight = kVariants[v - 1].U;
     *waves_per_group = kVariants[v - 1].W;
+    *packed_x = kVariants[v - 1].packed_x ? 1 : 0;
     return NVFP4_GEMV_OK;
 }
 
@@ -685,7 +851,7 @@ int nvfp4_gemv_plan(int64_t l, int64_t m, int64_t k, int aligned, const nvfp4_ge
     const int st = make_plan(l, m, k, aligned != 0, in, &p);
     if (st != NVFP4_GEMV_OK) return st;
     out->path = p.path;
-    out->variant = p.path == NVFP4_GEMV_PATH_FAST ? p.variant + 1 : 0;
+    out->variant = p.path == NVFP4_GEMV_PATH_GENERIC ? 0 : p.variant + 1;
     out->ksplit = static_cast<int32_t>(p.ksplit);
     out->reserved = 0;
     *workspace_bytes = p.ws_bytes;
