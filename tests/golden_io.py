@@ -42,3 +42,20 @@ def hand_examples():
                 alpha=np.array([float(alpha)], dtype=np.float32),
                 S=Fraction(S), c=int(c, 16)))
     return out
+
+
+def quant_examples():
+    """Hand-derived one-block quantiser examples: dicts with name, rule, gs,
+    values (float32 (16,)), sf (int) and packed (uint8 (8,))."""
+    out = []
+    with open(os.path.join(GOLDEN, "quant_examples.txt")) as f:
+        for line in f:
+            if line.startswith("#") or not line.strip():
+                continue
+            name, rule, gs, vals, sf, packed = line.split()
+            values = np.array([float(Fraction(v)) if v != "-0" else -0.0 for v in vals.split(",")],
+                              dtype=np.float32)
+            assert len(values) == 16
+            out.append(dict(name=name, rule=rule, gs=np.float32(float(Fraction(gs))), values=values,
+                            sf=int(sf, 16), packed=np.frombuffer(bytes.fromhex(packed), dtype=np.uint8)))
+    return out
