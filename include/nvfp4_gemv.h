@@ -61,6 +61,8 @@ extern "C" {
 #define NVFP4_GEMV_ERR_ALIGNMENT (-6)    /* c, alpha or workspace misaligned     */
 #define NVFP4_GEMV_ERR_DEVICE (-7)       /* no current HIP device                */
 #define NVFP4_GEMV_ERR_BAD_TUNING (-8)   /* invalid nvfp4_gemv_tuning_t field    */
+#define NVFP4_GEMV_ERR_BAD_ARGUMENT (-9) /* an enumerated argument (rounding     */
+                                         /* rule, flag) is out of range          */
 
 /*
  * Returns a static, NUL-terminated description of a status code (never NULL).

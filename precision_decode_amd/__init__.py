@@ -1,7 +1,9 @@
-"""NVFP4 block-scaled batched GEMV for MI355X (gfx950).
+"""NVFP4 block-scaled batched GEMV for MI355X (gfx950), and the BF16 -> NVFP4
+activation quantiser that feeds it.
 
 The computation runs in the hand-written HIP kernels of ``libnvfp4_gemv.so``
-(``csrc/nvfp4_gemv.hip``, C ABI in ``include/nvfp4_gemv.h``).  This package
+(``csrc/*.hip``, C ABI in ``include/nvfp4_gemv.h`` and
+``include/nvfp4_quantize.h``).  This package
 only marshals arguments to that library; it raises if the library is not
 built and never computes anything on the CPU.
 """
@@ -10,6 +12,7 @@ from ._binding import (  # noqa: F401
     LIB_PATH,
     NVFP4_GEMV_ERR_ALIAS,
     NVFP4_GEMV_ERR_ALIGNMENT,
+    NVFP4_GEMV_ERR_BAD_ARGUMENT,
     NVFP4_GEMV_ERR_BAD_SHAPE,
     NVFP4_GEMV_ERR_BAD_TUNING,
     NVFP4_GEMV_ERR_DEVICE,
@@ -20,10 +23,14 @@ from ._binding import (  # noqa: F401
     NVFP4_GEMV_PATH_AUTO,
     NVFP4_GEMV_PATH_FAST,
     NVFP4_GEMV_PATH_GENERIC,
+    NVFP4_ROUND_HALF_STEP,
+    NVFP4_ROUND_NEAREST_EVEN,
+    NVFP4_ROUND_NEAREST_LOWER,
     Nvfp4GemvError,
     Tuning,
     gemv,
     load,
+    nvfp4_gemv_bf16x_launch,
     nvfp4_gemv_launch,
     nvfp4_gemv_launch_ws,
     nvfp4_gemv_launch_tuned,
@@ -33,4 +40,6 @@ from ._binding import (  # noqa: F401
     nvfp4_gemv_variant_info,
     nvfp4_gemv_workspace_size,
     nvfp4_hbm_read_probe,
+    nvfp4_quantize_activation,
+    quantize_activation,
 )

@@ -1,7 +1,7 @@
 """ctypes binding of ``libnvfp4_gemv.so`` (argument marshalling only).
 
-Each C entry point of ``include/nvfp4_gemv.h`` has a Python function of the
-same name.  Pointer arguments accept a torch tensor (its ``data_ptr()``), a raw
+Each C entry point of ``include/nvfp4_gemv.h`` and ``include/nvfp4_quantize.h``
+has a Python function of the same name.  Pointer arguments accept a torch tensor (its ``data_ptr()``), a raw
 integer device address, or None where the C side allows NULL; ``stream``
 accepts None (torch's current stream), a ``torch.cuda.Stream`` or a raw
 ``hipStream_t`` integer.  A negative status raises :class:`Nvfp4GemvError`.
@@ -24,6 +24,11 @@ NVFP4_GEMV_ERR_ALIAS = -5
 NVFP4_GEMV_ERR_ALIGNMENT = -6
 NVFP4_GEMV_ERR_DEVICE = -7
 NVFP4_GEMV_ERR_BAD_TUNING = -8
+NVFP4_GEMV_ERR_BAD_ARGUMENT = -9
+
+NVFP4_ROUND_HALF_STEP = 0
+NVFP4_ROUND_NEAREST_EVEN = 1
+NVFP4_ROUND_NEAREST_LOWER = 2
 
 NVFP4_GEMV_PATH_AUTO = 0
 NVFP4_GEMV_PATH_FAST = 1
@@ -40,6 +45,8 @@ EXPORTED = (
     "nvfp4_gemv_plan",
     "nvfp4_gemv_launch_tuned",
     "nvfp4_hbm_read_probe",
+    "nvfp4_quantize_activation",
+    "nvfp4_gemv_bf16x_launch",
 )
 
 
@@ -91,6 +98,12 @@ def load():
     lib.nvfp4_gemv_launch_tuned.argtypes = gemv_args + [ctypes.POINTER(Tuning), _P, ctypes.c_size_t, _P]
     lib.nvfp4_hbm_read_probe.restype = ctypes.c_int
     lib.nvfp4_hbm_read_probe.argtypes = [_P, ctypes.c_size_t, _P, _P]
+    lib.nvfp4_quantize_activation.restype = ctypes.c_int
+    lib.nvfp4_quantize_activation.argtypes = [_P, _P, ctypes.c_int32, _P, _P, _I64, _I64,
+                                              ctypes.c_int32, _P]
+    lib.nvfp4_gemv_bf16x_launch.restype = ctypes.c_int
+    lib.nvfp4_gemv_bf16x_launch.argtypes = [_P, _P, _P, _P, _P, ctypes.c_int32, _P, _P, _P, _P,
+                                            _I64, _I64, _I64, _P]
     _lib = lib
     return lib
 
@@ -182,6 +195,40 @@ def nvfp4_gemv_launch_tuned(A_packed, sfA, x_packed, sfx, alpha, c, l, m, k, tun
 def nvfp4_hbm_read_probe(buffer, nbytes, sink, stream=None):
     _check(load().nvfp4_hbm_read_probe(_ptr(buffer), int(nbytes), _ptr(sink), _stream(stream)),
            "nvfp4_hbm_read_probe")
+
+
+def nvfp4_quantize_activation(x_bf16, global_scale, scale_per_row, x_packed, sf, rows, d, rule,
+                              stream=None):
+    _check(load().nvfp4_quantize_activation(_ptr(x_bf16), _ptr(global_scale), int(scale_per_row),
+                                            _ptr(x_packed), _ptr(sf), rows, d, int(rule),
+                                            _stream(stream)), "nvfp4_quantize_activation")
+
+
+def nvfp4_gemv_bf16x_launch(A_packed, sfA, A_scale, x_bf16, x_scale, rule, x_packed, sfx, alpha, c,
+                            l, m, k, stream=None):
+    _check(load().nvfp4_gemv_bf16x_launch(_ptr(A_packed), _ptr(sfA), _ptr(A_scale), _ptr(x_bf16),
+                                          _ptr(x_scale), int(rule), _ptr(x_packed), _ptr(sfx),
+                                          _ptr(alpha), _ptr(c), l, m, k, _stream(stream)),
+           "nvfp4_gemv_bf16x_launch")
+
+
+def quantize_activation(x, global_scale, rule=NVFP4_ROUND_HALF_STEP, stream=None):
+    """Tensor-level call: x (rows, d) bfloat16 (or its uint16/int16 bits),
+    global_scale a float32 device tensor of 1 or ``rows`` values.  Returns
+    (packed uint8 (rows, d/2), scales uint8 (rows, d/16))."""
+    import torch
+
+    if x.dim() != 2 or x.element_size() != 2 or not x.is_contiguous() or not x.is_cuda:
+        raise ValueError("x must be a contiguous 2-D 16-bit device tensor (bf16 bits)")
+    rows, d = x.shape
+    if global_scale.dtype != torch.float32 or not global_scale.is_cuda or \
+            global_scale.numel() not in (1, rows):
+        raise ValueError("global_scale must be a float32 device tensor of 1 or rows values")
+    per_row = 1 if (global_scale.numel() == rows and rows > 1) else 0
+    q = torch.empty((rows, d // 2), dtype=torch.uint8, device=x.device)
+    sf = torch.empty((rows, d // 16), dtype=torch.uint8, device=x.device)
+    nvfp4_quantize_activation(x, global_scale, per_row, q, sf, rows, d, rule, stream)
+    return q, sf
 
 
 def gemv(A_packed, sfA, x_packed, sfx, alpha=None, out=None, stream=None):

@@ -1,7 +1,7 @@
 """Ahead-of-time build of the HIP library for gfx950.
 
-``python -m precision_decode_amd.build`` compiles ``csrc/nvfp4_gemv.hip`` with
-hipcc into ``precision_decode_amd/libnvfp4_gemv.so`` (in the source tree, so the
+``python -m precision_decode_amd.build`` compiles the HIP sources under
+``csrc/`` with hipcc into ``precision_decode_amd/libnvfp4_gemv.so`` (in the source tree, so the
 built library travels with the tree).  Packed-FP32 VALU instructions are
 disabled for device code; floating-point contraction is off so every multiply
 and add rounds where the source says it does.
@@ -14,7 +14,7 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-SRC = os.path.join(HERE, "csrc", "nvfp4_gemv.hip")
+SRCS = [os.path.join(HERE, "csrc", n) for n in ("nvfp4_gemv.hip", "nvfp4_quantize.hip")]
 LIB = os.path.join(HERE, "libnvfp4_gemv.so")
 INCLUDE = os.path.join(ROOT, "include")
 ARCH = "gfx950"
@@ -31,7 +31,7 @@ def command(out: str) -> list:
     return [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
             "-ffp-contract=off", "-Wall", "-Wextra",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-            "-I", INCLUDE, SRC, "-o", out]
+            "-I", INCLUDE, *SRCS, "-o", out]
 
 
 def build(verbose: bool = False) -> str:

@@ -824,6 +824,7 @@ const char *nvfp4_gemv_status_string(int status) {
     case NVFP4_GEMV_ERR_ALIGNMENT: return "c must be 2-byte, alpha and workspace 4-byte aligned";
     case NVFP4_GEMV_ERR_DEVICE: return "no current HIP device";
     case NVFP4_GEMV_ERR_BAD_TUNING: return "invalid tuning request for this shape";
+    case NVFP4_GEMV_ERR_BAD_ARGUMENT: return "an enumerated argument (rule, flag) is out of range";
     default: return "unknown status";
     }
 }

@@ -12,16 +12,19 @@ import precision_decode_amd as pd
 from precision_decode_amd import _binding
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "nvfp4_gemv.h")
+HEADERS = [os.path.join(ROOT, "include", n) for n in sorted(os.listdir(os.path.join(ROOT, "include")))
+           if n.endswith(".h")]
 
 # Fake, never dereferenced device addresses (validation fails before any use).
 A, SA, X, SX, AL, C = 0x10000000, 0x20000000, 0x30000000, 0x40000000, 0x50000000, 0x60000000
 
 
 def header_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(nvfp4_\w+)\s*\(", text)))
+    names = set()
+    for h in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"\b(nvfp4_\w+)\s*\(", text))
+    return sorted(names)
 
 
 @pytest.fixture(scope="module")
@@ -46,7 +49,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_status_strings(lib):
-    for st in range(0, -9, -1):
+    for st in range(0, -10, -1):
         s = pd.nvfp4_gemv_status_string(st)
         assert s and s != "unknown status"
     assert pd.nvfp4_gemv_status_string(-99) == "unknown status"
@@ -163,3 +166,55 @@ def test_binding_refuses_host_tensors():
 def test_binding_exports_same_names():
     for name in _binding.EXPORTED:
         assert callable(getattr(pd, name))
+
+
+def test_header_constants_match_binding():
+    for h in HEADERS:
+        for name, val in re.findall(r"#define\s+(NVFP4_\w+)\s+\(?(-?\d+)\)?", open(h).read()):
+            assert getattr(_binding, name) == int(val), name
+
+
+# ---- activation quantiser and the bf16-activation GEMV (validation only)
+
+XB, GS, Q, SF = 0x11000000, 0x12000000, 0x13000000, 0x14000000
+
+
+def qcall(rows=2, d=64, x=XB, gs=GS, per_row=1, q=Q, sf=SF, rule=0):
+    return pd.load().nvfp4_quantize_activation(x, gs, per_row, q, sf, rows, d, rule, None)
+
+
+def test_quantize_validation(lib):
+    for kw in ("x", "gs", "q", "sf"):
+        assert qcall(**{kw: None}) == pd.NVFP4_GEMV_ERR_NULL_POINTER
+    for rule in (-1, 3):
+        assert qcall(rule=rule) == pd.NVFP4_GEMV_ERR_BAD_ARGUMENT
+    assert qcall(per_row=2) == pd.NVFP4_GEMV_ERR_BAD_ARGUMENT
+    for rows, d in ((0, 64), (2, 0), (2, 8), (2, 40), (-1, 64), (1 << 20, 1 << 16)):
+        assert qcall(rows=rows, d=d) == pd.NVFP4_GEMV_ERR_BAD_SHAPE
+    assert qcall(x=XB + 8) == pd.NVFP4_GEMV_ERR_ALIGNMENT
+    assert qcall(q=Q + 4) == pd.NVFP4_GEMV_ERR_ALIGNMENT
+    assert qcall(gs=GS + 2) == pd.NVFP4_GEMV_ERR_ALIGNMENT
+    assert qcall(q=XB + 64) == pd.NVFP4_GEMV_ERR_ALIAS         # inside x's 256 bytes
+    assert qcall(sf=XB + 255) == pd.NVFP4_GEMV_ERR_ALIAS
+    assert qcall(sf=GS + 4) == pd.NVFP4_GEMV_ERR_ALIAS          # per-row scales: 8 bytes
+    assert qcall(sf=Q + 63) == pd.NVFP4_GEMV_ERR_ALIAS          # q holds 64 bytes
+
+
+def bcall(l=2, m=8, k=64, a=A, sa=SA, asc=AL, x=XB, xs=GS, rule=0, q=Q, sf=SF, al=C + 4096, c=C):
+    return pd.load().nvfp4_gemv_bf16x_launch(a, sa, asc, x, xs, rule, q, sf, al, c, l, m, k, None)
+
+
+def test_bf16x_gemv_validation(lib):
+    for kw in ("a", "sa", "x", "xs", "q", "sf", "al", "c"):
+        assert bcall(**{kw: None}) == pd.NVFP4_GEMV_ERR_NULL_POINTER, kw
+    assert bcall(rule=5) == pd.NVFP4_GEMV_ERR_BAD_ARGUMENT
+    for l, m, k in ((0, 8, 64), (2, 0, 64), (2, 8, 40)):
+        assert bcall(l=l, m=m, k=k) == pd.NVFP4_GEMV_ERR_BAD_SHAPE
+    assert bcall(c=C + 1) == pd.NVFP4_GEMV_ERR_ALIGNMENT
+    assert bcall(al=C + 4098) == pd.NVFP4_GEMV_ERR_ALIGNMENT
+    assert bcall(asc=AL + 1) == pd.NVFP4_GEMV_ERR_ALIGNMENT
+    assert bcall(c=A + 10) == pd.NVFP4_GEMV_ERR_ALIAS           # c inside A
+    assert bcall(al=Q + 8) == pd.NVFP4_GEMV_ERR_ALIAS           # alpha inside x_packed
+    assert bcall(c=SF) == pd.NVFP4_GEMV_ERR_ALIAS               # c on sfx
+    assert bcall(q=AL) == pd.NVFP4_GEMV_ERR_ALIAS               # x_packed on A_scale
+    assert bcall(al=GS + 4) == pd.NVFP4_GEMV_ERR_ALIAS          # alpha on x_scale
