@@ -18,7 +18,13 @@ Prints one JSON line:
   cpu_baseline the CPU oracle (plain C, fp64, OpenMP over rows) on the same
                workload on this host's cores
 
+Other paths (--path), each printing its own JSON line of the same form:
+  quantize     the BF16 -> NVFP4 activation quantiser on a bf16 activation
+               batch (--act-config tokens | decode_x)
+  gemv_bf16x   the GEMV fed by a bf16 activation: quantiser + GEMV per step
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config decode]
+                       [--path gemv|quantize|gemv_bf16x]
 """
 from __future__ import annotations
 
@@ -36,8 +42,10 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
-KERNEL_SRC = os.path.join(ROOT, "precision_decode_amd", "csrc", "nvfp4_gemv.hip")
+CSRC = os.path.join(ROOT, "precision_decode_amd", "csrc")
 PROFILES = os.path.join(ROOT, "profiles")
+# counter summaries under profiles/ are valid only for the source they were taken on
+KERNEL_SOURCES = {"gemv_fast": "nvfp4_gemv.hip", "quantize_blocks": "nvfp4_quantize.hip"}
 
 
 def parse_args(argv=None):
@@ -45,8 +53,14 @@ def parse_args(argv=None):
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=2000)
     p.add_argument("--warmup", type=int, default=100)
+    p.add_argument("--path", default="gemv", choices=["gemv", "quantize", "gemv_bf16x"])
     p.add_argument("--config", default="decode",
                    help="integer-coded workload name from workloads.CONFIGS")
+    p.add_argument("--act-config", default="tokens",
+                   help="activation workload of --path quantize (workloads.ACT_CONFIGS)")
+    p.add_argument("--rule", type=int, default=0,
+                   help="E2M1 rounding rule of the quantiser (0 half-step, 1 nearest-even, "
+                        "2 nearest-lower)")
     p.add_argument("--replicas", type=int, default=0,
                    help="device copies of the inputs to rotate over (0: enough for >= 1 GB)")
     p.add_argument("--variant", type=int, default=0, help="fast-kernel variant (0 = default plan)")
@@ -59,23 +73,301 @@ def parse_args(argv=None):
     return p.parse_args(argv)
 
 
-def kernel_source_hash() -> str:
-    with open(KERNEL_SRC, "rb") as f:
+def kernel_source_hash(kernel: str = "gemv_fast") -> str:
+    with open(os.path.join(CSRC, KERNEL_SOURCES[kernel]), "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def recorded_traffic(config: str):
+def recorded_traffic(config: str, kernel: str = "gemv_fast"):
     """HBM bytes per launch from a committed counter summary, if it was taken
     on the current kernel source; otherwise None."""
-    path = os.path.join(PROFILES, f"gemv_fast_{config}_hbm_counters.txt")
+    path = os.path.join(PROFILES, f"{kernel}_{config}_hbm_counters.txt")
     if not os.path.exists(path):
         return None
     text = open(path).read()
     h = re.search(r"^kernel_source_sha256_16:\s*(\w+)", text, re.M)
     t = re.search(r"^hbm_bytes_per_launch:\s*([0-9.eE+]+)", text, re.M)
-    if not h or not t or h.group(1) != kernel_source_hash():
+    if not h or not t or h.group(1) != kernel_source_hash(kernel):
         return None
     return float(t.group(1))
+
+
+class Timer:
+    """HIP events on the launch stream around n back-to-back calls."""
+
+    def __init__(self, torch, stream):
+        self.torch, self.stream = torch, stream
+
+    def __call__(self, n, fn):
+        torch = self.torch
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        start.record(self.stream)
+        for i in range(n):
+            fn(i)
+        end.record(self.stream)
+        torch.cuda.synchronize()
+        return start.elapsed_time(end), time.perf_counter() - t0
+
+
+def replicate(torch, base, nbytes, reps_arg):
+    reps = reps_arg or max(1, -(-1_000_000_000 // nbytes))
+    return [base] + [{n: t.clone() for n, t in base.items()} for _ in range(reps - 1)], reps
+
+
+def run_copies(torch, mib):
+    if mib:
+        src = torch.ones(mib << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(4):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"[bench] ran 4 device copies of {mib} MiB", flush=True)
+
+
+def roofline(gbs, traffic, **extra):
+    r = {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+         "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic}
+    r.update({k: (round(v, 2) if isinstance(v, float) else v) for k, v in extra.items()})
+    return r
+
+
+def common_fields(args, gbs, ms_step, dtype):
+    return {"value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": round(ms_step, 6),
+            "us_per_call": round(ms_step * 1e3, 3),
+            "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2), "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": dtype, "data": "synthetic"}
+
+
+def timed_steps(args, timer, step, nbytes, label):
+    for i in range(args.warmup):
+        step(i)
+    timer.torch.cuda.synchronize()
+    ms_total, wall = timer(args.steps, step)
+    ms_step = ms_total / args.steps
+    gbs = nbytes / (ms_step * 1e-3) / 1e9
+    print(f"[bench] {label}: {args.steps} steps: {ms_step * 1e3:.2f} us/step, {gbs:.1f} GB/s "
+          f"({100 * gbs / HBM_PEAK_GBS:.1f}% of peak), host wall {wall:.3f}s", flush=True)
+    return ms_step, gbs
+
+
+def cpu_time(fn, runs=3):
+    times = []
+    for _ in range(runs):
+        t0 = time.perf_counter()
+        fn()
+        times.append(time.perf_counter() - t0)
+    return statistics.median(times)
+
+
+# ------------------------------------------------------------------------------------ GEMV
+def bench_gemv(args, torch, np, pd, workloads):
+    cfg = workloads.CONFIGS[args.config]
+    if cfg.kind != "integer":
+        print(f"{cfg.name} is not an integer-coded workload; bench it with an integer config",
+              file=sys.stderr)
+        return None
+    l, m, k = cfg.l, cfg.m, cfg.k
+    nbytes = cfg.bytes_moved
+    print(f"[bench] workload {cfg.name}: l={l} m={m} k={k}, {nbytes} bytes per step", flush=True)
+
+    ops = workloads.for_config(cfg)
+    base = {n: torch.from_numpy(np.ascontiguousarray(v)).cuda() for n, v in ops.items()}
+    replicas, reps = replicate(torch, base, nbytes, args.replicas)
+    c = torch.empty((l, m), dtype=torch.int16, device="cuda")
+    stream = torch.cuda.current_stream()
+    sptr = stream.cuda_stream
+    timer = Timer(torch, stream)
+
+    tuned = args.variant or args.ksplit
+    tuning = {"variant": args.variant, "ksplit": args.ksplit}
+    plan, ws_bytes = pd.nvfp4_gemv_plan(l, m, k, aligned=True, tuning=tuning if tuned else None)
+    ws = torch.empty(max(ws_bytes, 4), dtype=torch.uint8, device="cuda")
+
+    def step(i):
+        r = replicas[i % reps]
+        if tuned:
+            pd.nvfp4_gemv_launch_tuned(r["A"], r["sfA"], r["x"], r["sfx"], r["alpha"], c, l, m, k,
+                                       tuning, ws, ws_bytes, sptr)
+        else:
+            pd.nvfp4_gemv_launch(r["A"], r["sfA"], r["x"], r["sfx"], r["alpha"], c, l, m, k, sptr)
+
+    print(f"[bench] plan path={plan.path} variant={plan.variant} ksplit={plan.ksplit}; "
+          f"{reps} replicas ({reps * nbytes / 1e9:.2f} GB)", flush=True)
+    ms_step, gbs = timed_steps(args, timer, step, nbytes, "gemv")
+
+    nw = min(args.steps, 500)
+    warm_ms, _ = timer(nw, lambda i: step(0))
+    warm_gbs = nbytes / (warm_ms / nw * 1e-3) / 1e9
+    print(f"[bench] cache-resident (same buffers every step): {warm_gbs:.1f} GB/s", flush=True)
+
+    probe_gbs = probe_ws_gbs = None
+    if not args.no_probe:
+        pbytes = 1 << 30
+        pbuf = torch.empty(pbytes, dtype=torch.uint8, device="cuda")
+        pbuf.fill_(1)
+        sink = torch.empty(4096, dtype=torch.int32, device="cuda")
+        for _ in range(3):
+            pd.nvfp4_hbm_read_probe(pbuf, pbytes, sink, sptr)
+        pn = 20
+        pms, _ = timer(pn, lambda i: pd.nvfp4_hbm_read_probe(pbuf, pbytes, sink, sptr))
+        probe_gbs = pbytes / (pms / pn * 1e-3) / 1e9
+        del pbuf
+        print(f"[bench] streaming-read probe (1 GiB): {probe_gbs:.1f} GB/s", flush=True)
+        # the same probe over each copy's A in turn: the achievable read rate
+        # for a read of this workload's size, operands in HBM
+        abytes = replicas[0]["A"].numel()
+        pn = 4 * reps
+        pms, _ = timer(pn, lambda i: pd.nvfp4_hbm_read_probe(replicas[i % reps]["A"], abytes, sink,
+                                                             sptr))
+        probe_ws_gbs = abytes / (pms / pn * 1e-3) / 1e9
+        print(f"[bench] streaming-read probe over A ({abytes / 1e6:.1f} MB, rotated): "
+              f"{probe_ws_gbs:.1f} GB/s", flush=True)
+
+    run_copies(torch, args.copy_mib)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        from oracle import reference as ref
+
+        threads = ref.default_threads()
+        t_med = cpu_time(lambda: ref.gemv(ops["A"], ops["sfA"], ops["x"], ops["sfx"], ops["alpha"],
+                                          l, m, k, nthreads=threads))
+        cpu = {"value": round(nbytes / t_med / 1e9, 4), "unit": "GB/s", "cores": threads,
+               "kind": "oracle",
+               "sample": f"the whole {cfg.name} workload (l={l}, m={m}, k={k}), median of 3 runs "
+                         f"of {t_med:.3f}s, fp64 sums + fp32/fp16 epilogue, inputs in host memory"}
+        print(f"[bench] CPU oracle: {t_med:.3f}s per GEMV on {threads} threads", flush=True)
+
+    out = {"metric": "achieved HBM GB/s for the NVFP4 block-scaled batched GEMV (us/call and % of "
+                     "MI355X peak alongside)"}
+    out.update(common_fields(args, gbs, ms_step, "f32"))
+    out["config"] = {"workload": f"{cfg.name}: NVFP4 GEMV l={l} m={m} k={k}, integer-coded, "
+                                 f"alpha=1 ({cfg.note})",
+                     "l": l, "m": m, "k": k, "bytes_per_step": nbytes,
+                     "replicas": reps, "operands": "HBM (rotated over >= 1 GB of copies)",
+                     "plan": {"path": plan.path, "variant": plan.variant, "ksplit": plan.ksplit}}
+    out["roofline"] = roofline(gbs, recorded_traffic(cfg.name), probe_read_gbs=probe_gbs,
+                               probe_read_same_size_gbs=probe_ws_gbs, cache_resident_gbs=warm_gbs)
+    out["cpu_baseline"] = cpu
+    return out
+
+
+# ------------------------------------------------------------------------------ quantiser
+def bench_quantize(args, torch, np, pd, workloads):
+    cfg = workloads.ACT_CONFIGS[args.act_config]
+    rows, d = cfg.rows, cfg.d
+    nbytes = cfg.bytes_moved
+    print(f"[bench] activation workload {cfg.name}: rows={rows} d={d}, {nbytes} bytes per step, "
+          f"rule {args.rule}", flush=True)
+    vals = workloads.activation_bf16(cfg)
+    # the global scale a warm-up pass would cache: amax / (6 * 448) per row
+    gs = (np.maximum(np.abs(vals).max(axis=1), np.float32(1e-8)) / np.float32(2688.0)).astype(np.float32)
+    base = {"x": torch.from_numpy(workloads.bf16_bits(vals).view(np.int16)).cuda(),
+            "gs": torch.from_numpy(gs).cuda(),
+            "q": torch.empty((rows, d // 2), dtype=torch.uint8, device="cuda"),
+            "sf": torch.empty((rows, d // 16), dtype=torch.uint8, device="cuda")}
+    replicas, reps = replicate(torch, base, nbytes, args.replicas)
+    stream = torch.cuda.current_stream()
+    sptr = stream.cuda_stream
+    timer = Timer(torch, stream)
+
+    def step(i):
+        r = replicas[i % reps]
+        pd.nvfp4_quantize_activation(r["x"], r["gs"], 1 if rows > 1 else 0, r["q"], r["sf"], rows, d,
+                                     args.rule, sptr)
+
+    print(f"[bench] {reps} replicas ({reps * nbytes / 1e9:.2f} GB)", flush=True)
+    ms_step, gbs = timed_steps(args, timer, step, nbytes, "quantize")
+    run_copies(torch, args.copy_mib)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        from oracle import quantize as oq
+
+        sample = min(rows, 256)
+        with np.errstate(all="ignore"):
+            t_med = cpu_time(lambda: oq.quantize_with_scale(vals[:sample], gs[:sample], args.rule))
+        sbytes = nbytes * sample / rows
+        cpu = {"value": round(sbytes / t_med / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+               "sample": f"{sample} of the {rows} rows (d={d}), median of 3 runs of {t_med:.3f}s, "
+                         f"numpy fp32 steps, one thread"}
+        print(f"[bench] CPU oracle: {t_med:.3f}s for {sample} rows", flush=True)
+
+    out = {"metric": "achieved HBM GB/s of the BF16 -> NVFP4 activation quantiser (us/call alongside)"}
+    out.update(common_fields(args, gbs, ms_step, "f32"))
+    out["config"] = {"workload": f"{cfg.name}: quantise rows={rows} d={d} bf16 N(0,1), per-row "
+                                 f"global scale, rule {args.rule} ({cfg.note})",
+                     "rows": rows, "d": d, "rule": args.rule, "bytes_per_step": nbytes,
+                     "replicas": reps, "operands": "HBM (rotated over >= 1 GB of copies)"}
+    out["roofline"] = roofline(gbs, recorded_traffic(cfg.name, "quantize_blocks"))
+    out["cpu_baseline"] = cpu
+    return out
+
+
+# ------------------------------------------------------------- GEMV fed by a bf16 activation
+def bench_bf16x(args, torch, np, pd, workloads):
+    cfg = workloads.CONFIGS[args.config]
+    if cfg.kind != "integer":
+        print(f"{cfg.name} is not an integer-coded workload", file=sys.stderr)
+        return None
+    l, m, k = cfg.l, cfg.m, cfg.k
+    # A + sfA + bf16 x in; c, the quantised x, its scales and alpha out
+    nbytes = l * m * k // 2 + l * m * k // 16 + 2 * l * k + 2 * l * m + l * k // 2 + l * k // 16 + 8 * l
+    print(f"[bench] workload {cfg.name} with a bf16 activation: l={l} m={m} k={k}, {nbytes} bytes "
+          f"per step, rule {args.rule}", flush=True)
+    ops = workloads.for_config(cfg)
+    xv = workloads.gaussian_bf16(l, 1, k, seed=cfg.seed + 1)["x"]
+    xs = (np.maximum(np.abs(xv).max(axis=1), np.float32(1e-8)) / np.float32(2688.0)).astype(np.float32)
+    base = {"A": torch.from_numpy(ops["A"]).cuda(), "sfA": torch.from_numpy(ops["sfA"]).cuda(),
+            "x": torch.from_numpy(workloads.bf16_bits(xv).view(np.int16)).cuda(),
+            "xs": torch.from_numpy(xs).cuda(),
+            "xq": torch.empty((l, k // 2), dtype=torch.uint8, device="cuda"),
+            "sfx": torch.empty((l, k // 16), dtype=torch.uint8, device="cuda"),
+            "alpha": torch.empty(l, dtype=torch.float32, device="cuda")}
+    replicas, reps = replicate(torch, base, nbytes, args.replicas)
+    c = torch.empty((l, m), dtype=torch.int16, device="cuda")
+    stream = torch.cuda.current_stream()
+    sptr = stream.cuda_stream
+    timer = Timer(torch, stream)
+
+    def step(i):
+        r = replicas[i % reps]
+        pd.nvfp4_gemv_bf16x_launch(r["A"], r["sfA"], None, r["x"], r["xs"], args.rule, r["xq"],
+                                   r["sfx"], r["alpha"], c, l, m, k, sptr)
+
+    print(f"[bench] {reps} replicas ({reps * nbytes / 1e9:.2f} GB)", flush=True)
+    ms_step, gbs = timed_steps(args, timer, step, nbytes, "gemv_bf16x")
+    run_copies(torch, args.copy_mib)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        from oracle import quantize as oq
+        from oracle import reference as ref
+
+        threads = ref.default_threads()
+        with np.errstate(all="ignore"):
+            t_med = cpu_time(lambda: oq.activation_gemv(ops["A"], ops["sfA"], None, xv, xs, args.rule,
+                                                        l, m, k))
+        cpu = {"value": round(nbytes / t_med / 1e9, 4), "unit": "GB/s", "cores": threads,
+               "kind": "oracle",
+               "sample": f"the whole {cfg.name} workload with a bf16 activation, median of 3 runs of "
+                         f"{t_med:.3f}s (numpy quantiser, C fp64 GEMV on {threads} threads)"}
+        print(f"[bench] CPU oracle: {t_med:.3f}s per call", flush=True)
+
+    out = {"metric": "achieved HBM GB/s of the NVFP4 GEMV fed by a bf16 activation (quantiser + "
+                     "GEMV per call)"}
+    out.update(common_fields(args, gbs, ms_step, "f32"))
+    out["config"] = {"workload": f"{cfg.name}: bf16 x quantised (rule {args.rule}) then NVFP4 GEMV "
+                                 f"l={l} m={m} k={k}, integer-coded A ({cfg.note})",
+                     "l": l, "m": m, "k": k, "rule": args.rule, "bytes_per_step": nbytes,
+                     "replicas": reps, "operands": "HBM (rotated over >= 1 GB of copies)"}
+    out["roofline"] = roofline(gbs, None)
+    out["cpu_baseline"] = cpu
+    return out
 
 
 def main(argv=None) -> int:
@@ -83,7 +375,7 @@ def main(argv=None) -> int:
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU only: the NVFP4 GEMV runs on a single MI355X and this "
-              "build has no multi-GPU path (sharding along M is described in DESIGN.md). "
+              "build has no multi-GPU path (the design notes describe sharding along M). "
               "Run with --gpus 1.", file=sys.stderr)
         return 2
 
@@ -102,142 +394,10 @@ def main(argv=None) -> int:
         return 1
     torch.cuda.set_device(0)
 
-    cfg = workloads.CONFIGS[args.config]
-    if cfg.kind != "integer":
-        print(f"{cfg.name} is not an integer-coded workload; bench it with an integer config",
-              file=sys.stderr)
+    fn = {"gemv": bench_gemv, "quantize": bench_quantize, "gemv_bf16x": bench_bf16x}[args.path]
+    out = fn(args, torch, np, pd, workloads)
+    if out is None:
         return 2
-    l, m, k = cfg.l, cfg.m, cfg.k
-    nbytes = cfg.bytes_moved
-    print(f"[bench] workload {cfg.name}: l={l} m={m} k={k}, {nbytes} bytes per step", flush=True)
-
-    ops = workloads.for_config(cfg)
-    base = {n: torch.from_numpy(np.ascontiguousarray(v)).cuda() for n, v in ops.items()}
-    reps = args.replicas or max(1, -(-1_000_000_000 // nbytes))
-    replicas = [base] + [{n: t.clone() for n, t in base.items()} for _ in range(reps - 1)]
-    c = torch.empty((l, m), dtype=torch.int16, device="cuda")
-    stream = torch.cuda.current_stream()
-    sptr = stream.cuda_stream
-
-    tuned = args.variant or args.ksplit
-    tuning = {"variant": args.variant, "ksplit": args.ksplit}
-    plan, ws_bytes = pd.nvfp4_gemv_plan(l, m, k, aligned=True, tuning=tuning if tuned else None)
-    ws = torch.empty(max(ws_bytes, 4), dtype=torch.uint8, device="cuda")
-
-    def step(i):
-        r = replicas[i % reps]
-        if tuned:
-            pd.nvfp4_gemv_launch_tuned(r["A"], r["sfA"], r["x"], r["sfx"], r["alpha"], c, l, m, k,
-                                       tuning, ws, ws_bytes, sptr)
-        else:
-            pd.nvfp4_gemv_launch(r["A"], r["sfA"], r["x"], r["sfx"], r["alpha"], c, l, m, k, sptr)
-
-    def timed(n, fn):
-        start = torch.cuda.Event(enable_timing=True)
-        end = torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        start.record(stream)
-        for i in range(n):
-            fn(i)
-        end.record(stream)
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
-        return start.elapsed_time(end), wall
-
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    print(f"[bench] warmup {args.warmup} done; plan path={plan.path} variant={plan.variant} "
-          f"ksplit={plan.ksplit}; {reps} replicas ({reps * nbytes / 1e9:.2f} GB)", flush=True)
-
-    ms_total, wall = timed(args.steps, step)
-    ms_step = ms_total / args.steps
-    gbs = nbytes / (ms_step * 1e-3) / 1e9
-    print(f"[bench] {args.steps} steps: {ms_step * 1e3:.2f} us/step, {gbs:.1f} GB/s "
-          f"({100 * gbs / HBM_PEAK_GBS:.1f}% of peak), host wall {wall:.3f}s", flush=True)
-
-    warm_ms, _ = timed(min(args.steps, 500), lambda i: step(0))
-    warm_gbs = nbytes / (warm_ms / min(args.steps, 500) * 1e-3) / 1e9
-    print(f"[bench] cache-resident (same buffers every step): {warm_gbs:.1f} GB/s", flush=True)
-
-    probe_gbs = probe_ws_gbs = None
-    if not args.no_probe:
-        pbytes = 1 << 30
-        pbuf = torch.empty(pbytes, dtype=torch.uint8, device="cuda")
-        pbuf.fill_(1)
-        sink = torch.empty(4096, dtype=torch.int32, device="cuda")
-        for _ in range(3):
-            pd.nvfp4_hbm_read_probe(pbuf, pbytes, sink, sptr)
-        pn = 20
-        pms, _ = timed(pn, lambda i: pd.nvfp4_hbm_read_probe(pbuf, pbytes, sink, sptr))
-        probe_gbs = pbytes / (pms / pn * 1e-3) / 1e9
-        del pbuf
-        print(f"[bench] streaming-read probe (1 GiB): {probe_gbs:.1f} GB/s", flush=True)
-        # the same probe over each copy's A in turn: the achievable read rate
-        # for a read of this workload's size, operands in HBM
-        abytes = replicas[0]["A"].numel()
-        pn = 4 * reps
-        pms, _ = timed(pn, lambda i: pd.nvfp4_hbm_read_probe(replicas[i % reps]["A"], abytes, sink, sptr))
-        probe_ws_gbs = abytes / (pms / pn * 1e-3) / 1e9
-        print(f"[bench] streaming-read probe over A ({abytes / 1e6:.1f} MB, rotated): "
-              f"{probe_ws_gbs:.1f} GB/s", flush=True)
-
-    if args.copy_mib:
-        src = torch.ones(args.copy_mib << 20, dtype=torch.uint8, device="cuda")
-        dst = torch.empty_like(src)
-        for _ in range(4):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        print(f"[bench] ran 4 device copies of {args.copy_mib} MiB", flush=True)
-
-    cpu = None
-    if not args.no_cpu_baseline:
-        from oracle import reference as ref
-
-        threads = ref.default_threads()
-        times = []
-        for _ in range(3):
-            t0 = time.perf_counter()
-            ref.gemv(ops["A"], ops["sfA"], ops["x"], ops["sfx"], ops["alpha"], l, m, k, nthreads=threads)
-            times.append(time.perf_counter() - t0)
-        t_med = statistics.median(times)
-        cpu = {"value": round(nbytes / t_med / 1e9, 4), "unit": "GB/s", "cores": threads,
-               "kind": "oracle",
-               "sample": f"the whole {cfg.name} workload (l={l}, m={m}, k={k}), median of 3 runs "
-                         f"of {t_med:.3f}s, fp64 sums + fp32/fp16 epilogue, inputs in host memory"}
-        print(f"[bench] CPU oracle: {t_med:.3f}s per GEMV on {threads} threads", flush=True)
-
-    traffic = recorded_traffic(cfg.name)
-    out = {
-        "metric": "achieved HBM GB/s for the NVFP4 block-scaled batched GEMV (us/call and % of "
-                  "MI355X peak alongside)",
-        "value": round(gbs, 2),
-        "unit": "GB/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 6),
-        "us_per_call": round(ms_step * 1e3, 3),
-        "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "f32",
-        "data": "synthetic",
-        "config": {"workload": f"{cfg.name}: NVFP4 GEMV l={l} m={m} k={k}, integer-coded, "
-                               f"alpha=1 ({cfg.note})",
-                   "l": l, "m": m, "k": k, "bytes_per_step": nbytes,
-                   "replicas": reps, "operands": "HBM (rotated over >= 1 GB of copies)",
-                   "plan": {"path": plan.path, "variant": plan.variant, "ksplit": plan.ksplit}},
-        "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(gbs / HBM_PEAK_GBS, 4),
-                     "traffic": traffic,
-                     "probe_read_gbs": round(probe_gbs, 2) if probe_gbs else None,
-                     "probe_read_same_size_gbs": round(probe_ws_gbs, 2) if probe_ws_gbs else None,
-                     "cache_resident_gbs": round(warm_gbs, 2)},
-        "cpu_baseline": cpu,
-    }
     print(json.dumps(out), flush=True)
     return 0
 

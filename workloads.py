@@ -139,3 +139,41 @@ def for_config(cfg: Config):
     if cfg.kind != "integer":
         raise ValueError(f"{cfg.name} is not integer-coded")
     return integer_coded(cfg.l, cfg.m, cfg.k, cfg.seed, cfg.alpha)
+
+
+def bf16_bits(values) -> np.ndarray:
+    """Bit patterns (uint16) of float32 values that hold bf16 numbers: the upper
+    half of each float32 word (a pure re-encoding, no rounding)."""
+    v = np.ascontiguousarray(np.asarray(values, dtype=np.float32))
+    return (v.view(np.uint32) >> 16).astype(np.uint16)
+
+
+@dataclass(frozen=True)
+class ActConfig:
+    """A bf16 activation batch for the activation quantiser: ``rows`` vectors
+    of length ``d``, N(0, 1) rounded to bf16."""
+    name: str
+    rows: int
+    d: int
+    seed: int = 0
+    note: str = ""
+
+    @property
+    def bytes_moved(self) -> int:
+        """Algorithmic HBM bytes of one quantisation: bf16 in, codes and block
+        scales out (the per-row global scales are 4 bytes a row)."""
+        n = self.rows * self.d
+        return 2 * n + n // 2 + n // 16 + 4 * self.rows
+
+
+ACT_CONFIGS = {
+    "decode_x": ActConfig("decode_x", 1, 16384,
+                          note="the decode workload's activation vector (k = 16384)"),
+    "tokens": ActConfig("tokens", 4096, 7168,
+                        note="4096 token activations of the batched workload's K (7168)"),
+}
+
+
+def activation_bf16(cfg: ActConfig) -> np.ndarray:
+    """float32 (rows, d) holding bf16 values, N(0, 1)."""
+    return gaussian_bf16(1, cfg.rows, cfg.d, seed=cfg.seed)["A"][0]
