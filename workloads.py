@@ -177,3 +177,81 @@ ACT_CONFIGS = {
 def activation_bf16(cfg: ActConfig) -> np.ndarray:
     """float32 (rows, d) holding bf16 values, N(0, 1)."""
     return gaussian_bf16(1, cfg.rows, cfg.d, seed=cfg.seed)["A"][0]
+
+
+@dataclass(frozen=True)
+class SmallNConfig:
+    """n integer-coded vectors per batch against one integer-coded weight
+    matrix per batch (A (l, m, k/2), B (l, n, k/2))."""
+    name: str
+    l: int
+    m: int
+    n: int
+    k: int
+    seed: int = 0
+    note: str = ""
+
+    @property
+    def bytes_moved(self) -> int:
+        l, m, n, k = self.l, self.m, self.n, self.k
+        return l * m * k * 9 // 16 + l * n * k * 9 // 16 + 2 * l * m * n + 4 * l
+
+
+SMALLN_CONFIGS = {
+    "tiny_n3": SmallNConfig("tiny_n3", 2, 80, 3, 256, note="tiny, ragged rows"),
+    "decode_n4": SmallNConfig("decode_n4", 1, 7168, 4, 16384,
+                              note="the decode weight against 4 vectors (speculative tokens)"),
+    "decode_n16": SmallNConfig("decode_n16", 1, 7168, 16, 16384,
+                               note="the decode weight against 16 vectors (a decode batch)"),
+}
+
+
+def smalln_operands(cfg: SmallNConfig):
+    """A, sfA (l, m, .), B, sfB (l, n, .), alpha (l,) U[0.5, 2]."""
+    a = integer_coded(cfg.l, cfg.m, cfg.k, seed=cfg.seed, alpha="uniform")
+    b = integer_coded(cfg.l, cfg.n, cfg.k, seed=cfg.seed + 1)
+    return {"A": a["A"], "sfA": a["sfA"], "B": b["A"], "sfB": b["sfA"], "alpha": a["alpha"]}
+
+
+@dataclass(frozen=True)
+class MoeConfig:
+    """Grouped (MoE) GEMV: ``tokens`` token rows already grouped by expert, the
+    count of each expert drawn from a seeded multinomial (some experts get
+    none), integer-coded activations and expert weights (experts, n, k/2),
+    per-expert global scales U[0.5, 2]."""
+    name: str
+    experts: int
+    n: int
+    k: int
+    tokens: int
+    seed: int = 0
+    note: str = ""
+
+
+MOE_CONFIGS = {
+    "moe_tiny": MoeConfig("moe_tiny", 6, 96, 256, 20, note="tiny, ragged rows"),
+    "moe_decode": MoeConfig("moe_decode", 64, 2048, 7168, 128,
+                            note="64 experts of 2048 x 7168, 128 routed token slots"),
+}
+
+
+def moe_operands(cfg: MoeConfig):
+    """X, sfX (tokens, .), W, sfW (experts, n, .), offsets int32 (experts,)
+    cumulative token counts, gs_x, gs_w (experts,)."""
+    rng = np.random.default_rng(cfg.seed + 1000)
+    counts = rng.multinomial(cfg.tokens, np.full(cfg.experts, 1.0 / cfg.experts))
+    offsets = np.cumsum(counts).astype(np.int32)
+    gs_x = rng.uniform(0.5, 2.0, size=cfg.experts).astype(np.float32)
+    gs_w = rng.uniform(0.5, 2.0, size=cfg.experts).astype(np.float32)
+    w = integer_coded(cfg.experts, cfg.n, cfg.k, seed=cfg.seed)
+    x = integer_coded(1, cfg.tokens, cfg.k, seed=cfg.seed + 1)
+    return {"X": x["A"][0], "sfX": x["sfA"][0], "W": w["A"], "sfW": w["sfA"], "offsets": offsets,
+            "gs_x": gs_x, "gs_w": gs_w}
+
+
+def moe_bytes_moved(cfg: MoeConfig, offsets) -> int:
+    """Algorithmic bytes of one grouped call: the weights of experts with at
+    least one token, the token activations, the outputs (bf16)."""
+    counts = np.diff(np.concatenate([[0], np.asarray(offsets, dtype=np.int64)]))
+    active = int((counts > 0).sum())
+    return active * cfg.n * cfg.k * 9 // 16 + cfg.tokens * cfg.k * 9 // 16 + 2 * cfg.tokens * cfg.n
