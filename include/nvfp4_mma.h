@@ -1,0 +1,142 @@
+/*
+ * nvfp4_mma.h - C ABI of two MI355X (gfx950) NVFP4 block-scaled products of a
+ * weight matrix with several vectors: the small-N GEMM and the grouped (MoE)
+ * GEMV.  Both use the scaled dot product of nvfp4_gemv.h (16 consecutive K
+ * elements share one E4M3 scale, E2M1 codes packed two per byte with element
+ * 2i in bits 3:0, sign in bit 3 of a code), accumulate in fp32 and round the
+ * product with the global scale to fp16 or bf16 (round to nearest even).
+ *
+ * Small-N GEMM.  The blog post "nvFP4 Batch GEMV算子系列(下)" (section
+ * "pytorch实现NVFP4 batch gemv") computes its batched GEMV as a scaled matrix
+ * product whose N dimension is padded for the library call; here N = n
+ * vectors are used as they are:
+ *
+ *   S[b,r,j] = sum_kk e2m1(A[b,r,kk]) e4m3(sfA[b,r,kk/16]) e2m1(B[b,j,kk]) e4m3(sfB[b,j,kk/16])
+ *   c[b,r,j] = out( f32( alpha[b] * S[b,r,j] ) )
+ *
+ * for b < l, r < m, j < n, with
+ *   A_packed uint8 [l][m][k/2], sfA uint8 [l][m][k/16],
+ *   B_packed uint8 [l][n][k/2], sfB uint8 [l][n][k/16],
+ *   alpha    float [l] or NULL (1), c uint16 [l][m][n] (fp16 or bf16 bits).
+ *
+ * Grouped GEMV.  The CuTeDSL bridge page (sections "Tensor Layout
+ * Conversion" and "Kernel Launch") runs a 2D x 3D grouped GEMM: token rows
+ * sorted by expert, one weight matrix per expert, cumulative token offsets per
+ * expert and one fp32 global scale per expert for each operand.  Token t with
+ * offsets[e-1] <= t < offsets[e] (offsets[-1] = 0) belongs to expert e and
+ *
+ *   S[t,r]  = sum_kk e2m1(X[t,kk]) e4m3(sfX[t,kk/16]) e2m1(W[e,r,kk]) e4m3(sfW[e,r,kk/16])
+ *   c[t,r]  = out( f32( f32(gs_x[e] * gs_w[e]) * S[t,r] ) )
+ *
+ * for r < n, with
+ *   X_packed uint8 [tokens][k/2], sfX uint8 [tokens][k/16],
+ *   W_packed uint8 [experts][n][k/2], sfW uint8 [experts][n][k/16],
+ *   offsets  int32 [experts] cumulative token counts (non-decreasing, at most
+ *            `tokens`), gs_x, gs_w float [experts] or NULL (1),
+ *   c        uint16 [tokens][n] (fp16 or bf16 bits).
+ * Rows of c whose token belongs to no expert (t >= offsets[experts-1]) are
+ * left untouched.  The offsets live on the device and are never read by the
+ * host; the kernels clamp them to [0, tokens], so any values are memory-safe,
+ * but token ranges that overlap (decreasing offsets) give unspecified values
+ * in the overlapping rows.
+ *
+ * out_type: NVFP4_OUT_F16 (the blog post's output type) or NVFP4_OUT_BF16
+ * (the bridge page's).  Accumulation order inside the fp32 sums is not fixed;
+ * with the integer-coded inputs every partial sum is exact, so results are
+ * bit-identical to the exact values rounded as above.
+ *
+ * All data pointers are DEVICE pointers owned by the caller; the library never
+ * keeps them after the enqueued work.  `stream` is a hipStream_t (NULL = the
+ * default stream).  Calls only enqueue work: no device synchronisation, no
+ * host read of device memory.  Shape rules: every dimension >= 1 (tokens may
+ * be 0 for the grouped call), k >= 16, k % 16 == 0, byte sizes within int64,
+ * and the output count below 2^31.  The fast kernels need k % 32 == 0 and
+ * 16-byte aligned packed operands, 2-byte aligned scales; other valid calls
+ * take a slower generic kernel with the same results.  Every argument is
+ * checked before any HIP call; invalid calls return a negative status of
+ * nvfp4_gemv.h and enqueue nothing.  No C++ exception crosses this interface.
+ */
+#ifndef NVFP4_MMA_H
+#define NVFP4_MMA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "nvfp4_gemv.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define NVFP4_OUT_F16 0
+#define NVFP4_OUT_BF16 1
+
+/*
+ * The small-N GEMM above.  When the plan splits K across workgroups the fp32
+ * partial sums go to the library-owned per-(device, stream) workspace of
+ * nvfp4_gemv_launch (allocated on first need, kept until the process ends).
+ * Returns NVFP4_GEMV_OK or a negative status (BAD_ARGUMENT for an unknown
+ * out_type).
+ */
+int nvfp4_gemm_smalln_launch(const uint8_t *A_packed, const uint8_t *sfA,
+                             const uint8_t *B_packed, const uint8_t *sfB,
+                             const float *alpha, uint16_t *c,
+                             int64_t l, int64_t m, int64_t n, int64_t k,
+                             int32_t out_type, void *stream);
+
+/*
+ * Number of fast small-N / grouped kernel variants, and the shape of variant
+ * v (1-based): MFMA row tiles of 16 weight rows per wave, K windows of 128
+ * elements kept in flight per wave, waves per workgroup (each wave takes
+ * every waves-th window of the workgroup's K range).  Returns a status.
+ */
+int nvfp4_mma_num_variants(void);
+int nvfp4_mma_variant_info(int v, int32_t *row_tiles_per_wave, int32_t *windows_in_flight,
+                           int32_t *waves_per_group);
+
+/*
+ * The small-N plan the library would use (path, variant, K split) and the
+ * workspace it needs, as nvfp4_gemv_plan does for the GEMV; `in` may be NULL.
+ */
+int nvfp4_gemm_smalln_plan(int64_t l, int64_t m, int64_t n, int64_t k, int aligned,
+                           const nvfp4_gemv_tuning_t *in, nvfp4_gemv_tuning_t *out,
+                           size_t *workspace_bytes);
+
+/*
+ * The small-N GEMM with an explicit plan (`tuning` may be NULL) and a
+ * caller-owned workspace of at least the bytes nvfp4_gemm_smalln_plan reports
+ * (4-byte aligned; may be NULL when that is 0).  Allocates nothing.
+ */
+int nvfp4_gemm_smalln_launch_tuned(const uint8_t *A_packed, const uint8_t *sfA,
+                                   const uint8_t *B_packed, const uint8_t *sfB,
+                                   const float *alpha, uint16_t *c,
+                                   int64_t l, int64_t m, int64_t n, int64_t k,
+                                   int32_t out_type, const nvfp4_gemv_tuning_t *tuning,
+                                   void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * The grouped (MoE) GEMV above.  Never splits K and needs no workspace.
+ * Returns NVFP4_GEMV_OK or a negative status.
+ */
+int nvfp4_grouped_gemv_launch(const uint8_t *X_packed, const uint8_t *sfX,
+                              const uint8_t *W_packed, const uint8_t *sfW,
+                              const int32_t *offsets, const float *gs_x, const float *gs_w,
+                              uint16_t *c, int64_t tokens, int64_t experts, int64_t n, int64_t k,
+                              int32_t out_type, void *stream);
+
+/*
+ * The grouped GEMV with an explicit kernel choice (`tuning` may be NULL;
+ * its ksplit must be 0 or 1).
+ */
+int nvfp4_grouped_gemv_launch_tuned(const uint8_t *X_packed, const uint8_t *sfX,
+                                    const uint8_t *W_packed, const uint8_t *sfW,
+                                    const int32_t *offsets, const float *gs_x,
+                                    const float *gs_w, uint16_t *c, int64_t tokens,
+                                    int64_t experts, int64_t n, int64_t k, int32_t out_type,
+                                    const nvfp4_gemv_tuning_t *tuning, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NVFP4_MMA_H */

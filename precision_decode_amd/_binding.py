@@ -1,7 +1,7 @@
 """ctypes binding of ``libnvfp4_gemv.so`` (argument marshalling only).
 
-Each C entry point of ``include/nvfp4_gemv.h`` and ``include/nvfp4_quantize.h``
-has a Python function of the same name.  Pointer arguments accept a torch tensor (its ``data_ptr()``), a raw
+Each C entry point of ``include/nvfp4_gemv.h``, ``include/nvfp4_quantize.h``
+and ``include/nvfp4_mma.h`` has a Python function of the same name.  Pointer arguments accept a torch tensor (its ``data_ptr()``), a raw
 integer device address, or None where the C side allows NULL; ``stream``
 accepts None (torch's current stream), a ``torch.cuda.Stream`` or a raw
 ``hipStream_t`` integer.  A negative status raises :class:`Nvfp4GemvError`.
@@ -30,6 +30,9 @@ NVFP4_ROUND_HALF_STEP = 0
 NVFP4_ROUND_NEAREST_EVEN = 1
 NVFP4_ROUND_NEAREST_LOWER = 2
 
+NVFP4_OUT_F16 = 0
+NVFP4_OUT_BF16 = 1
+
 NVFP4_GEMV_PATH_AUTO = 0
 NVFP4_GEMV_PATH_FAST = 1
 NVFP4_GEMV_PATH_GENERIC = 2
@@ -47,6 +50,13 @@ EXPORTED = (
     "nvfp4_hbm_read_probe",
     "nvfp4_quantize_activation",
     "nvfp4_gemv_bf16x_launch",
+    "nvfp4_gemm_smalln_launch",
+    "nvfp4_mma_num_variants",
+    "nvfp4_mma_variant_info",
+    "nvfp4_gemm_smalln_plan",
+    "nvfp4_gemm_smalln_launch_tuned",
+    "nvfp4_grouped_gemv_launch",
+    "nvfp4_grouped_gemv_launch_tuned",
 )
 
 
@@ -104,6 +114,25 @@ def load():
     lib.nvfp4_gemv_bf16x_launch.restype = ctypes.c_int
     lib.nvfp4_gemv_bf16x_launch.argtypes = [_P, _P, _P, _P, _P, ctypes.c_int32, _P, _P, _P, _P,
                                             _I64, _I64, _I64, _P]
+    smalln_args = [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, ctypes.c_int32]
+    lib.nvfp4_gemm_smalln_launch.restype = ctypes.c_int
+    lib.nvfp4_gemm_smalln_launch.argtypes = smalln_args + [_P]
+    lib.nvfp4_mma_num_variants.restype = ctypes.c_int
+    lib.nvfp4_mma_num_variants.argtypes = []
+    lib.nvfp4_mma_variant_info.restype = ctypes.c_int
+    lib.nvfp4_mma_variant_info.argtypes = [ctypes.c_int] + [ctypes.POINTER(ctypes.c_int32)] * 3
+    lib.nvfp4_gemm_smalln_plan.restype = ctypes.c_int
+    lib.nvfp4_gemm_smalln_plan.argtypes = [_I64, _I64, _I64, _I64, ctypes.c_int,
+                                           ctypes.POINTER(Tuning), ctypes.POINTER(Tuning),
+                                           ctypes.POINTER(ctypes.c_size_t)]
+    lib.nvfp4_gemm_smalln_launch_tuned.restype = ctypes.c_int
+    lib.nvfp4_gemm_smalln_launch_tuned.argtypes = smalln_args + [ctypes.POINTER(Tuning), _P,
+                                                                 ctypes.c_size_t, _P]
+    grouped_args = [_P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, ctypes.c_int32]
+    lib.nvfp4_grouped_gemv_launch.restype = ctypes.c_int
+    lib.nvfp4_grouped_gemv_launch.argtypes = grouped_args + [_P]
+    lib.nvfp4_grouped_gemv_launch_tuned.restype = ctypes.c_int
+    lib.nvfp4_grouped_gemv_launch_tuned.argtypes = grouped_args + [ctypes.POINTER(Tuning), _P]
     _lib = lib
     return lib
 
@@ -210,6 +239,61 @@ def nvfp4_gemv_bf16x_launch(A_packed, sfA, A_scale, x_bf16, x_scale, rule, x_pac
                                           _ptr(x_scale), int(rule), _ptr(x_packed), _ptr(sfx),
                                           _ptr(alpha), _ptr(c), l, m, k, _stream(stream)),
            "nvfp4_gemv_bf16x_launch")
+
+
+def nvfp4_gemm_smalln_launch(A_packed, sfA, B_packed, sfB, alpha, c, l, m, n, k,
+                             out_type=NVFP4_OUT_F16, stream=None):
+    _check(load().nvfp4_gemm_smalln_launch(_ptr(A_packed), _ptr(sfA), _ptr(B_packed), _ptr(sfB),
+                                           _ptr(alpha), _ptr(c), l, m, n, k, int(out_type),
+                                           _stream(stream)), "nvfp4_gemm_smalln_launch")
+
+
+def nvfp4_mma_num_variants() -> int:
+    return int(load().nvfp4_mma_num_variants())
+
+
+def nvfp4_mma_variant_info(v: int):
+    """(row tiles of 16 per wave, windows in flight, waves per group)."""
+    r, u, w = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+    _check(load().nvfp4_mma_variant_info(v, ctypes.byref(r), ctypes.byref(u), ctypes.byref(w)),
+           "nvfp4_mma_variant_info")
+    return r.value, u.value, w.value
+
+
+def nvfp4_gemm_smalln_plan(l, m, n, k, aligned=True, tuning=None):
+    """Returns (Tuning actually used, workspace bytes)."""
+    out = Tuning()
+    ws = ctypes.c_size_t()
+    _check(load().nvfp4_gemm_smalln_plan(l, m, n, k, int(bool(aligned)), _tuning(tuning),
+                                         ctypes.byref(out), ctypes.byref(ws)),
+           "nvfp4_gemm_smalln_plan")
+    return out, int(ws.value)
+
+
+def nvfp4_gemm_smalln_launch_tuned(A_packed, sfA, B_packed, sfB, alpha, c, l, m, n, k, out_type,
+                                   tuning, workspace, workspace_bytes, stream=None):
+    _check(load().nvfp4_gemm_smalln_launch_tuned(_ptr(A_packed), _ptr(sfA), _ptr(B_packed),
+                                                 _ptr(sfB), _ptr(alpha), _ptr(c), l, m, n, k,
+                                                 int(out_type), _tuning(tuning), _ptr(workspace),
+                                                 int(workspace_bytes), _stream(stream)),
+           "nvfp4_gemm_smalln_launch_tuned")
+
+
+def nvfp4_grouped_gemv_launch(X_packed, sfX, W_packed, sfW, offsets, gs_x, gs_w, c, tokens, experts,
+                              n, k, out_type=NVFP4_OUT_BF16, stream=None):
+    _check(load().nvfp4_grouped_gemv_launch(_ptr(X_packed), _ptr(sfX), _ptr(W_packed), _ptr(sfW),
+                                            _ptr(offsets), _ptr(gs_x), _ptr(gs_w), _ptr(c), tokens,
+                                            experts, n, k, int(out_type), _stream(stream)),
+           "nvfp4_grouped_gemv_launch")
+
+
+def nvfp4_grouped_gemv_launch_tuned(X_packed, sfX, W_packed, sfW, offsets, gs_x, gs_w, c, tokens,
+                                    experts, n, k, out_type, tuning, stream=None):
+    _check(load().nvfp4_grouped_gemv_launch_tuned(_ptr(X_packed), _ptr(sfX), _ptr(W_packed),
+                                                  _ptr(sfW), _ptr(offsets), _ptr(gs_x), _ptr(gs_w),
+                                                  _ptr(c), tokens, experts, n, k, int(out_type),
+                                                  _tuning(tuning), _stream(stream)),
+           "nvfp4_grouped_gemv_launch_tuned")
 
 
 def quantize_activation(x, global_scale, rule=NVFP4_ROUND_HALF_STEP, stream=None):

@@ -14,7 +14,7 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-SRCS = [os.path.join(HERE, "csrc", n) for n in ("nvfp4_gemv.hip", "nvfp4_quantize.hip")]
+SRCS = [os.path.join(HERE, "csrc", n) for n in ("nvfp4_gemv.hip", "nvfp4_quantize.hip", "nvfp4_mma.hip")]
 LIB = os.path.join(HERE, "libnvfp4_gemv.so")
 INCLUDE = os.path.join(ROOT, "include")
 ARCH = "gfx950"

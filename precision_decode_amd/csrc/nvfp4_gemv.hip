@@ -42,15 +42,13 @@
 #include <mutex>
 #include <utility>
 
+#include "device_common.h"
 #include "nvfp4_gemv.h"
 
 namespace {
 
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
+using namespace nvfp4dev;
 
-constexpr int kWave = 64;
 constexpr int64_t kIterElems = 2048;    // K elements one wave covers per row per iteration
 constexpr int64_t kMaxChunk = 16384;    // K elements staged in LDS per workgroup (32 KiB)
 constexpr int64_t kMinSplitChunk = 2048;
@@ -61,22 +59,6 @@ constexpr int kProbeThreads = 256;
 constexpr int kProbeMaxGroups = 4096;
 
 // ---------------------------------------------------------------- decode
-// Two E2M1 codes (byte SEL of w) -> two fp16, exact.  The scale operand of the
-// gfx950 conversion is a power of two carried in a float; 1.0 leaves values
-// unscaled.
-template <int SEL>
-__device__ __forceinline__ f16x2 e2m1x2_f16(uint32_t w) {
-    return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, SEL);
-}
-
-// Two E4M3 codes (bytes 0 and 1 of w) -> two fp32, exact.
-__device__ __forceinline__ f32x2 e4m3x2_f32(uint32_t w) {
-    return __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w), false);
-}
-
-__device__ __forceinline__ uint32_t bits(f16x2 v) { return __builtin_bit_cast(uint32_t, v); }
-__device__ __forceinline__ f16x2 halves(uint32_t w) { return __builtin_bit_cast(f16x2, w); }
-
 // acc + sum over the 8 codes of `a` of e2m1(code) * x~ (8 fp16 in xq).
 __device__ __forceinline__ float dot8(uint32_t a, u32x4 xq, float acc) {
     acc = __builtin_amdgcn_fdot2(e2m1x2_f16<0>(a), halves(xq.x), acc, false);
@@ -120,40 +102,6 @@ __device__ __forceinline__ u32x4 load_nt16(const uint8_t *p) {
     return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
 }
 
-// Sum over the 64 lanes, the same value in every lane, without LDS: DPP
-// exchanges inside 16-lane rows (neighbour, pair, mirror of 8, mirror of 16),
-// then swaps of 16-lane rows and of 32-lane halves.  Each step adds two values
-// that every lane of a pair adds in the same order, so all lanes agree bit
-// for bit.
-template <int CTRL>
-__device__ __forceinline__ float dpp(float v) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL,
-                                                              0xF, 0xF, false));
-}
-__device__ __forceinline__ float wave_sum(float v) {
-    v += dpp<0xB1>(v);    // quad_perm [1,0,3,2]
-    v += dpp<0x4E>(v);    // quad_perm [2,3,0,1]
-    v += dpp<0x141>(v);   // row_half_mirror
-    v += dpp<0x140>(v);   // row_mirror
-    const unsigned u = __builtin_bit_cast(unsigned, v);
-    const auto r16 = __builtin_amdgcn_permlane16_swap(u, u, false, false);
-    v = __builtin_bit_cast(float, static_cast<unsigned>(r16[0])) +
-        __builtin_bit_cast(float, static_cast<unsigned>(r16[1]));
-    const unsigned w = __builtin_bit_cast(unsigned, v);
-    const auto r32 = __builtin_amdgcn_permlane32_swap(w, w, false, false);
-    return __builtin_bit_cast(float, static_cast<unsigned>(r32[0])) +
-           __builtin_bit_cast(float, static_cast<unsigned>(r32[1]));
-}
-
-// fp16 bits of f16(f32(al * v)): the product is rounded to fp32 first.  The
-// empty asm keeps that rounding: without it the compiler folds the multiply
-// and the conversion into one mixed-precision FMA that rounds only once, to
-// fp16, which differs on a few outputs.
-__device__ __forceinline__ uint16_t f16_of_product(float al, float v) {
-    float p = al * v;
-    __asm__ volatile("" : "+v"(p));
-    return __builtin_bit_cast(uint16_t, static_cast<_Float16>(p));
-}
 
 // ---------------------------------------------------------------- fast kernel
 // Workgroup = W waves; wave w streams rows rb*W*R + w*R .. +R-1 of batch b over
@@ -172,19 +120,6 @@ __device__ __forceinline__ uint16_t f16_of_product(float al, float v) {
 // contributes +0.  So no load sits under a per-lane branch, the compiler can
 // count outstanding loads, and U iterations of every row stay in flight.
 constexpr int kMaxIters = static_cast<int>(kMaxChunk / kIterElems);   // 8
-
-// Word 3 of a buffer descriptor: 32-bit data format, untyped (raw) access.
-constexpr int kRawBufferFlags = 0x00020000;
-// Cache-policy operand of a buffer load: non-temporal (streamed, read once).
-constexpr int kNonTemporal = 2;
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_of(const uint8_t *base, int bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(base), 0, bytes, kRawBufferFlags);
-}
-
-// Keeps the compiler's scheduler from moving any instruction across this
-// point (the phases below rely on issue order for the load counters).
-__device__ __forceinline__ void phase_fence() { __builtin_amdgcn_sched_barrier(0); }
 
 // Makes a loaded value available here, so its load cannot be sunk into a
 // later branch.
@@ -788,11 +723,15 @@ int run(const Plan &p, const uint8_t *A, const uint8_t *sfA, const uint8_t *x,
     return NVFP4_GEMV_OK;
 }
 
+}  // namespace
+
 // Library-owned split-K workspaces, one per (device, stream).
+namespace {
 std::mutex g_ws_mutex;
 std::map<std::pair<int, void *>, std::pair<void *, size_t>> g_ws;
+}  // namespace
 
-void *owned_workspace(int dev, void *stream, size_t need) {
+void *nvfp4_stream_workspace(int dev, void *stream, size_t need) {
     std::lock_guard<std::mutex> lock(g_ws_mutex);
     auto &slot = g_ws[std::make_pair(dev, stream)];
     if (slot.second >= need) return slot.first;
@@ -807,8 +746,6 @@ void *owned_workspace(int dev, void *stream, size_t need) {
     slot = std::make_pair(ptr, need);
     return ptr;
 }
-
-}  // namespace
 
 extern "C" {
 
@@ -906,7 +843,7 @@ int nvfp4_gemv_launch(const uint8_t *A_packed, const uint8_t *sfA, const uint8_t
     if (p.ws_bytes > 0) {
         int dev = -1;
         if (hipGetDevice(&dev) != hipSuccess) return NVFP4_GEMV_ERR_DEVICE;
-        ws = owned_workspace(dev, stream, p.ws_bytes);
+        ws = nvfp4_stream_workspace(dev, stream, p.ws_bytes);
         if (!ws) return NVFP4_GEMV_ERR_WORKSPACE;
     }
     return run(p, A_packed, sfA, x_packed, sfx, alpha, c, l, m, k, ws,

@@ -1,0 +1,659 @@
+// NVFP4 block-scaled products of a weight matrix with several vectors on
+// MI355X (gfx950): the small-N GEMM (n vectors per weight matrix) and the
+// grouped (MoE) GEMV (the tokens of each expert against that expert's
+// weights).  The scaled dot product is the NVFP4 batched GEMV's ("nvFP4 Batch
+// GEMV算子系列(下)", section "NVFP4 Batched GEMV 概念阐述"); the grouped form is
+// the 2D x 3D grouped GEMM of the CuTeDSL bridge page (section "Kernel
+// Launch"), shrunk to one output column per token.
+//
+// With up to 16 vectors per weight row the VALU can no longer do every
+// product (each weight element meets up to 16 vectors), while the bytes are
+// still those of a GEMV: weights are read once and dominate the traffic.  So
+// the products go to the matrix cores and the VALU only decodes:
+//
+//  * a weight element times its block scale, e2m1 * e4m3, has at most 5
+//    significant bits and lies in 2^-10 .. 2688, so it is exact in fp16; the
+//    same holds for the vectors.  Each lane decodes 32 codes (16 bytes) and
+//    their two block scales into four 8-element fp16 operands with the gfx950
+//    packed FP4 -> fp16 conversion and one packed fp16 multiply per pair;
+//  * v_mfma_f32_16x16x32_f16 multiplies a 16-row tile of weights by 16
+//    vectors over 32 K elements; products of two such values are exact in
+//    fp32 and the matrix core accumulates in fp32.  Lane i + 16q holds row
+//    (or vector) i, elements 8q .. 8q+7 of the 32; the contraction does not
+//    care which K element sits where as long as both operands agree, so a
+//    lane's 16-byte load covers 32 consecutive elements, split over the four
+//    MFMA steps of a 128-element window;
+//  * each wave streams its tile rows with 16-byte non-temporal buffer loads
+//    (16 rows x 64 contiguous bytes per instruction), keeps several windows
+//    in flight, and reads the vectors' codes with ordinary (cached) loads:
+//    every workgroup reads the same vectors, so they stay in L2;
+//  * the waves of a workgroup share the tile rows and take interleaved
+//    windows of its K range; their fp32 tiles are added in wave order through
+//    LDS, so the result does not depend on scheduling.  Few tiles are
+//    balanced by splitting K across workgroups (small-N GEMM only), with fp32
+//    partials added in split order by a second kernel.
+//
+// Every accumulator starts at +0.0, so an exactly-zero result is +0.  With
+// integer-coded inputs (E2M1 values times scales 0, 1, 2) every partial sum is
+// a multiple of 1/4 below 2^22, exact in fp32 in any order.
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cstddef>
+#include <cstdint>
+
+#include "device_common.h"
+#include "nvfp4_gemv.h"
+#include "nvfp4_mma.h"
+
+namespace {
+
+using namespace nvfp4dev;
+
+constexpr int kTile = 16;            // MFMA tile: 16 weight rows x 16 vectors
+constexpr int kWinElems = 128;       // K elements of one window (4 lane groups x 32)
+constexpr int64_t kMaxFastK = int64_t(1) << 26;   // keeps 32-row descriptors within 31 bits
+constexpr int64_t kTargetGroups = 1024;           // workgroups wanted before splitting K
+constexpr int kReduceThreads = 256;
+constexpr int kGenericWaves = 4;
+
+struct MmaArgs {
+    const uint8_t *W, *sW;      // weights [groups][rows][k/2], scales [groups][rows][k/16]
+    const uint8_t *V, *sV;      // vectors [.][k/2], scales [.][k/16]
+    const float *alpha;         // small-N: [groups] or NULL
+    const int32_t *offsets;     // grouped: [groups] cumulative token ends
+    const float *gs_v, *gs_w;   // grouped: [groups] or NULL
+    uint16_t *c;
+    float *part;                // small-N split-K partials, or NULL
+    int64_t groups, rows, nvec, k;   // nvec: n (small-N) or tokens (grouped)
+    int64_t kchunk;             // K elements per workgroup
+    int64_t row_blocks;         // workgroups along the rows of one group
+    int32_t out_bf16;
+};
+
+// Vectors [v0, v1) that group g multiplies: n per batch for the small-N GEMM,
+// the expert's token range for the grouped GEMV (offsets clamped to the
+// token count, so any offsets stay inside the arrays).
+template <bool GROUPED>
+__device__ __forceinline__ void vector_range(const MmaArgs &a, int64_t g, int64_t *v0, int64_t *v1) {
+    if (GROUPED) {
+        auto clampt = [&](int64_t v) { return v < 0 ? int64_t(0) : (v > a.nvec ? a.nvec : v); };
+        *v0 = g > 0 ? clampt(a.offsets[g - 1]) : 0;
+        *v1 = clampt(a.offsets[g]);
+    } else {
+        *v0 = g * a.nvec;
+        *v1 = *v0 + a.nvec;
+    }
+}
+
+__device__ __forceinline__ uint16_t round_out(float al, float v, int32_t bf16) {
+    return bf16 ? bf16_of_product(al, v) : f16_of_product(al, v);
+}
+
+__device__ __forceinline__ float group_alpha(const MmaArgs &a, int64_t g, bool grouped) {
+    if (grouped) {
+        const float gv = a.gs_v ? a.gs_v[g] : 1.0f;
+        const float gw = a.gs_w ? a.gs_w[g] : 1.0f;
+        return gv * gw;   // one fp32 rounding
+    }
+    return a.alpha ? a.alpha[g] : 1.0f;
+}
+
+// ---------------------------------------------------------------- decode
+__device__ __forceinline__ f16x8 join(f16x2 p, f16x2 q, f16x2 r, f16x2 s) {
+    return f16x8{p.x, p.y, q.x, q.y, r.x, r.y, s.x, s.y};
+}
+
+// 32 codes (16 bytes, element 2i in the low nibble of byte i) and their two
+// block-scale codes (bytes 0 and 1 of s2) -> four MFMA operands holding
+// e2m1 * e4m3 for elements 0-7, 8-15, 16-23, 24-31.  Exact in fp16.
+__device__ __forceinline__ void decode32(u32x4 q, uint32_t s2, f16x8 (&o)[4]) {
+    const f16x2 s = e4m3x2_f16(s2);
+    const f16x2 s0 = {s.x, s.x};
+    const f16x2 s1 = {s.y, s.y};
+    o[0] = join(e2m1x2_f16<0>(q.x) * s0, e2m1x2_f16<1>(q.x) * s0, e2m1x2_f16<2>(q.x) * s0,
+                e2m1x2_f16<3>(q.x) * s0);
+    o[1] = join(e2m1x2_f16<0>(q.y) * s0, e2m1x2_f16<1>(q.y) * s0, e2m1x2_f16<2>(q.y) * s0,
+                e2m1x2_f16<3>(q.y) * s0);
+    o[2] = join(e2m1x2_f16<0>(q.z) * s1, e2m1x2_f16<1>(q.z) * s1, e2m1x2_f16<2>(q.z) * s1,
+                e2m1x2_f16<3>(q.z) * s1);
+    o[3] = join(e2m1x2_f16<0>(q.w) * s1, e2m1x2_f16<1>(q.w) * s1, e2m1x2_f16<2>(q.w) * s1,
+                e2m1x2_f16<3>(q.w) * s1);
+}
+
+// ---------------------------------------------------------------- fast kernel
+// blockIdx.x enumerates (split, group, row block) with the row block fastest.
+// A workgroup owns R*16 weight rows of one group and the K range
+// [split*kchunk, min(k, (split+1)*kchunk)); wave w takes windows w, w+W, ...
+// of it.  Lane i + 16q loads, per window, the 32 elements at window offset
+// 32q of weight row i of each row tile and of vector i of the current pass of
+// 16 vectors.
+//
+// All global reads are buffer loads: a descriptor covers the workgroup's
+// valid weight rows (or the pass's vectors) over the whole K, and a lane
+// whose row or vector does not exist, or whose elements lie past the K range,
+// gets zeros from the hardware range check without touching memory.  No load
+// sits under a branch, so the compiler can count outstanding loads and keep U
+// windows in flight.
+//
+// Small-N: the A operand of the MFMA is the weight tile, the B operand the
+// vectors, so lane i + 16q ends with rows 4q .. 4q+3, vector i.  Grouped: the
+// operands swap, so lane i + 16q ends with tokens 4q .. 4q+3, row i, and the
+// 16 lanes of a quarter write 16 consecutive outputs of a token.
+template <int R, int U, int W, bool GROUPED>
+__global__ void __launch_bounds__(W * kWave) mma_stream(const MmaArgs a) {
+    __shared__ f32x4 red[(W > 1 ? W - 1 : 1) * R * kWave];
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int li = lane & (kTile - 1);
+    const int kq = lane >> 4;
+
+    int64_t gi = blockIdx.x;
+    const int64_t rb = gi % a.row_blocks;
+    gi /= a.row_blocks;
+    const int64_t grp = gi % a.groups;
+    const int64_t split = gi / a.groups;
+
+    int64_t v0, v1;
+    vector_range<GROUPED>(a, grp, &v0, &v1);
+    if (v1 <= v0) return;   // workgroup-uniform: an expert without tokens
+
+    const int64_t k = a.k;
+    const uint32_t half = static_cast<uint32_t>(k / 2);
+    const uint32_t sixteenth = static_cast<uint32_t>(k / 16);
+    const int64_t kb0 = split * a.kchunk;
+    const int64_t kend = (k - kb0 < a.kchunk) ? k : kb0 + a.kchunk;
+    const int nwin = static_cast<int>((kend - kb0 + kWinElems - 1) / kWinElems);
+    const int niter = nwin > wave ? (nwin - wave + W - 1) / W : 0;
+
+    const int64_t row0 = rb * (R * kTile);
+    const int64_t nrows = (a.rows - row0 < R * kTile) ? a.rows - row0 : R * kTile;
+    const __amdgpu_buffer_rsrc_t wdesc =
+        buffer_of(a.W + (grp * a.rows + row0) * (k / 2), static_cast<int>(nrows * (k / 2)));
+    const __amdgpu_buffer_rsrc_t swdesc =
+        buffer_of(a.sW + (grp * a.rows + row0) * (k / 16), static_cast<int>(nrows * (k / 16)));
+    const float al = group_alpha(a, grp, GROUPED);
+
+    for (int64_t vp = v0; vp < v1; vp += kTile) {
+        const int64_t nv = (v1 - vp < kTile) ? v1 - vp : kTile;
+        const __amdgpu_buffer_rsrc_t vdesc =
+            buffer_of(a.V + vp * (k / 2), static_cast<int>(nv * (k / 2)));
+        const __amdgpu_buffer_rsrc_t svdesc =
+            buffer_of(a.sV + vp * (k / 16), static_cast<int>(nv * (k / 16)));
+
+        u32x4 wq[U][R], vq[U];
+        uint16_t ws[U][R], vs[U];
+        auto issue = [&](int i, int u) {
+            const int64_t kk = kb0 + static_cast<int64_t>(wave + W * i) * kWinElems + kq * 32;
+            const bool in = kk < kend;
+            const uint32_t ko = static_cast<uint32_t>(kk / 2);
+            const uint32_t so = static_cast<uint32_t>(kk / 16);
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const uint32_t row = static_cast<uint32_t>(r * kTile + li);
+                const uint32_t o = in ? row * half + ko : kOutOfRange;
+                const uint32_t os = in ? row * sixteenth + so : kOutOfRange;
+                wq[u][r] = __builtin_bit_cast(
+                    u32x4, __builtin_amdgcn_raw_buffer_load_b128(wdesc, o, 0, kNonTemporal));
+                ws[u][r] = __builtin_amdgcn_raw_buffer_load_b16(swdesc, os, 0, kNonTemporal);
+            }
+            const uint32_t o = in ? static_cast<uint32_t>(li) * half + ko : kOutOfRange;
+            const uint32_t os = in ? static_cast<uint32_t>(li) * sixteenth + so : kOutOfRange;
+            vq[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vdesc, o, 0, 0));
+            vs[u] = __builtin_amdgcn_raw_buffer_load_b16(svdesc, os, 0, 0);
+        };
+
+        f32x4 acc[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) acc[r] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+        auto consume = [&](int u) {
+            f16x8 vo[4];
+            decode32(vq[u], vs[u], vo);
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                f16x8 wo[4];
+                decode32(wq[u][r], ws[u][r], wo);
+#pragma unroll
+                for (int s = 0; s < 4; ++s) {
+                    if (GROUPED)
+                        acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vo[s], wo[s], acc[r], 0, 0, 0);
+                    else
+                        acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wo[s], vo[s], acc[r], 0, 0, 0);
+                }
+            }
+        };
+
+        phase_fence();
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            issue(u, u);
+            phase_fence();
+        }
+        for (int i = 0; i < niter; i += U) {
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                if (i + u < niter) consume(u);   // wave-uniform
+                issue(i + u + U, u);             // past the wave's windows: zeros, no traffic
+                phase_fence();
+            }
+        }
+
+        // Tiles of waves 1..W-1 through LDS, added to wave 0's in wave order.
+        if (W > 1) {
+            if (wave > 0) {
+#pragma unroll
+                for (int r = 0; r < R; ++r) red[((wave - 1) * R + r) * kWave + lane] = acc[r];
+            }
+            __syncthreads();
+        }
+        if (wave == 0) {
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                f32x4 s = acc[r];
+                for (int w = 1; w < W; ++w) s += red[((w - 1) * R + r) * kWave + lane];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    if (GROUPED) {
+                        const int64_t t = vp + kq * 4 + e;
+                        const int64_t row = row0 + r * kTile + li;
+                        if (t < v1 && row < a.rows)
+                            a.c[t * a.rows + row] = round_out(al, s[e], a.out_bf16);
+                    } else {
+                        const int64_t row = row0 + r * kTile + kq * 4 + e;
+                        const int64_t col = vp - v0 + li;
+                        if (row < a.rows && col < a.nvec) {
+                            const int64_t o = (grp * a.rows + row) * a.nvec + col;
+                            if (a.part != nullptr)
+                                a.part[split * a.groups * a.rows * a.nvec + o] = s[e];
+                            else
+                                a.c[o] = round_out(al, s[e], a.out_bf16);
+                        }
+                    }
+                }
+            }
+        }
+        if (W > 1 && vp + kTile < v1) __syncthreads();   // before the next pass reuses `red`
+    }
+}
+
+// ---------------------------------------------------------------- generic kernel
+// Any k % 16 == 0 and any byte alignment.  One wave per (group, weight row);
+// lanes take 16-element blocks; bytes are loaded singly; vectors one by one.
+__device__ __forceinline__ uint32_t load_u32_bytes(const uint8_t *p) {
+    return static_cast<uint32_t>(p[0]) | (static_cast<uint32_t>(p[1]) << 8) |
+           (static_cast<uint32_t>(p[2]) << 16) | (static_cast<uint32_t>(p[3]) << 24);
+}
+
+__device__ __forceinline__ float dot8_codes(uint32_t a, uint32_t v, float acc) {
+    acc = __builtin_amdgcn_fdot2(e2m1x2_f16<0>(a), e2m1x2_f16<0>(v), acc, false);
+    acc = __builtin_amdgcn_fdot2(e2m1x2_f16<1>(a), e2m1x2_f16<1>(v), acc, false);
+    acc = __builtin_amdgcn_fdot2(e2m1x2_f16<2>(a), e2m1x2_f16<2>(v), acc, false);
+    acc = __builtin_amdgcn_fdot2(e2m1x2_f16<3>(a), e2m1x2_f16<3>(v), acc, false);
+    return acc;
+}
+
+template <bool GROUPED>
+__global__ void __launch_bounds__(kGenericWaves * kWave) mma_generic(const MmaArgs a) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    const int64_t rb = blockIdx.x % a.row_blocks;
+    const int64_t grp = blockIdx.x / a.row_blocks;
+    const int64_t row = rb * kGenericWaves + wave;
+    if (row >= a.rows) return;
+    int64_t v0, v1;
+    vector_range<GROUPED>(a, grp, &v0, &v1);
+    const int64_t k = a.k;
+    const uint8_t *wrow = a.W + (grp * a.rows + row) * (k / 2);
+    const uint8_t *swrow = a.sW + (grp * a.rows + row) * (k / 16);
+    const float al = group_alpha(a, grp, GROUPED);
+    for (int64_t v = v0; v < v1; ++v) {
+        const uint8_t *vrow = a.V + v * (k / 2);
+        const uint8_t *svrow = a.sV + v * (k / 16);
+        float acc = 0.0f;
+        for (int64_t blk = lane; blk < k / 16; blk += kWave) {
+            float bs = dot8_codes(load_u32_bytes(wrow + blk * 8), load_u32_bytes(vrow + blk * 8), 0.0f);
+            bs = dot8_codes(load_u32_bytes(wrow + blk * 8 + 4), load_u32_bytes(vrow + blk * 8 + 4), bs);
+            // sW * sV is exact in fp32 (4 + 4 significant bits)
+            const float sc = e4m3x2_f32(swrow[blk]).x * e4m3x2_f32(svrow[blk]).x;
+            acc = __builtin_fmaf(bs, sc, acc);
+        }
+        const float s = wave_sum(acc);
+        if (lane == 0) {
+            if (GROUPED) {
+                a.c[v * a.rows + row] = round_out(al, s, a.out_bf16);
+            } else {
+                a.c[(grp * a.rows + row) * a.nvec + (v - v0)] = round_out(al, s, a.out_bf16);
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------- split-K second pass
+// c[i] = out(alpha[i / per_group] * (((0 + p[0][i]) + p[1][i]) + ...)).
+__global__ void __launch_bounds__(kReduceThreads)
+mma_splitk_reduce(const float *__restrict__ part, const float *__restrict__ alpha,
+                  uint16_t *__restrict__ c, int64_t total, int64_t per_group, int64_t ksplit,
+                  int32_t out_bf16) {
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * kReduceThreads + threadIdx.x;
+    if (i >= total) return;
+    float s = 0.0f;
+    for (int64_t j = 0; j < ksplit; ++j) s += part[j * total + i];
+    const float al = alpha ? alpha[i / per_group] : 1.0f;
+    c[i] = round_out(al, s, out_bf16);
+}
+
+// ---------------------------------------------------------------- host side
+struct Variant {
+    int R, U, W;
+};
+// {row tiles per wave, windows in flight, waves per workgroup}
+constexpr Variant kVariants[] = {
+    {1, 4, 4}, {1, 4, 8}, {2, 4, 4}, {2, 2, 8}, {1, 2, 8}, {2, 2, 4},
+};
+constexpr int kNumVariants = static_cast<int>(sizeof(kVariants) / sizeof(kVariants[0]));
+
+typedef void (*MmaKernel)(const MmaArgs);
+
+template <bool G>
+MmaKernel fast_kernel(int v) {
+    switch (v) {
+    case 0: return mma_stream<1, 4, 4, G>;
+    case 1: return mma_stream<1, 4, 8, G>;
+    case 2: return mma_stream<2, 4, 4, G>;
+    case 3: return mma_stream<2, 2, 8, G>;
+    case 4: return mma_stream<1, 2, 8, G>;
+    case 5: return mma_stream<2, 2, 4, G>;
+    default: return nullptr;
+    }
+}
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+struct Plan {
+    int path;
+    int variant;
+    int64_t ksplit, kchunk, row_blocks, groups;
+    int threads;
+    size_t ws_bytes;
+};
+
+bool fits_int64_product(int64_t a, int64_t b) { return a == 0 || b <= INT64_MAX / a; }
+
+// groups x rows x (k/2) and the other byte counts within int64, outputs < 2^31.
+int check_dims(int64_t groups, int64_t rows, int64_t nvec, int64_t k, bool allow_zero_vec) {
+    if (groups < 1 || rows < 1 || nvec < (allow_zero_vec ? 0 : 1) || k < 16 || k % 16 != 0)
+        return NVFP4_GEMV_ERR_BAD_SHAPE;
+    if (k >= (int64_t(1) << 31)) return NVFP4_GEMV_ERR_BAD_SHAPE;
+    if (!fits_int64_product(groups, rows) || !fits_int64_product(groups * rows, k / 2))
+        return NVFP4_GEMV_ERR_BAD_SHAPE;
+    if (!fits_int64_product(nvec, k / 2)) return NVFP4_GEMV_ERR_BAD_SHAPE;
+    return NVFP4_GEMV_OK;
+}
+
+int make_plan(int64_t groups, int64_t rows, int64_t nvec_per_group, int64_t k, bool aligned,
+              bool grouped, const nvfp4_gemv_tuning_t *t, Plan *p) {
+    nvfp4_gemv_tuning_t tun = {NVFP4_GEMV_PATH_AUTO, 0, 0, 0};
+    if (t) tun = *t;
+    if (tun.reserved != 0 || tun.path < NVFP4_GEMV_PATH_AUTO || tun.path > NVFP4_GEMV_PATH_GENERIC ||
+        tun.variant < 0 || tun.variant > kNumVariants || tun.ksplit < 0)
+        return NVFP4_GEMV_ERR_BAD_TUNING;
+    const bool fast_ok = aligned && k % 32 == 0 && k <= kMaxFastK;
+    if (tun.path == NVFP4_GEMV_PATH_FAST && !fast_ok) return NVFP4_GEMV_ERR_BAD_TUNING;
+    if (tun.path == NVFP4_GEMV_PATH_GENERIC && (tun.variant != 0 || tun.ksplit > 1))
+        return NVFP4_GEMV_ERR_BAD_TUNING;
+    if (grouped && tun.ksplit > 1) return NVFP4_GEMV_ERR_BAD_TUNING;
+    const bool fast = tun.path != NVFP4_GEMV_PATH_GENERIC && fast_ok;
+    p->path = fast ? NVFP4_GEMV_PATH_FAST : NVFP4_GEMV_PATH_GENERIC;
+    if (!fast) {
+        p->variant = 0;
+        p->ksplit = 1;
+        p->kchunk = k;
+        p->row_blocks = ceil_div(rows, kGenericWaves);
+        p->threads = kGenericWaves * kWave;
+    } else {
+        p->variant = tun.variant > 0 ? tun.variant - 1 : 0;
+        const Variant &v = kVariants[p->variant];
+        p->row_blocks = ceil_div(rows, int64_t(v.R) * kTile);
+        p->threads = v.W * kWave;
+        int64_t ks = 1;
+        if (tun.ksplit > 0) {
+            ks = tun.ksplit;
+        } else if (!grouped) {
+            // split K while there are too few workgroups, keeping at least one
+            // window per wave in every split
+            const int64_t wg1 = groups * p->row_blocks;
+            const int64_t most = k / (int64_t(v.W) * kWinElems);
+            while (wg1 * ks < kTargetGroups && ks * 2 <= most) ks *= 2;
+        }
+        if (ks > k / 32) return NVFP4_GEMV_ERR_BAD_TUNING;
+        int64_t kchunk = ceil_div(ceil_div(k, ks), 32) * 32;
+        p->ksplit = ceil_div(k, kchunk);
+        p->kchunk = kchunk;
+    }
+    p->groups = groups * p->row_blocks * p->ksplit;
+    if (p->groups >= (int64_t(1) << 31)) return NVFP4_GEMV_ERR_BAD_SHAPE;
+    p->ws_bytes = p->ksplit > 1
+                      ? static_cast<size_t>(p->ksplit) * groups * rows * nvec_per_group * sizeof(float)
+                      : 0;
+    return NVFP4_GEMV_OK;
+}
+
+bool overlaps(const void *p, size_t pn, const void *q, size_t qn) {
+    if (!p || !q || pn == 0 || qn == 0) return false;
+    const uintptr_t a = reinterpret_cast<uintptr_t>(p), b = reinterpret_cast<uintptr_t>(q);
+    return a < b + qn && b < a + pn;
+}
+
+bool aligned_ptrs(const void *w, const void *sw, const void *v, const void *sv) {
+    auto al = [](const void *p, uintptr_t n) { return reinterpret_cast<uintptr_t>(p) % n == 0; };
+    return al(w, 16) && al(v, 16) && al(sw, 2) && al(sv, 2);
+}
+
+int launch(const Plan &p, bool grouped, MmaArgs a, hipStream_t stream) {
+    a.kchunk = p.kchunk;
+    a.row_blocks = p.row_blocks;
+    const void *fn;
+    if (p.path == NVFP4_GEMV_PATH_FAST)
+        fn = reinterpret_cast<const void *>(grouped ? fast_kernel<true>(p.variant)
+                                                    : fast_kernel<false>(p.variant));
+    else
+        fn = reinterpret_cast<const void *>(grouped ? mma_generic<true> : mma_generic<false>);
+    void *args[] = {&a};
+    hipError_t e = hipLaunchKernel(fn, dim3(static_cast<uint32_t>(p.groups)), dim3(p.threads), args,
+                                   0, stream);
+    if (e != hipSuccess) return NVFP4_GEMV_ERR_LAUNCH;
+    if (a.part != nullptr) {
+        const float *part = a.part;
+        const float *alpha = a.alpha;
+        uint16_t *c = a.c;
+        int64_t total = a.groups * a.rows * a.nvec, per_group = a.rows * a.nvec, ks = p.ksplit;
+        int32_t bf = a.out_bf16;
+        void *rargs[] = {&part, &alpha, &c, &total, &per_group, &ks, &bf};
+        e = hipLaunchKernel(reinterpret_cast<const void *>(mma_splitk_reduce),
+                            dim3(static_cast<uint32_t>(ceil_div(total, kReduceThreads))),
+                            dim3(kReduceThreads), rargs, 0, stream);
+        if (e != hipSuccess) return NVFP4_GEMV_ERR_LAUNCH;
+    }
+    return NVFP4_GEMV_OK;
+}
+
+int validate_smalln(const uint8_t *A, const uint8_t *sfA, const uint8_t *B, const uint8_t *sfB,
+                    const float *alpha, uint16_t *c, int64_t l, int64_t m, int64_t n, int64_t k,
+                    int32_t out_type) {
+    if (!A || !sfA || !B || !sfB || !c) return NVFP4_GEMV_ERR_NULL_POINTER;
+    if (out_type != NVFP4_OUT_F16 && out_type != NVFP4_OUT_BF16) return NVFP4_GEMV_ERR_BAD_ARGUMENT;
+    int s = check_dims(l, m, n, k, false);
+    if (s != NVFP4_GEMV_OK) return s;
+    if (!fits_int64_product(l, n) || !fits_int64_product(l * n, k / 2) ||
+        !fits_int64_product(l * m, n) || l * m * n >= (int64_t(1) << 31))
+        return NVFP4_GEMV_ERR_BAD_SHAPE;
+    if (reinterpret_cast<uintptr_t>(c) % 2 != 0 || reinterpret_cast<uintptr_t>(alpha) % 4 != 0)
+        return NVFP4_GEMV_ERR_ALIGNMENT;
+    const size_t cn = static_cast<size_t>(l * m * n) * 2;
+    if (overlaps(c, cn, A, static_cast<size_t>(l * m) * (k / 2)) ||
+        overlaps(c, cn, sfA, static_cast<size_t>(l * m) * (k / 16)) ||
+        overlaps(c, cn, B, static_cast<size_t>(l * n) * (k / 2)) ||
+        overlaps(c, cn, sfB, static_cast<size_t>(l * n) * (k / 16)) ||
+        overlaps(c, cn, alpha, static_cast<size_t>(l) * 4))
+        return NVFP4_GEMV_ERR_ALIAS;
+    return NVFP4_GEMV_OK;
+}
+
+int validate_grouped(const uint8_t *X, const uint8_t *sfX, const uint8_t *W, const uint8_t *sfW,
+                     const int32_t *offsets, const float *gs_x, const float *gs_w, uint16_t *c,
+                     int64_t tokens, int64_t experts, int64_t n, int64_t k, int32_t out_type) {
+    if (!X || !sfX || !W || !sfW || !offsets || !c) return NVFP4_GEMV_ERR_NULL_POINTER;
+    if (out_type != NVFP4_OUT_F16 && out_type != NVFP4_OUT_BF16) return NVFP4_GEMV_ERR_BAD_ARGUMENT;
+    int s = check_dims(experts, n, tokens, k, true);
+    if (s != NVFP4_GEMV_OK) return s;
+    if (!fits_int64_product(tokens, n) || tokens * n >= (int64_t(1) << 31))
+        return NVFP4_GEMV_ERR_BAD_SHAPE;
+    auto mis = [](const void *p, uintptr_t a) { return reinterpret_cast<uintptr_t>(p) % a != 0; };
+    if (mis(c, 2) || mis(offsets, 4) || mis(gs_x, 4) || mis(gs_w, 4)) return NVFP4_GEMV_ERR_ALIGNMENT;
+    const size_t cn = static_cast<size_t>(tokens * n) * 2;
+    if (overlaps(c, cn, X, static_cast<size_t>(tokens) * (k / 2)) ||
+        overlaps(c, cn, sfX, static_cast<size_t>(tokens) * (k / 16)) ||
+        overlaps(c, cn, W, static_cast<size_t>(experts * n) * (k / 2)) ||
+        overlaps(c, cn, sfW, static_cast<size_t>(experts * n) * (k / 16)) ||
+        overlaps(c, cn, offsets, static_cast<size_t>(experts) * 4) ||
+        overlaps(c, cn, gs_x, static_cast<size_t>(experts) * 4) ||
+        overlaps(c, cn, gs_w, static_cast<size_t>(experts) * 4))
+        return NVFP4_GEMV_ERR_ALIAS;
+    return NVFP4_GEMV_OK;
+}
+
+MmaArgs smalln_args(const uint8_t *A, const uint8_t *sfA, const uint8_t *B, const uint8_t *sfB,
+                    const float *alpha, uint16_t *c, int64_t l, int64_t m, int64_t n, int64_t k,
+                    int32_t out_type, float *part) {
+    MmaArgs a = {};
+    a.W = A;
+    a.sW = sfA;
+    a.V = B;
+    a.sV = sfB;
+    a.alpha = alpha;
+    a.c = c;
+    a.part = part;
+    a.groups = l;
+    a.rows = m;
+    a.nvec = n;
+    a.k = k;
+    a.out_bf16 = out_type == NVFP4_OUT_BF16;
+    return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+int nvfp4_mma_num_variants(void) { return kNumVariants; }
+
+int nvfp4_mma_variant_info(int v, int32_t *row_tiles_per_wave, int32_t *windows_in_flight,
+                           int32_t *waves_per_group) {
+    if (!row_tiles_per_wave || !windows_in_flight || !waves_per_group)
+        return NVFP4_GEMV_ERR_NULL_POINTER;
+    if (v < 1 || v > kNumVariants) return NVFP4_GEMV_ERR_BAD_TUNING;
+    *row_tiles_per_wave = kVariants[v - 1].R;
+    *windows_in_flight = kVariants[v - 1].U;
+    *waves_per_group = kVariants[v - 1].W;
+    return NVFP4_GEMV_OK;
+}
+
+int nvfp4_gemm_smalln_plan(int64_t l, int64_t m, int64_t n, int64_t k, int aligned,
+                           const nvfp4_gemv_tuning_t *in, nvfp4_gemv_tuning_t *out,
+                           size_t *workspace_bytes) {
+    if (!out || !workspace_bytes) return NVFP4_GEMV_ERR_NULL_POINTER;
+    int s = check_dims(l, m, n, k, false);
+    if (s != NVFP4_GEMV_OK) return s;
+    Plan p;
+    s = make_plan(l, m, n, k, aligned != 0, false, in, &p);
+    if (s != NVFP4_GEMV_OK) return s;
+    out->path = p.path;
+    out->variant = p.path == NVFP4_GEMV_PATH_FAST ? p.variant + 1 : 0;
+    out->ksplit = static_cast<int32_t>(p.ksplit);
+    out->reserved = 0;
+    *workspace_bytes = p.ws_bytes;
+    return NVFP4_GEMV_OK;
+}
+
+int nvfp4_gemm_smalln_launch_tuned(const uint8_t *A_packed, const uint8_t *sfA,
+                                   const uint8_t *B_packed, const uint8_t *sfB,
+                                   const float *alpha, uint16_t *c, int64_t l, int64_t m,
+                                   int64_t n, int64_t k, int32_t out_type,
+                                   const nvfp4_gemv_tuning_t *tuning, void *workspace,
+                                   size_t workspace_bytes, void *stream) {
+    int s = validate_smalln(A_packed, sfA, B_packed, sfB, alpha, c, l, m, n, k, out_type);
+    if (s != NVFP4_GEMV_OK) return s;
+    Plan p;
+    s = make_plan(l, m, n, k, aligned_ptrs(A_packed, sfA, B_packed, sfB), false, tuning, &p);
+    if (s != NVFP4_GEMV_OK) return s;
+    float *part = nullptr;
+    if (p.ws_bytes > 0) {
+        if (!workspace || workspace_bytes < p.ws_bytes) return NVFP4_GEMV_ERR_WORKSPACE;
+        if (reinterpret_cast<uintptr_t>(workspace) % 4 != 0) return NVFP4_GEMV_ERR_ALIGNMENT;
+        part = static_cast<float *>(workspace);
+    }
+    return launch(p, false,
+                  smalln_args(A_packed, sfA, B_packed, sfB, alpha, c, l, m, n, k, out_type, part),
+                  static_cast<hipStream_t>(stream));
+}
+
+int nvfp4_gemm_smalln_launch(const uint8_t *A_packed, const uint8_t *sfA, const uint8_t *B_packed,
+                             const uint8_t *sfB, const float *alpha, uint16_t *c, int64_t l,
+                             int64_t m, int64_t n, int64_t k, int32_t out_type, void *stream) {
+    int s = validate_smalln(A_packed, sfA, B_packed, sfB, alpha, c, l, m, n, k, out_type);
+    if (s != NVFP4_GEMV_OK) return s;
+    Plan p;
+    s = make_plan(l, m, n, k, aligned_ptrs(A_packed, sfA, B_packed, sfB), false, nullptr, &p);
+    if (s != NVFP4_GEMV_OK) return s;
+    float *part = nullptr;
+    if (p.ws_bytes > 0) {
+        int dev = -1;
+        if (hipGetDevice(&dev) != hipSuccess) return NVFP4_GEMV_ERR_DEVICE;
+        part = static_cast<float *>(nvfp4_stream_workspace(dev, stream, p.ws_bytes));
+        if (!part) return NVFP4_GEMV_ERR_WORKSPACE;
+    }
+    return launch(p, false,
+                  smalln_args(A_packed, sfA, B_packed, sfB, alpha, c, l, m, n, k, out_type, part),
+                  static_cast<hipStream_t>(stream));
+}
+
+int nvfp4_grouped_gemv_launch_tuned(const uint8_t *X_packed, const uint8_t *sfX,
+                                    const uint8_t *W_packed, const uint8_t *sfW,
+                                    const int32_t *offsets, const float *gs_x, const float *gs_w,
+                                    uint16_t *c, int64_t tokens, int64_t experts, int64_t n,
+                                    int64_t k, int32_t out_type, const nvfp4_gemv_tuning_t *tuning,
+                                    void *stream) {
+    int s = validate_grouped(X_packed, sfX, W_packed, sfW, offsets, gs_x, gs_w, c, tokens, experts,
+                             n, k, out_type);
+    if (s != NVFP4_GEMV_OK) return s;
+    Plan p;
+    s = make_plan(experts, n, 0, k, aligned_ptrs(W_packed, sfW, X_packed, sfX), true, tuning, &p);
+    if (s != NVFP4_GEMV_OK) return s;
+    if (tokens == 0) return NVFP4_GEMV_OK;
+    MmaArgs a = {};
+    a.W = W_packed;
+    a.sW = sfW;
+    a.V = X_packed;
+    a.sV = sfX;
+    a.offsets = offsets;
+    a.gs_v = gs_x;
+    a.gs_w = gs_w;
+    a.c = c;
+    a.groups = experts;
+    a.rows = n;
+    a.nvec = tokens;
+    a.k = k;
+    a.out_bf16 = out_type == NVFP4_OUT_BF16;
+    return launch(p, true, a, static_cast<hipStream_t>(stream));
+}
+
+int nvfp4_grouped_gemv_launch(const uint8_t *X_packed, const uint8_t *sfX, const uint8_t *W_packed,
+                              const uint8_t *sfW, const int32_t *offsets, const float *gs_x,
+                              const float *gs_w, uint16_t *c, int64_t tokens, int64_t experts,
+                              int64_t n, int64_t k, int32_t out_type, void *stream) {
+    return nvfp4_grouped_gemv_launch_tuned(X_packed, sfX, W_packed, sfW, offsets, gs_x, gs_w, c,
+                                           tokens, experts, n, k, out_type, nullptr, stream);
+}
+
+}  // extern "C"

@@ -29,17 +29,25 @@ def run_gpu(dops, l, m, k, tuning=None, use_alpha=True, mode="launch", stream=No
 
 
 def f16_ordered(bits):
-    """Map fp16 bit patterns to integers whose difference counts ulps."""
+    """Map fp16 (or bf16) bit patterns to integers whose difference counts ulps."""
     b = np.asarray(bits, dtype=np.uint16).astype(np.int64)
     mag = b & 0x7FFF
     return np.where(b & 0x8000, -mag, mag)
 
 
-def assert_bits_equal(got, want, what=""):
+def nan_mask(bits, fmt="f16"):
+    """NaN positions of fp16 or bf16 bit patterns."""
+    b = np.asarray(bits, dtype=np.uint16)
+    if fmt == "bf16":
+        return (b & 0x7FFF) > 0x7F80
+    return (b & 0x7FFF) > 0x7C00
+
+
+def assert_bits_equal(got, want, what="", fmt="f16"):
     got = np.asarray(got, dtype=np.uint16)
     want = np.asarray(want, dtype=np.uint16)
-    gnan = np.isnan(got.view(np.float16))
-    wnan = np.isnan(want.view(np.float16))
+    gnan = nan_mask(got, fmt)
+    wnan = nan_mask(want, fmt)
     assert np.array_equal(gnan, wnan), f"{what}: NaN positions differ"
     diff = (got != want) & ~gnan
     if diff.any():
@@ -48,12 +56,20 @@ def assert_bits_equal(got, want, what=""):
         raise AssertionError(f"{what}: {int(diff.sum())} of {got.size} outputs differ, e.g. {details}")
 
 
-def assert_within_tolerance(got, want, ulps=2, rel=1e-3, what=""):
-    """|got - want| <= max(ulps fp16 ulps, rel * |want|), NaN where the oracle has NaN."""
+def bits_to_f64(bits, fmt="f16"):
+    b = np.asarray(bits, dtype=np.uint16)
+    if fmt == "bf16":
+        return (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return b.view(np.float16).astype(np.float64)
+
+
+def assert_within_tolerance(got, want, ulps=2, rel=1e-3, what="", fmt="f16"):
+    """|got - want| <= max(ulps ulps of the output format, rel * |want|), NaN where the
+    oracle has NaN."""
     got = np.asarray(got, dtype=np.uint16)
     want = np.asarray(want, dtype=np.uint16)
-    g = got.view(np.float16).astype(np.float64)
-    w = want.view(np.float16).astype(np.float64)
+    g = bits_to_f64(got, fmt)
+    w = bits_to_f64(want, fmt)
     assert np.array_equal(np.isnan(g), np.isnan(w)), f"{what}: NaN positions differ"
     fin = ~np.isnan(w)
     ulp_ok = np.abs(f16_ordered(got) - f16_ordered(want)) <= ulps

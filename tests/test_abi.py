@@ -218,3 +218,93 @@ def test_bf16x_gemv_validation(lib):
     assert bcall(c=SF) == pd.NVFP4_GEMV_ERR_ALIAS               # c on sfx
     assert bcall(q=AL) == pd.NVFP4_GEMV_ERR_ALIAS               # x_packed on A_scale
     assert bcall(al=GS + 4) == pd.NVFP4_GEMV_ERR_ALIAS          # alpha on x_scale
+
+
+# ---- small-N GEMM and grouped GEMV (validation and plans only)
+
+B_, SB_, OF, GX, GW = 0x15000000, 0x16000000, 0x17000000, 0x18000000, 0x19000000
+
+
+def scall(l=2, m=24, n=4, k=64, a=A, sa=SA, b=B_, sb=SB_, al=AL, c=C, out=0):
+    return pd.load().nvfp4_gemm_smalln_launch(a, sa, b, sb, al, c, l, m, n, k, out, None)
+
+
+def test_smalln_validation(lib):
+    for kw in ("a", "sa", "b", "sb", "c"):
+        assert scall(**{kw: None}) == pd.NVFP4_GEMV_ERR_NULL_POINTER, kw
+    for out in (-1, 2):
+        assert scall(out=out) == pd.NVFP4_GEMV_ERR_BAD_ARGUMENT
+    for l, m, n, k in ((0, 8, 2, 64), (1, 0, 2, 64), (1, 8, 0, 64), (1, 8, 2, 40), (1, 8, 2, 8),
+                       (1 << 12, 1 << 12, 1 << 8, 64)):
+        assert scall(l=l, m=m, n=n, k=k) == pd.NVFP4_GEMV_ERR_BAD_SHAPE, (l, m, n, k)
+    assert scall(c=C + 1) == pd.NVFP4_GEMV_ERR_ALIGNMENT
+    assert scall(al=AL + 2) == pd.NVFP4_GEMV_ERR_ALIGNMENT
+    assert scall(c=A + 10) == pd.NVFP4_GEMV_ERR_ALIAS
+    assert scall(c=B_ + 8) == pd.NVFP4_GEMV_ERR_ALIAS
+    assert scall(c=SB_ - 2) == pd.NVFP4_GEMV_ERR_ALIAS          # c's 192 bytes reach sfB
+
+
+def test_smalln_plans(lib):
+    t, ws = pd.nvfp4_gemm_smalln_plan(1, 7168, 16, 16384)
+    assert t.path == pd.NVFP4_GEMV_PATH_FAST and t.variant >= 1
+    assert ws == (t.ksplit * 7168 * 16 * 4 if t.ksplit > 1 else 0)
+    t, ws = pd.nvfp4_gemm_smalln_plan(2, 100, 3, 48)           # k % 32 != 0
+    assert t.path == pd.NVFP4_GEMV_PATH_GENERIC and t.ksplit == 1 and ws == 0
+    t, _ = pd.nvfp4_gemm_smalln_plan(2, 100, 3, 64, aligned=False)
+    assert t.path == pd.NVFP4_GEMV_PATH_GENERIC
+    n = pd.nvfp4_mma_num_variants()
+    for v in range(1, n + 1):
+        r, u, w = pd.nvfp4_mma_variant_info(v)
+        assert r in (1, 2) and u >= 1 and 1 <= w <= 16
+        t, ws = pd.nvfp4_gemm_smalln_plan(3, 100, 5, 4096, tuning={"variant": v, "ksplit": 3})
+        assert t.variant == v and t.ksplit == 3 and ws == 3 * 3 * 100 * 5 * 4
+    for bad in ({"variant": n + 1}, {"ksplit": 3, "path": pd.NVFP4_GEMV_PATH_GENERIC},
+                {"path": pd.NVFP4_GEMV_PATH_GENERIC, "variant": 1}, {"path": 3}):
+        with pytest.raises(pd.Nvfp4GemvError):
+            pd.nvfp4_gemm_smalln_plan(1, 64, 4, 4096, tuning=bad)
+    with pytest.raises(pd.Nvfp4GemvError):
+        pd.nvfp4_gemm_smalln_plan(1, 64, 4, 64, tuning={"ksplit": 3})   # under 32 elements a split
+    with pytest.raises(pd.Nvfp4GemvError):
+        pd.nvfp4_gemm_smalln_plan(1, 64, 4, 48, tuning={"path": pd.NVFP4_GEMV_PATH_FAST})
+    with pytest.raises(pd.Nvfp4GemvError):
+        pd.nvfp4_mma_variant_info(0)
+
+
+def test_smalln_tuned_needs_workspace(lib):
+    l, m, n, k = 1, 64, 4, 4096
+    t = _binding.Tuning(0, 0, 4, 0)
+    _, need = pd.nvfp4_gemm_smalln_plan(l, m, n, k, tuning=t)
+    assert need == 4 * m * n * 4
+    f = lib.nvfp4_gemm_smalln_launch_tuned
+    assert f(A, SA, B_, SB_, AL, C, l, m, n, k, 0, ctypes.byref(t), None, 0, None) == \
+        pd.NVFP4_GEMV_ERR_WORKSPACE
+    assert f(A, SA, B_, SB_, AL, C, l, m, n, k, 0, ctypes.byref(t), 0x70000000, need - 4, None) == \
+        pd.NVFP4_GEMV_ERR_WORKSPACE
+    assert f(A, SA, B_, SB_, AL, C, l, m, n, k, 0, ctypes.byref(t), 0x70000002, need, None) == \
+        pd.NVFP4_GEMV_ERR_ALIGNMENT
+
+
+def gcall(tokens=8, experts=3, n=32, k=64, x=X, sx=SX, w=A, sw=SA, of=OF, gx=GX, gw=GW, c=C, out=1,
+          tuning=None):
+    if tuning is None:
+        return pd.load().nvfp4_grouped_gemv_launch(x, sx, w, sw, of, gx, gw, c, tokens, experts, n,
+                                                   k, out, None)
+    return pd.load().nvfp4_grouped_gemv_launch_tuned(x, sx, w, sw, of, gx, gw, c, tokens, experts,
+                                                     n, k, out, ctypes.byref(tuning), None)
+
+
+def test_grouped_validation(lib):
+    for kw in ("x", "sx", "w", "sw", "of", "c"):
+        assert gcall(**{kw: None}) == pd.NVFP4_GEMV_ERR_NULL_POINTER, kw
+    assert gcall(out=3) == pd.NVFP4_GEMV_ERR_BAD_ARGUMENT
+    for tokens, experts, n, k in ((-1, 3, 32, 64), (8, 0, 32, 64), (8, 3, 0, 64), (8, 3, 32, 40),
+                                  (1 << 20, 3, 1 << 12, 64)):
+        assert gcall(tokens=tokens, experts=experts, n=n, k=k) == pd.NVFP4_GEMV_ERR_BAD_SHAPE
+    assert gcall(c=C + 1) == pd.NVFP4_GEMV_ERR_ALIGNMENT
+    assert gcall(of=OF + 2) == pd.NVFP4_GEMV_ERR_ALIGNMENT
+    assert gcall(gx=GX + 1) == pd.NVFP4_GEMV_ERR_ALIGNMENT
+    assert gcall(c=A + 64) == pd.NVFP4_GEMV_ERR_ALIAS               # c inside the weights
+    assert gcall(c=OF - 4) == pd.NVFP4_GEMV_ERR_ALIAS               # c's 512 bytes reach offsets
+    assert gcall(c=GW) == pd.NVFP4_GEMV_ERR_ALIAS
+    assert gcall(tuning=_binding.Tuning(0, 0, 2, 0)) == pd.NVFP4_GEMV_ERR_BAD_TUNING   # no K split
+    assert gcall(tuning=_binding.Tuning(1, 0, 0, 0), k=48) == pd.NVFP4_GEMV_ERR_BAD_TUNING

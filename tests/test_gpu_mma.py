@@ -1,0 +1,280 @@
+"""GPU parity of the small-N GEMM and the grouped (MoE) GEMV: the HIP library,
+called through its C ABI, against the CPU oracle (``oracle.multi``).
+
+Integer-coded inputs must match bit for bit in both output formats (every fp32
+partial sum is exact, whatever order the matrix cores add in); Gaussian
+quantised inputs must agree within max(2 ulps of the output format, 1e-3
+relative).
+"""
+import numpy as np
+import pytest
+import torch
+
+import precision_decode_amd as pd
+import workloads
+from gpu_util import assert_bits_equal, assert_within_tolerance, to_device
+from oracle import multi
+from oracle import quantize as oq
+
+pytestmark = [pytest.mark.gpu, pytest.mark.filterwarnings("ignore::RuntimeWarning")]
+
+FMT = {pd.NVFP4_OUT_F16: "f16", pd.NVFP4_OUT_BF16: "bf16"}
+FILL = 0xFFFF   # a NaN pattern in both formats: marks outputs the kernel must not touch
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu_ready():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    pd.load()
+
+
+# ---------------------------------------------------------------- small-N GEMM
+def smalln_ops(l, m, n, k, seed=0):
+    a = workloads.integer_coded(l, m, k, seed=seed, alpha="uniform")
+    b = workloads.integer_coded(l, n, k, seed=seed + 1)
+    return {"A": a["A"], "sfA": a["sfA"], "B": b["A"], "sfB": b["sfA"], "alpha": a["alpha"]}
+
+
+def run_smalln(ops, l, m, n, k, out_type=pd.NVFP4_OUT_F16, tuning=None, use_alpha=True, dev=None):
+    d = dev or to_device(ops)
+    c = torch.full((l, m, n), -1, dtype=torch.int16, device="cuda")
+    alpha = d["alpha"] if use_alpha else None
+    if tuning is None:
+        pd.nvfp4_gemm_smalln_launch(d["A"], d["sfA"], d["B"], d["sfB"], alpha, c, l, m, n, k, out_type)
+    else:
+        _, ws_bytes = pd.nvfp4_gemm_smalln_plan(l, m, n, k, aligned=True, tuning=tuning)
+        ws = torch.empty(max(ws_bytes, 4), dtype=torch.uint8, device="cuda")
+        pd.nvfp4_gemm_smalln_launch_tuned(d["A"], d["sfA"], d["B"], d["sfB"], alpha, c, l, m, n, k,
+                                          out_type, tuning, ws, ws_bytes)
+    torch.cuda.synchronize()
+    return c.cpu().numpy().view(np.uint16)
+
+
+def oracle_smalln(ops, l, m, n, k, out_type=pd.NVFP4_OUT_F16, use_alpha=True):
+    return multi.gemm_smalln(ops["A"], ops["sfA"], ops["B"], ops["sfB"],
+                             ops["alpha"] if use_alpha else None, l, m, n, k, FMT[out_type])
+
+
+@pytest.mark.parametrize("name", list(workloads.SMALLN_CONFIGS))
+@pytest.mark.parametrize("out_type", [pd.NVFP4_OUT_F16, pd.NVFP4_OUT_BF16])
+def test_smalln_configs_bit_exact(name, out_type):
+    cfg = workloads.SMALLN_CONFIGS[name]
+    ops = workloads.smalln_operands(cfg)
+    want = oracle_smalln(ops, cfg.l, cfg.m, cfg.n, cfg.k, out_type)
+    got = run_smalln(ops, cfg.l, cfg.m, cfg.n, cfg.k, out_type)
+    assert_bits_equal(got, want, name, FMT[out_type])
+
+
+SMALLN_SHAPES = [
+    (1, 1, 1, 32), (2, 80, 3, 256), (1, 17, 16, 2080), (3, 33, 5, 4096), (1, 100, 17, 1024),
+    (2, 48, 2, 160), (1, 7, 40, 512), (1, 300, 16, 16384),
+]
+
+
+@pytest.mark.parametrize("l,m,n,k", SMALLN_SHAPES)
+def test_smalln_default_plan_shapes(l, m, n, k):
+    ops = smalln_ops(l, m, n, k, seed=l + m + n + k)
+    assert_bits_equal(run_smalln(ops, l, m, n, k), oracle_smalln(ops, l, m, n, k), f"{(l, m, n, k)}")
+
+
+@pytest.mark.parametrize("variant", range(1, 7))
+@pytest.mark.parametrize("ksplit", [1, 3])
+def test_smalln_every_variant(variant, ksplit):
+    assert pd.nvfp4_mma_num_variants() == 6
+    l, m, n, k = 2, 75, 11, 2080       # ragged rows, k not a multiple of the 128-element window
+    ops = smalln_ops(l, m, n, k, seed=variant * 10 + ksplit)
+    want = oracle_smalln(ops, l, m, n, k, pd.NVFP4_OUT_BF16)
+    tuning = {"path": pd.NVFP4_GEMV_PATH_FAST, "variant": variant, "ksplit": ksplit}
+    got = run_smalln(ops, l, m, n, k, pd.NVFP4_OUT_BF16, tuning=tuning)
+    assert_bits_equal(got, want, f"variant {variant} ksplit {ksplit}", "bf16")
+
+
+@pytest.mark.parametrize("l,m,n,k", [(1, 9, 4, 48), (2, 21, 3, 2064), (1, 5, 18, 80)])
+def test_smalln_generic_path(l, m, n, k):
+    ops = smalln_ops(l, m, n, k, seed=7)
+    got = run_smalln(ops, l, m, n, k, tuning={"path": pd.NVFP4_GEMV_PATH_GENERIC})
+    assert_bits_equal(got, oracle_smalln(ops, l, m, n, k), "generic")
+
+
+def test_smalln_misaligned_pointers_take_generic_path():
+    l, m, n, k = 1, 40, 6, 256
+    ops = smalln_ops(l, m, n, k, seed=8)
+    d = to_device(ops)
+    big = torch.zeros(d["B"].numel() + 3, dtype=torch.uint8, device="cuda")
+    big[3:] = d["B"].reshape(-1)
+    d["B"] = big[3:]                       # 3 bytes past a 16-byte boundary
+    assert pd.nvfp4_gemm_smalln_plan(l, m, n, k, aligned=False)[0].path == pd.NVFP4_GEMV_PATH_GENERIC
+    got = run_smalln(ops, l, m, n, k, dev=d)
+    assert_bits_equal(got, oracle_smalln(ops, l, m, n, k), "misaligned B")
+
+
+def test_smalln_special_values_every_variant():
+    """Every finite scale code (subnormal, negative, up to 448) on arbitrary
+    bytes, plus NaN codes planted in one weight row and one vector.  Terms then
+    span many binades, so the fp32 sums are not exact: the tolerance applies,
+    and NaN positions must agree exactly."""
+    l, m, n, k = 2, 40, 7, 512
+    finite = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+    a = workloads.random_bytes(l, m, k, seed=11, scale_codes=finite)
+    b = workloads.random_bytes(l, n, k, seed=12, scale_codes=finite)
+    ops = {"A": a["A"], "sfA": a["sfA"], "B": b["A"], "sfB": b["sfA"], "alpha": a["alpha"]}
+    ops["sfA"][0, 3, 1] = 0x7F
+    ops["sfB"][1, 2, 5] = 0xFF
+    want = oracle_smalln(ops, l, m, n, k)
+    nan = np.isnan(want.view(np.float16))
+    assert nan[0, 3].all() and nan[1, :, 2].all() and nan.sum() == n + m
+    for v in range(1, pd.nvfp4_mma_num_variants() + 1):
+        got = run_smalln(ops, l, m, n, k, tuning={"variant": v})
+        assert_within_tolerance(got, want, what=f"special values variant {v}")
+
+
+def test_smalln_gaussian_within_tolerance():
+    l, m, n, k = 4, 512, 8, 4096
+    rawA = workloads.gaussian_bf16(l, m, k, seed=21)["A"]
+    rawB = workloads.gaussian_bf16(l, n, k, seed=22)["A"]
+    ops = {"A": np.empty((l, m, k // 2), np.uint8), "sfA": np.empty((l, m, k // 16), np.uint8),
+           "B": np.empty((l, n, k // 2), np.uint8), "sfB": np.empty((l, n, k // 16), np.uint8),
+           "alpha": np.empty(l, np.float32)}
+    for b in range(l):
+        ops["A"][b], ops["sfA"][b], ga = oq.quantize_nvfp4(rawA[b])
+        ops["B"][b], ops["sfB"][b], gb = oq.quantize_nvfp4(rawB[b])
+        ops["alpha"][b] = np.float32(ga * gb)
+    for out_type in (pd.NVFP4_OUT_F16, pd.NVFP4_OUT_BF16):
+        want = oracle_smalln(ops, l, m, n, k, out_type)
+        got = run_smalln(ops, l, m, n, k, out_type)
+        assert_within_tolerance(got, want, what="gaussian small-N", fmt=FMT[out_type])
+        print(f"gaussian small-N {FMT[out_type]}: {float(np.mean(got == want)):.6f} bit-identical")
+
+
+def test_smalln_zero_scales_give_positive_zero_and_alpha_null():
+    l, m, n, k = 1, 32, 4, 256
+    ops = smalln_ops(l, m, n, k, seed=13)
+    ops["sfB"][:] = 0
+    got = run_smalln(ops, l, m, n, k, use_alpha=False)
+    assert np.all(got == 0)
+    ops = smalln_ops(l, m, n, k, seed=14)
+    got = run_smalln(ops, l, m, n, k, use_alpha=False)
+    assert_bits_equal(got, oracle_smalln(ops, l, m, n, k, use_alpha=False), "alpha NULL")
+
+
+def test_smalln_negative_zero_codes_give_positive_zero():
+    l, m, n, k = 1, 16, 16, 128
+    ops = smalln_ops(l, m, n, k, seed=15)
+    ops["A"][:] = 0x88                     # every weight code is -0
+    got = run_smalln(ops, l, m, n, k)
+    assert np.all(got == 0x0000)
+
+
+def test_smalln_run_to_run_determinism_with_split():
+    l, m, n, k = 1, 200, 16, 8192
+    rawA = workloads.gaussian_bf16(1, m, k, seed=31)["A"][0]
+    rawB = workloads.gaussian_bf16(1, n, k, seed=32)["A"][0]
+    A, sA, _ = oq.quantize_nvfp4(rawA)
+    B, sB, _ = oq.quantize_nvfp4(rawB)
+    ops = {"A": A[None], "sfA": sA[None], "B": B[None], "sfB": sB[None],
+           "alpha": np.ones(1, np.float32)}
+    d = to_device(ops)
+    tuning = {"ksplit": 4}
+    first = run_smalln(ops, l, m, n, k, tuning=tuning, dev=d)
+    for _ in range(3):
+        assert np.array_equal(run_smalln(ops, l, m, n, k, tuning=tuning, dev=d), first)
+
+
+# ---------------------------------------------------------------- grouped (MoE) GEMV
+def run_grouped(ops, tokens, experts, n, k, out_type=pd.NVFP4_OUT_BF16, tuning=None, scales=True):
+    d = to_device(ops)
+    c = torch.full((max(tokens, 1), n), FILL - 65536, dtype=torch.int16, device="cuda")
+    gx, gw = (d["gs_x"], d["gs_w"]) if scales else (None, None)
+    args = (d["X"], d["sfX"], d["W"], d["sfW"], d["offsets"], gx, gw, c, tokens, experts, n, k,
+            out_type)
+    if tuning is None:
+        pd.nvfp4_grouped_gemv_launch(*args)
+    else:
+        pd.nvfp4_grouped_gemv_launch_tuned(*args, tuning)
+    torch.cuda.synchronize()
+    return c.cpu().numpy().view(np.uint16)[:tokens]
+
+
+def oracle_grouped(ops, tokens, experts, n, k, out_type=pd.NVFP4_OUT_BF16, scales=True):
+    return multi.grouped_gemv(ops["X"], ops["sfX"], ops["W"], ops["sfW"], ops["offsets"],
+                              ops["gs_x"] if scales else None, ops["gs_w"] if scales else None,
+                              tokens, experts, n, k, FMT[out_type], fill=FILL)
+
+
+def grouped_ops(counts, n, k, seed=0):
+    experts, tokens = len(counts), int(sum(counts))
+    w = workloads.integer_coded(experts, n, k, seed=seed)
+    x = workloads.integer_coded(1, max(tokens, 1), k, seed=seed + 1)
+    rng = np.random.default_rng(seed + 2)
+    return {"X": x["A"][0][:max(tokens, 1)], "sfX": x["sfA"][0][:max(tokens, 1)], "W": w["A"],
+            "sfW": w["sfA"], "offsets": np.cumsum(counts).astype(np.int32),
+            "gs_x": rng.uniform(0.5, 2, experts).astype(np.float32),
+            "gs_w": rng.uniform(0.5, 2, experts).astype(np.float32)}
+
+
+@pytest.mark.parametrize("name", list(workloads.MOE_CONFIGS))
+@pytest.mark.parametrize("out_type", [pd.NVFP4_OUT_F16, pd.NVFP4_OUT_BF16])
+def test_grouped_configs_bit_exact(name, out_type):
+    cfg = workloads.MOE_CONFIGS[name]
+    ops = workloads.moe_operands(cfg)
+    want = oracle_grouped(ops, cfg.tokens, cfg.experts, cfg.n, cfg.k, out_type)
+    got = run_grouped(ops, cfg.tokens, cfg.experts, cfg.n, cfg.k, out_type)
+    assert_bits_equal(got, want, name, FMT[out_type])
+
+
+@pytest.mark.parametrize("counts,n,k", [
+    ([3, 0, 1, 5], 40, 256),          # an expert without tokens, ragged rows
+    ([0, 0, 37], 17, 2080),           # more than two passes of 16 tokens
+    ([1], 1, 32),
+    ([16, 16], 33, 512),
+    ([2, 1, 0, 0, 4, 9], 96, 1024),
+])
+@pytest.mark.parametrize("variant", [0, 1, 2, 3, 4, 5, 6])
+def test_grouped_shapes_every_variant(counts, n, k, variant):
+    ops = grouped_ops(counts, n, k, seed=sum(counts) + n + variant)
+    tokens, experts = int(sum(counts)), len(counts)
+    want = oracle_grouped(ops, tokens, experts, n, k)
+    got = run_grouped(ops, tokens, experts, n, k, tuning={"variant": variant})
+    assert_bits_equal(got, want, f"{counts} n={n} k={k} v={variant}", "bf16")
+
+
+def test_grouped_rows_past_the_last_offset_untouched():
+    counts, n, k = [2, 3], 24, 256
+    ops = grouped_ops(counts, n, k, seed=41)
+    tokens = 9                                    # tokens 5..8 belong to no expert
+    extra = workloads.integer_coded(1, tokens, k, seed=42)
+    ops["X"], ops["sfX"] = extra["A"][0], extra["sfA"][0]
+    got = run_grouped(ops, tokens, 2, n, k)
+    want = oracle_grouped(ops, tokens, 2, n, k)
+    assert np.all(got[5:] == FILL)
+    assert_bits_equal(got[:5], want[:5], "covered rows", "bf16")
+
+
+def test_grouped_generic_path_and_null_scales():
+    counts, n, k = [4, 0, 3], 20, 208            # k % 32 == 16: generic kernel
+    ops = grouped_ops(counts, n, k, seed=43)
+    for scales in (True, False):
+        want = oracle_grouped(ops, 7, 3, n, k, scales=scales)
+        got = run_grouped(ops, 7, 3, n, k, scales=scales)
+        assert_bits_equal(got, want, f"generic scales={scales}", "bf16")
+    ops = grouped_ops(counts, n, 256, seed=44)
+    got = run_grouped(ops, 7, 3, n, 256, tuning={"path": pd.NVFP4_GEMV_PATH_GENERIC})
+    assert_bits_equal(got, oracle_grouped(ops, 7, 3, n, 256), "generic forced", "bf16")
+
+
+def test_grouped_out_of_range_offsets_stay_in_bounds():
+    """Offsets past the token count are clamped on the device: the call reads
+    and writes only the arrays it was given."""
+    counts, n, k = [3, 2], 16, 128
+    ops = grouped_ops(counts, n, k, seed=45)
+    ops["offsets"] = np.array([3, 1000], dtype=np.int32)
+    got = run_grouped(ops, 5, 2, n, k)
+    ops["offsets"] = np.array([3, 5], dtype=np.int32)
+    assert_bits_equal(got, oracle_grouped(ops, 5, 2, n, k), "clamped offsets", "bf16")
+
+
+def test_grouped_zero_tokens_is_a_no_op():
+    ops = grouped_ops([0, 0], 16, 64, seed=46)
+    got = run_grouped(ops, 0, 2, 16, 64)
+    assert got.size == 0
