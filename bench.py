@@ -22,9 +22,13 @@ Other paths (--path), each printing its own JSON line of the same form:
   quantize     the BF16 -> NVFP4 activation quantiser on a bf16 activation
                batch (--act-config tokens | decode_x)
   gemv_bf16x   the GEMV fed by a bf16 activation: quantiser + GEMV per step
+  smalln       the small-N GEMM: one weight matrix against n vectors
+               (--smalln-config decode_n4 | decode_n16 | tiny_n3)
+  grouped      the grouped (MoE) GEMV: routed tokens against their experts'
+               weights (--moe-config moe_decode | moe_tiny)
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config decode]
-                       [--path gemv|quantize|gemv_bf16x]
+                       [--path gemv|quantize|gemv_bf16x|smalln|grouped]
 """
 from __future__ import annotations
 
@@ -45,7 +49,8 @@ HBM_PEAK_GBS = 8000.0
 CSRC = os.path.join(ROOT, "precision_decode_amd", "csrc")
 PROFILES = os.path.join(ROOT, "profiles")
 # counter summaries under profiles/ are valid only for the source they were taken on
-KERNEL_SOURCES = {"gemv_fast": "nvfp4_gemv.hip", "quantize_blocks": "nvfp4_quantize.hip"}
+KERNEL_SOURCES = {"gemv_fast": "nvfp4_gemv.hip", "quantize_blocks": "nvfp4_quantize.hip",
+                  "mma_stream": "nvfp4_mma.hip"}
 
 
 def parse_args(argv=None):
@@ -53,17 +58,26 @@ def parse_args(argv=None):
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=2000)
     p.add_argument("--warmup", type=int, default=100)
-    p.add_argument("--path", default="gemv", choices=["gemv", "quantize", "gemv_bf16x"])
+    p.add_argument("--path", default="gemv",
+                   choices=["gemv", "quantize", "gemv_bf16x", "smalln", "grouped"])
     p.add_argument("--config", default="decode",
                    help="integer-coded workload name from workloads.CONFIGS")
     p.add_argument("--act-config", default="tokens",
                    help="activation workload of --path quantize (workloads.ACT_CONFIGS)")
+    p.add_argument("--smalln-config", default="decode_n16",
+                   help="workload of --path smalln (workloads.SMALLN_CONFIGS)")
+    p.add_argument("--moe-config", default="moe_decode",
+                   help="workload of --path grouped (workloads.MOE_CONFIGS)")
+    p.add_argument("--out-type", type=int, default=None,
+                   help="output format of --path smalln / grouped: 0 fp16, 1 bf16 "
+                        "(default fp16 for smalln, bf16 for grouped)")
     p.add_argument("--rule", type=int, default=0,
                    help="E2M1 rounding rule of the quantiser (0 half-step, 1 nearest-even, "
                         "2 nearest-lower)")
     p.add_argument("--replicas", type=int, default=0,
                    help="device copies of the inputs to rotate over (0: enough for >= 1 GB)")
-    p.add_argument("--variant", type=int, default=0, help="fast-kernel variant (0 = default plan)")
+    p.add_argument("--variant", type=int, default=0,
+                   help="fast-kernel variant of the chosen path (0 = default plan)")
     p.add_argument("--ksplit", type=int, default=0, help="K split (0 = default plan)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-probe", action="store_true")
@@ -108,6 +122,7 @@ class Timer:
         for i in range(n):
             fn(i)
         end.record(self.stream)
+        self.enqueue_s = time.perf_counter() - t0
         torch.cuda.synchronize()
         return start.elapsed_time(end), time.perf_counter() - t0
 
@@ -150,7 +165,8 @@ def timed_steps(args, timer, step, nbytes, label):
     ms_step = ms_total / args.steps
     gbs = nbytes / (ms_step * 1e-3) / 1e9
     print(f"[bench] {label}: {args.steps} steps: {ms_step * 1e3:.2f} us/step, {gbs:.1f} GB/s "
-          f"({100 * gbs / HBM_PEAK_GBS:.1f}% of peak), host wall {wall:.3f}s", flush=True)
+          f"({100 * gbs / HBM_PEAK_GBS:.1f}% of peak), host wall {wall:.3f}s, host enqueue "
+          f"{timer.enqueue_s / args.steps * 1e6:.2f} us/step", flush=True)
     return ms_step, gbs
 
 
@@ -370,6 +386,127 @@ def bench_bf16x(args, torch, np, pd, workloads):
     return out
 
 
+# ------------------------------------------------------------------------- small-N GEMM
+def bench_smalln(args, torch, np, pd, workloads):
+    cfg = workloads.SMALLN_CONFIGS[args.smalln_config]
+    l, m, n, k = cfg.l, cfg.m, cfg.n, cfg.k
+    out_type = pd.NVFP4_OUT_F16 if args.out_type is None else args.out_type
+    nbytes = cfg.bytes_moved
+    print(f"[bench] small-N workload {cfg.name}: l={l} m={m} n={n} k={k}, {nbytes} bytes per step",
+          flush=True)
+    ops = workloads.smalln_operands(cfg)
+    base = {name: torch.from_numpy(np.ascontiguousarray(v)).cuda() for name, v in ops.items()}
+    replicas, reps = replicate(torch, base, nbytes, args.replicas)
+    c = torch.empty((l, m, n), dtype=torch.int16, device="cuda")
+    stream = torch.cuda.current_stream()
+    sptr = stream.cuda_stream
+    timer = Timer(torch, stream)
+    tuned = args.variant or args.ksplit
+    tuning = {"variant": args.variant, "ksplit": args.ksplit}
+    plan, ws_bytes = pd.nvfp4_gemm_smalln_plan(l, m, n, k, tuning=tuning if tuned else None)
+    ws = torch.empty(max(ws_bytes, 4), dtype=torch.uint8, device="cuda")
+
+    def step(i):
+        r = replicas[i % reps]
+        if tuned:
+            pd.nvfp4_gemm_smalln_launch_tuned(r["A"], r["sfA"], r["B"], r["sfB"], r["alpha"], c, l, m,
+                                              n, k, out_type, tuning, ws, ws_bytes, sptr)
+        else:
+            pd.nvfp4_gemm_smalln_launch(r["A"], r["sfA"], r["B"], r["sfB"], r["alpha"], c, l, m, n, k,
+                                        out_type, sptr)
+
+    print(f"[bench] plan path={plan.path} variant={plan.variant} ksplit={plan.ksplit}; "
+          f"{reps} replicas ({reps * nbytes / 1e9:.2f} GB)", flush=True)
+    ms_step, gbs = timed_steps(args, timer, step, nbytes, "smalln")
+    run_copies(torch, args.copy_mib)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        from oracle import multi
+        from oracle import reference as ref
+
+        threads = ref.default_threads()
+        fmt = "bf16" if out_type == pd.NVFP4_OUT_BF16 else "f16"
+        t_med = cpu_time(lambda: multi.gemm_smalln(ops["A"], ops["sfA"], ops["B"], ops["sfB"],
+                                                   ops["alpha"], l, m, n, k, fmt, nthreads=threads))
+        cpu = {"value": round(nbytes / t_med / 1e9, 4), "unit": "GB/s", "cores": threads,
+               "kind": "oracle",
+               "sample": f"the whole {cfg.name} workload, median of 3 runs of {t_med:.3f}s "
+                         f"(C fp64 sums, one vector at a time, {threads} threads)"}
+        print(f"[bench] CPU oracle: {t_med:.3f}s per call", flush=True)
+
+    flops = 2 * l * m * n * k
+    out = {"metric": "achieved HBM GB/s of the NVFP4 small-N block-scaled GEMM (us/call alongside)"}
+    out.update(common_fields(args, gbs, ms_step, "f32"))
+    out["config"] = {"workload": f"{cfg.name}: NVFP4 GEMM l={l} m={m} n={n} k={k}, integer-coded, "
+                                 f"alpha U[0.5,2] ({cfg.note})",
+                     "l": l, "m": m, "n": n, "k": k, "out": "bf16" if out_type else "f16",
+                     "bytes_per_step": nbytes, "replicas": reps,
+                     "operands": "HBM (rotated over >= 1 GB of copies)",
+                     "plan": {"path": plan.path, "variant": plan.variant, "ksplit": plan.ksplit}}
+    out["roofline"] = roofline(gbs, recorded_traffic(cfg.name, "mma_stream"),
+                               mfma_tflops=flops / (ms_step * 1e-3) / 1e12)
+    out["cpu_baseline"] = cpu
+    return out
+
+
+# ------------------------------------------------------------------- grouped (MoE) GEMV
+def bench_grouped(args, torch, np, pd, workloads):
+    cfg = workloads.MOE_CONFIGS[args.moe_config]
+    out_type = pd.NVFP4_OUT_BF16 if args.out_type is None else args.out_type
+    ops = workloads.moe_operands(cfg)
+    E, n, k, T = cfg.experts, cfg.n, cfg.k, cfg.tokens
+    nbytes = workloads.moe_bytes_moved(cfg, ops["offsets"])
+    active = int((np.diff(np.concatenate([[0], ops["offsets"]])) > 0).sum())
+    print(f"[bench] grouped workload {cfg.name}: {E} experts ({active} with tokens) of n={n} k={k}, "
+          f"{T} tokens, {nbytes} bytes per step", flush=True)
+    base = {name: torch.from_numpy(np.ascontiguousarray(v)).cuda() for name, v in ops.items()}
+    replicas, reps = replicate(torch, base, nbytes, args.replicas)
+    c = torch.empty((T, n), dtype=torch.int16, device="cuda")
+    stream = torch.cuda.current_stream()
+    sptr = stream.cuda_stream
+    timer = Timer(torch, stream)
+    tuning = {"variant": args.variant}
+
+    def step(i):
+        r = replicas[i % reps]
+        pd.nvfp4_grouped_gemv_launch_tuned(r["X"], r["sfX"], r["W"], r["sfW"], r["offsets"], r["gs_x"],
+                                           r["gs_w"], c, T, E, n, k, out_type, tuning, sptr)
+
+    print(f"[bench] variant={args.variant or 'default'}; {reps} replicas "
+          f"({reps * nbytes / 1e9:.2f} GB)", flush=True)
+    ms_step, gbs = timed_steps(args, timer, step, nbytes, "grouped")
+    run_copies(torch, args.copy_mib)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        from oracle import multi
+        from oracle import reference as ref
+
+        threads = ref.default_threads()
+        fmt = "bf16" if out_type == pd.NVFP4_OUT_BF16 else "f16"
+        t_med = cpu_time(lambda: multi.grouped_gemv(ops["X"], ops["sfX"], ops["W"], ops["sfW"],
+                                                    ops["offsets"], ops["gs_x"], ops["gs_w"], T, E,
+                                                    n, k, fmt, nthreads=threads))
+        cpu = {"value": round(nbytes / t_med / 1e9, 4), "unit": "GB/s", "cores": threads,
+               "kind": "oracle",
+               "sample": f"the whole {cfg.name} workload, median of 3 runs of {t_med:.3f}s "
+                         f"(C fp64 sums token by token, {threads} threads)"}
+        print(f"[bench] CPU oracle: {t_med:.3f}s per call", flush=True)
+
+    out = {"metric": "achieved HBM GB/s of the NVFP4 grouped (MoE) GEMV (us/call alongside)"}
+    out.update(common_fields(args, gbs, ms_step, "f32"))
+    out["config"] = {"workload": f"{cfg.name}: {E} experts of n={n} k={k}, {T} routed tokens "
+                                 f"(multinomial counts, {active} experts active), integer-coded "
+                                 f"({cfg.note})",
+                     "experts": E, "active_experts": active, "n": n, "k": k, "tokens": T,
+                     "out": "bf16" if out_type else "f16", "bytes_per_step": nbytes,
+                     "replicas": reps, "operands": "HBM (rotated over >= 1 GB of copies)"}
+    out["roofline"] = roofline(gbs, recorded_traffic(cfg.name, "mma_stream"))
+    out["cpu_baseline"] = cpu
+    return out
+
+
 def main(argv=None) -> int:
     args = parse_args(argv)
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -394,7 +531,8 @@ def main(argv=None) -> int:
         return 1
     torch.cuda.set_device(0)
 
-    fn = {"gemv": bench_gemv, "quantize": bench_quantize, "gemv_bf16x": bench_bf16x}[args.path]
+    fn = {"gemv": bench_gemv, "quantize": bench_quantize, "gemv_bf16x": bench_bf16x,
+          "smalln": bench_smalln, "grouped": bench_grouped}[args.path]
     out = fn(args, torch, np, pd, workloads)
     if out is None:
         return 2

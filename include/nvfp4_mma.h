@@ -50,10 +50,10 @@
  * default stream).  Calls only enqueue work: no device synchronisation, no
  * host read of device memory.  Shape rules: every dimension >= 1 (tokens may
  * be 0 for the grouped call), k >= 16, k % 16 == 0, byte sizes within int64,
- * and the output count below 2^31.  The fast kernels need k % 32 == 0 and
- * 16-byte aligned packed operands, 2-byte aligned scales; other valid calls
- * take a slower generic kernel with the same results.  Every argument is
- * checked before any HIP call; invalid calls return a negative status of
+ * and the output count below 2^31.  The fast kernels need k % 64 == 0,
+ * k <= 2^26, 16-byte aligned packed operands and 4-byte aligned scales; other
+ * valid calls take a slower generic kernel with the same results.  Every
+ * argument is checked before any HIP call; invalid calls return a negative status of
  * nvfp4_gemv.h and enqueue nothing.  No C++ exception crosses this interface.
  */
 #ifndef NVFP4_MMA_H
@@ -71,6 +71,16 @@ extern "C" {
 #define NVFP4_OUT_F16 0
 #define NVFP4_OUT_BF16 1
 
+/* Launch-plan control of the small-N and grouped kernels (tests and sweeps). */
+typedef struct nvfp4_mma_tuning_t {
+    int32_t path;           /* NVFP4_GEMV_PATH_* of nvfp4_gemv.h                        */
+    int32_t variant;        /* fast-kernel variant, 0 = default, 1..nvfp4_mma_num_variants() */
+    int32_t ksplit;         /* K split across workgroups, 0 = default, >= 1 explicit;
+                               the grouped GEMV takes 0 or 1 only                     */
+    int32_t rows_per_block; /* weight rows per workgroup, 0 = default, 1 .. 16 x the
+                               variant's row tiles per wave                            */
+} nvfp4_mma_tuning_t;
+
 /*
  * The small-N GEMM above.  When the plan splits K across workgroups the fp32
  * partial sums go to the library-owned per-(device, stream) workspace of
@@ -86,20 +96,23 @@ int nvfp4_gemm_smalln_launch(const uint8_t *A_packed, const uint8_t *sfA,
 
 /*
  * Number of fast small-N / grouped kernel variants, and the shape of variant
- * v (1-based): MFMA row tiles of 16 weight rows per wave, K windows of 128
- * elements kept in flight per wave, waves per workgroup (each wave takes
- * every waves-th window of the workgroup's K range).  Returns a status.
+ * v (1-based): MFMA row tiles of 16 weight rows per wave, K windows of 256
+ * elements (128 bytes of every row) kept in flight per wave, waves per
+ * workgroup (each wave takes every waves-th window of the workgroup's K
+ * range).  Returns a status.
  */
 int nvfp4_mma_num_variants(void);
 int nvfp4_mma_variant_info(int v, int32_t *row_tiles_per_wave, int32_t *windows_in_flight,
                            int32_t *waves_per_group);
 
 /*
- * The small-N plan the library would use (path, variant, K split) and the
- * workspace it needs, as nvfp4_gemv_plan does for the GEMV; `in` may be NULL.
+ * The small-N plan the library would use (path, variant, K split, rows per
+ * workgroup; the last three 0 for the generic kernel) and the workspace it
+ * needs, as nvfp4_gemv_plan does for the GEMV; `in` may be NULL.  `aligned`
+ * says whether the pointers meet the fast kernels' alignment rules.
  */
 int nvfp4_gemm_smalln_plan(int64_t l, int64_t m, int64_t n, int64_t k, int aligned,
-                           const nvfp4_gemv_tuning_t *in, nvfp4_gemv_tuning_t *out,
+                           const nvfp4_mma_tuning_t *in, nvfp4_mma_tuning_t *out,
                            size_t *workspace_bytes);
 
 /*
@@ -111,7 +124,7 @@ int nvfp4_gemm_smalln_launch_tuned(const uint8_t *A_packed, const uint8_t *sfA,
                                    const uint8_t *B_packed, const uint8_t *sfB,
                                    const float *alpha, uint16_t *c,
                                    int64_t l, int64_t m, int64_t n, int64_t k,
-                                   int32_t out_type, const nvfp4_gemv_tuning_t *tuning,
+                                   int32_t out_type, const nvfp4_mma_tuning_t *tuning,
                                    void *workspace, size_t workspace_bytes, void *stream);
 
 /*
@@ -133,7 +146,7 @@ int nvfp4_grouped_gemv_launch_tuned(const uint8_t *X_packed, const uint8_t *sfX,
                                     const int32_t *offsets, const float *gs_x,
                                     const float *gs_w, uint16_t *c, int64_t tokens,
                                     int64_t experts, int64_t n, int64_t k, int32_t out_type,
-                                    const nvfp4_gemv_tuning_t *tuning, void *stream);
+                                    const nvfp4_mma_tuning_t *tuning, void *stream);
 
 #ifdef __cplusplus
 }

@@ -11,6 +11,7 @@ built and never computes anything on the CPU.
 from ._binding import (  # noqa: F401
     EXPORTED,
     LIB_PATH,
+    MmaTuning,
     NVFP4_GEMV_ERR_ALIAS,
     NVFP4_GEMV_ERR_ALIGNMENT,
     NVFP4_GEMV_ERR_BAD_ARGUMENT,

@@ -75,6 +75,16 @@ class Tuning(ctypes.Structure):
         return f"Tuning(path={self.path}, variant={self.variant}, ksplit={self.ksplit})"
 
 
+class MmaTuning(ctypes.Structure):
+    """Mirror of ``nvfp4_mma_tuning_t``."""
+    _fields_ = [("path", ctypes.c_int32), ("variant", ctypes.c_int32),
+                ("ksplit", ctypes.c_int32), ("rows_per_block", ctypes.c_int32)]
+
+    def __repr__(self):
+        return (f"MmaTuning(path={self.path}, variant={self.variant}, ksplit={self.ksplit}, "
+                f"rows_per_block={self.rows_per_block})")
+
+
 _lib = None
 _P = ctypes.c_void_p
 _I64 = ctypes.c_int64
@@ -123,16 +133,16 @@ def load():
     lib.nvfp4_mma_variant_info.argtypes = [ctypes.c_int] + [ctypes.POINTER(ctypes.c_int32)] * 3
     lib.nvfp4_gemm_smalln_plan.restype = ctypes.c_int
     lib.nvfp4_gemm_smalln_plan.argtypes = [_I64, _I64, _I64, _I64, ctypes.c_int,
-                                           ctypes.POINTER(Tuning), ctypes.POINTER(Tuning),
+                                           ctypes.POINTER(MmaTuning), ctypes.POINTER(MmaTuning),
                                            ctypes.POINTER(ctypes.c_size_t)]
     lib.nvfp4_gemm_smalln_launch_tuned.restype = ctypes.c_int
-    lib.nvfp4_gemm_smalln_launch_tuned.argtypes = smalln_args + [ctypes.POINTER(Tuning), _P,
+    lib.nvfp4_gemm_smalln_launch_tuned.argtypes = smalln_args + [ctypes.POINTER(MmaTuning), _P,
                                                                  ctypes.c_size_t, _P]
     grouped_args = [_P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, ctypes.c_int32]
     lib.nvfp4_grouped_gemv_launch.restype = ctypes.c_int
     lib.nvfp4_grouped_gemv_launch.argtypes = grouped_args + [_P]
     lib.nvfp4_grouped_gemv_launch_tuned.restype = ctypes.c_int
-    lib.nvfp4_grouped_gemv_launch_tuned.argtypes = grouped_args + [ctypes.POINTER(Tuning), _P]
+    lib.nvfp4_grouped_gemv_launch_tuned.argtypes = grouped_args + [ctypes.POINTER(MmaTuning), _P]
     _lib = lib
     return lib
 
@@ -204,6 +214,15 @@ def _tuning(t):
                                int(t.get("ksplit", 0)), 0))
 
 
+def _mma_tuning(t):
+    if t is None:
+        return None
+    if isinstance(t, MmaTuning):
+        return ctypes.byref(t)
+    return ctypes.byref(MmaTuning(int(t.get("path", 0)), int(t.get("variant", 0)),
+                                  int(t.get("ksplit", 0)), int(t.get("rows_per_block", 0))))
+
+
 def nvfp4_gemv_plan(l, m, k, aligned=True, tuning=None):
     """Returns (Tuning actually used, workspace bytes)."""
     out = Tuning()
@@ -261,10 +280,10 @@ def nvfp4_mma_variant_info(v: int):
 
 
 def nvfp4_gemm_smalln_plan(l, m, n, k, aligned=True, tuning=None):
-    """Returns (Tuning actually used, workspace bytes)."""
-    out = Tuning()
+    """Returns (MmaTuning actually used, workspace bytes)."""
+    out = MmaTuning()
     ws = ctypes.c_size_t()
-    _check(load().nvfp4_gemm_smalln_plan(l, m, n, k, int(bool(aligned)), _tuning(tuning),
+    _check(load().nvfp4_gemm_smalln_plan(l, m, n, k, int(bool(aligned)), _mma_tuning(tuning),
                                          ctypes.byref(out), ctypes.byref(ws)),
            "nvfp4_gemm_smalln_plan")
     return out, int(ws.value)
@@ -274,7 +293,7 @@ def nvfp4_gemm_smalln_launch_tuned(A_packed, sfA, B_packed, sfB, alpha, c, l, m,
                                    tuning, workspace, workspace_bytes, stream=None):
     _check(load().nvfp4_gemm_smalln_launch_tuned(_ptr(A_packed), _ptr(sfA), _ptr(B_packed),
                                                  _ptr(sfB), _ptr(alpha), _ptr(c), l, m, n, k,
-                                                 int(out_type), _tuning(tuning), _ptr(workspace),
+                                                 int(out_type), _mma_tuning(tuning), _ptr(workspace),
                                                  int(workspace_bytes), _stream(stream)),
            "nvfp4_gemm_smalln_launch_tuned")
 
@@ -292,7 +311,7 @@ def nvfp4_grouped_gemv_launch_tuned(X_packed, sfX, W_packed, sfW, offsets, gs_x,
     _check(load().nvfp4_grouped_gemv_launch_tuned(_ptr(X_packed), _ptr(sfX), _ptr(W_packed),
                                                   _ptr(sfW), _ptr(offsets), _ptr(gs_x), _ptr(gs_w),
                                                   _ptr(c), tokens, experts, n, k, int(out_type),
-                                                  _tuning(tuning), _stream(stream)),
+                                                  _mma_tuning(tuning), _stream(stream)),
            "nvfp4_grouped_gemv_launch_tuned")
 
 

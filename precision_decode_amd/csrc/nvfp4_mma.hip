@@ -21,10 +21,10 @@
 //    fp32 and the matrix core accumulates in fp32.  Lane i + 16q holds row
 //    (or vector) i, elements 8q .. 8q+7 of the 32; the contraction does not
 //    care which K element sits where as long as both operands agree, so a
-//    lane's 16-byte load covers 32 consecutive elements, split over the four
-//    MFMA steps of a 128-element window;
+//    lane's 16-byte load covers 32 consecutive elements, split over four
+//    MFMA steps;
 //  * each wave streams its tile rows with 16-byte non-temporal buffer loads
-//    (16 rows x 64 contiguous bytes per instruction), keeps several windows
+//    (two instructions per 128-byte line of 16 rows), keeps several windows
 //    in flight, and reads the vectors' codes with ordinary (cached) loads:
 //    every workgroup reads the same vectors, so they stay in L2;
 //  * the waves of a workgroup share the tile rows and take interleaved
@@ -51,9 +51,10 @@ namespace {
 using namespace nvfp4dev;
 
 constexpr int kTile = 16;            // MFMA tile: 16 weight rows x 16 vectors
-constexpr int kWinElems = 128;       // K elements of one window (4 lane groups x 32)
+constexpr int kWinElems = 256;       // K elements of one window: 128 bytes of every row
+constexpr int kLaneElems = 64;       // K elements of one window in one lane (32 code bytes)
 constexpr int64_t kMaxFastK = int64_t(1) << 26;   // keeps 32-row descriptors within 31 bits
-constexpr int64_t kTargetGroups = 1024;           // workgroups wanted before splitting K
+constexpr int64_t kComputeUnits = 256;            // CUs of an MI355X (8 XCDs x 32)
 constexpr int kReduceThreads = 256;
 constexpr int kGenericWaves = 4;
 
@@ -68,6 +69,7 @@ struct MmaArgs {
     int64_t groups, rows, nvec, k;   // nvec: n (small-N) or tokens (grouped)
     int64_t kchunk;             // K elements per workgroup
     int64_t row_blocks;         // workgroups along the rows of one group
+    int64_t rows_per_block;     // weight rows per workgroup (at most 16 per row tile)
     int32_t out_bf16;
 };
 
@@ -123,11 +125,17 @@ __device__ __forceinline__ void decode32(u32x4 q, uint32_t s2, f16x8 (&o)[4]) {
 
 // ---------------------------------------------------------------- fast kernel
 // blockIdx.x enumerates (split, group, row block) with the row block fastest.
-// A workgroup owns R*16 weight rows of one group and the K range
+// A workgroup owns rows_per_block (at most R*16) weight rows of one group,
+// their MFMA tiles padded with rows that read zeros, and the K range
 // [split*kchunk, min(k, (split+1)*kchunk)); wave w takes windows w, w+W, ...
-// of it.  Lane i + 16q loads, per window, the 32 elements at window offset
-// 32q of weight row i of each row tile and of vector i of the current pass of
-// 16 vectors.
+// of it.  A window is 256 elements, 128 bytes of every row: one whole cache
+// line, read by two back-to-back load instructions of the same wave, so no
+// line is shared between waves.  Lane i + 16q loads, per window, the 64
+// elements at window offset 64q (32 code bytes, two 16-byte loads) and their
+// four scale codes (one 4-byte load) of weight row i of each row tile and of
+// vector i of the current pass of 16 vectors.  The scale lines are read 16
+// bytes per row and window, so they are loaded through the cache rather than
+// as streamed data.
 //
 // All global reads are buffer loads: a descriptor covers the workgroup's
 // valid weight rows (or the pass's vectors) over the whole K, and a lane
@@ -166,8 +174,8 @@ __global__ void __launch_bounds__(W * kWave) mma_stream(const MmaArgs a) {
     const int nwin = static_cast<int>((kend - kb0 + kWinElems - 1) / kWinElems);
     const int niter = nwin > wave ? (nwin - wave + W - 1) / W : 0;
 
-    const int64_t row0 = rb * (R * kTile);
-    const int64_t nrows = (a.rows - row0 < R * kTile) ? a.rows - row0 : R * kTile;
+    const int64_t row0 = rb * a.rows_per_block;
+    const int64_t nrows = (a.rows - row0 < a.rows_per_block) ? a.rows - row0 : a.rows_per_block;
     const __amdgpu_buffer_rsrc_t wdesc =
         buffer_of(a.W + (grp * a.rows + row0) * (k / 2), static_cast<int>(nrows * (k / 2)));
     const __amdgpu_buffer_rsrc_t swdesc =
@@ -181,10 +189,10 @@ __global__ void __launch_bounds__(W * kWave) mma_stream(const MmaArgs a) {
         const __amdgpu_buffer_rsrc_t svdesc =
             buffer_of(a.sV + vp * (k / 16), static_cast<int>(nv * (k / 16)));
 
-        u32x4 wq[U][R], vq[U];
-        uint16_t ws[U][R], vs[U];
+        u32x4 wq[U][R][2], vq[U][2];
+        uint32_t ws[U][R], vs[U];
         auto issue = [&](int i, int u) {
-            const int64_t kk = kb0 + static_cast<int64_t>(wave + W * i) * kWinElems + kq * 32;
+            const int64_t kk = kb0 + static_cast<int64_t>(wave + W * i) * kWinElems + kq * kLaneElems;
             const bool in = kk < kend;
             const uint32_t ko = static_cast<uint32_t>(kk / 2);
             const uint32_t so = static_cast<uint32_t>(kk / 16);
@@ -193,14 +201,19 @@ __global__ void __launch_bounds__(W * kWave) mma_stream(const MmaArgs a) {
                 const uint32_t row = static_cast<uint32_t>(r * kTile + li);
                 const uint32_t o = in ? row * half + ko : kOutOfRange;
                 const uint32_t os = in ? row * sixteenth + so : kOutOfRange;
-                wq[u][r] = __builtin_bit_cast(
-                    u32x4, __builtin_amdgcn_raw_buffer_load_b128(wdesc, o, 0, kNonTemporal));
-                ws[u][r] = __builtin_amdgcn_raw_buffer_load_b16(swdesc, os, 0, kNonTemporal);
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+                    wq[u][r][h] = __builtin_bit_cast(
+                        u32x4, __builtin_amdgcn_raw_buffer_load_b128(wdesc, o + 16 * h, 0, kNonTemporal));
+                ws[u][r] = __builtin_amdgcn_raw_buffer_load_b32(swdesc, os, 0, 0);
             }
             const uint32_t o = in ? static_cast<uint32_t>(li) * half + ko : kOutOfRange;
             const uint32_t os = in ? static_cast<uint32_t>(li) * sixteenth + so : kOutOfRange;
-            vq[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vdesc, o, 0, 0));
-            vs[u] = __builtin_amdgcn_raw_buffer_load_b16(svdesc, os, 0, 0);
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+                vq[u][h] = __builtin_bit_cast(u32x4,
+                                              __builtin_amdgcn_raw_buffer_load_b128(vdesc, o + 16 * h, 0, 0));
+            vs[u] = __builtin_amdgcn_raw_buffer_load_b32(svdesc, os, 0, 0);
         };
 
         f32x4 acc[R];
@@ -208,18 +221,23 @@ __global__ void __launch_bounds__(W * kWave) mma_stream(const MmaArgs a) {
         for (int r = 0; r < R; ++r) acc[r] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
         auto consume = [&](int u) {
-            f16x8 vo[4];
-            decode32(vq[u], vs[u], vo);
 #pragma unroll
-            for (int r = 0; r < R; ++r) {
-                f16x8 wo[4];
-                decode32(wq[u][r], ws[u][r], wo);
+            for (int h = 0; h < 2; ++h) {
+                f16x8 vo[4];
+                decode32(vq[u][h], vs[u] >> (16 * h), vo);
 #pragma unroll
-                for (int s = 0; s < 4; ++s) {
-                    if (GROUPED)
-                        acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vo[s], wo[s], acc[r], 0, 0, 0);
-                    else
-                        acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wo[s], vo[s], acc[r], 0, 0, 0);
+                for (int r = 0; r < R; ++r) {
+                    f16x8 wo[4];
+                    decode32(wq[u][r][h], ws[u][r] >> (16 * h), wo);
+#pragma unroll
+                    for (int s = 0; s < 4; ++s) {
+                        if (GROUPED)
+                            acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vo[s], wo[s], acc[r], 0,
+                                                                            0, 0);
+                        else
+                            acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wo[s], vo[s], acc[r], 0,
+                                                                            0, 0);
+                    }
                 }
             }
         };
@@ -256,14 +274,14 @@ __global__ void __launch_bounds__(W * kWave) mma_stream(const MmaArgs a) {
                 for (int e = 0; e < 4; ++e) {
                     if (GROUPED) {
                         const int64_t t = vp + kq * 4 + e;
-                        const int64_t row = row0 + r * kTile + li;
-                        if (t < v1 && row < a.rows)
-                            a.c[t * a.rows + row] = round_out(al, s[e], a.out_bf16);
+                        const int rr = r * kTile + li;
+                        if (t < v1 && rr < nrows)
+                            a.c[t * a.rows + row0 + rr] = round_out(al, s[e], a.out_bf16);
                     } else {
-                        const int64_t row = row0 + r * kTile + kq * 4 + e;
+                        const int rr = r * kTile + kq * 4 + e;
                         const int64_t col = vp - v0 + li;
-                        if (row < a.rows && col < a.nvec) {
-                            const int64_t o = (grp * a.rows + row) * a.nvec + col;
+                        if (rr < nrows && col < a.nvec) {
+                            const int64_t o = (grp * a.rows + row0 + rr) * a.nvec + col;
                             if (a.part != nullptr)
                                 a.part[split * a.groups * a.rows * a.nvec + o] = s[e];
                             else
@@ -349,21 +367,26 @@ struct Variant {
 };
 // {row tiles per wave, windows in flight, waves per workgroup}
 constexpr Variant kVariants[] = {
-    {1, 4, 4}, {1, 4, 8}, {2, 4, 4}, {2, 2, 8}, {1, 2, 8}, {2, 2, 4},
+    {1, 2, 4}, {1, 2, 8}, {2, 2, 4}, {2, 1, 8}, {1, 3, 4}, {2, 2, 8},
 };
 constexpr int kNumVariants = static_cast<int>(sizeof(kVariants) / sizeof(kVariants[0]));
+// Defaults from MI355X sweeps of every variant: {2, 2, 4} on the decode-style
+// small-N workloads (one 7168 x 16384 weight against 4 or 16 vectors), {2, 1, 8}
+// on the grouped decode workload (64 experts of 2048 x 7168, 128 tokens).
+constexpr int kDefaultSmallN = 2;
+constexpr int kDefaultGrouped = 3;
 
 typedef void (*MmaKernel)(const MmaArgs);
 
 template <bool G>
 MmaKernel fast_kernel(int v) {
     switch (v) {
-    case 0: return mma_stream<1, 4, 4, G>;
-    case 1: return mma_stream<1, 4, 8, G>;
-    case 2: return mma_stream<2, 4, 4, G>;
-    case 3: return mma_stream<2, 2, 8, G>;
-    case 4: return mma_stream<1, 2, 8, G>;
-    case 5: return mma_stream<2, 2, 4, G>;
+    case 0: return mma_stream<1, 2, 4, G>;
+    case 1: return mma_stream<1, 2, 8, G>;
+    case 2: return mma_stream<2, 2, 4, G>;
+    case 3: return mma_stream<2, 1, 8, G>;
+    case 4: return mma_stream<1, 3, 4, G>;
+    case 5: return mma_stream<2, 2, 8, G>;
     default: return nullptr;
     }
 }
@@ -373,7 +396,7 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 struct Plan {
     int path;
     int variant;
-    int64_t ksplit, kchunk, row_blocks, groups;
+    int64_t ksplit, kchunk, row_blocks, rows_per_block, groups;
     int threads;
     size_t ws_bytes;
 };
@@ -391,46 +414,70 @@ int check_dims(int64_t groups, int64_t rows, int64_t nvec, int64_t k, bool allow
     return NVFP4_GEMV_OK;
 }
 
+// Workgroups of the fast kernel: (split, group, row block).  Defaults:
+//  * the small-N GEMM splits K (powers of two, at least one window per wave
+//    and split) while there are fewer 16-row tiles than compute units;
+//  * while the workgroups are few (under 8 per compute unit), the rows per
+//    workgroup shrink so that the count becomes a multiple of the 256 compute
+//    units of an MI355X: a workgroup's time is set by its rows, so equal rows
+//    on every unit beat full tiles on some and idle units elsewhere.
 int make_plan(int64_t groups, int64_t rows, int64_t nvec_per_group, int64_t k, bool aligned,
-              bool grouped, const nvfp4_gemv_tuning_t *t, Plan *p) {
-    nvfp4_gemv_tuning_t tun = {NVFP4_GEMV_PATH_AUTO, 0, 0, 0};
+              bool grouped, const nvfp4_mma_tuning_t *t, Plan *p) {
+    nvfp4_mma_tuning_t tun = {NVFP4_GEMV_PATH_AUTO, 0, 0, 0};
     if (t) tun = *t;
-    if (tun.reserved != 0 || tun.path < NVFP4_GEMV_PATH_AUTO || tun.path > NVFP4_GEMV_PATH_GENERIC ||
-        tun.variant < 0 || tun.variant > kNumVariants || tun.ksplit < 0)
+    if (tun.path < NVFP4_GEMV_PATH_AUTO || tun.path > NVFP4_GEMV_PATH_GENERIC || tun.variant < 0 ||
+        tun.variant > kNumVariants || tun.ksplit < 0 || tun.rows_per_block < 0)
         return NVFP4_GEMV_ERR_BAD_TUNING;
-    const bool fast_ok = aligned && k % 32 == 0 && k <= kMaxFastK;
+    const bool fast_ok = aligned && k % 64 == 0 && k <= kMaxFastK;
     if (tun.path == NVFP4_GEMV_PATH_FAST && !fast_ok) return NVFP4_GEMV_ERR_BAD_TUNING;
-    if (tun.path == NVFP4_GEMV_PATH_GENERIC && (tun.variant != 0 || tun.ksplit > 1))
+    if (tun.path == NVFP4_GEMV_PATH_GENERIC &&
+        (tun.variant != 0 || tun.ksplit > 1 || tun.rows_per_block != 0))
         return NVFP4_GEMV_ERR_BAD_TUNING;
     if (grouped && tun.ksplit > 1) return NVFP4_GEMV_ERR_BAD_TUNING;
     const bool fast = tun.path != NVFP4_GEMV_PATH_GENERIC && fast_ok;
     p->path = fast ? NVFP4_GEMV_PATH_FAST : NVFP4_GEMV_PATH_GENERIC;
     if (!fast) {
+        // (with NVFP4_GEMV_PATH_AUTO, fast-kernel settings are ignored where the
+        // shape or alignment rules the fast kernel out; an explicit K split is not)
+        if (tun.ksplit > 1) return NVFP4_GEMV_ERR_BAD_TUNING;
         p->variant = 0;
         p->ksplit = 1;
         p->kchunk = k;
-        p->row_blocks = ceil_div(rows, kGenericWaves);
+        p->rows_per_block = kGenericWaves;
         p->threads = kGenericWaves * kWave;
     } else {
-        p->variant = tun.variant > 0 ? tun.variant - 1 : 0;
+        p->variant = tun.variant > 0 ? tun.variant - 1 : (grouped ? kDefaultGrouped : kDefaultSmallN);
         const Variant &v = kVariants[p->variant];
-        p->row_blocks = ceil_div(rows, int64_t(v.R) * kTile);
-        p->threads = v.W * kWave;
+        const int64_t tile_rows = int64_t(v.R) * kTile;
+        if (tun.rows_per_block > tile_rows) return NVFP4_GEMV_ERR_BAD_TUNING;
         int64_t ks = 1;
         if (tun.ksplit > 0) {
             ks = tun.ksplit;
         } else if (!grouped) {
-            // split K while there are too few workgroups, keeping at least one
-            // window per wave in every split
-            const int64_t wg1 = groups * p->row_blocks;
+            const int64_t wg1 = groups * ceil_div(rows, int64_t(kTile));
             const int64_t most = k / (int64_t(v.W) * kWinElems);
-            while (wg1 * ks < kTargetGroups && ks * 2 <= most) ks *= 2;
+            while (wg1 * ks < kComputeUnits && ks * 2 <= most) ks *= 2;
         }
-        if (ks > k / 32) return NVFP4_GEMV_ERR_BAD_TUNING;
-        int64_t kchunk = ceil_div(ceil_div(k, ks), 32) * 32;
+        if (ks > k / kLaneElems) return NVFP4_GEMV_ERR_BAD_TUNING;
+        const int64_t kchunk = ceil_div(ceil_div(k, ks), kLaneElems) * kLaneElems;
         p->ksplit = ceil_div(k, kchunk);
         p->kchunk = kchunk;
+        int64_t rpb = tile_rows;
+        if (tun.rows_per_block > 0) {
+            rpb = tun.rows_per_block;
+        } else {
+            const int64_t wg = groups * ceil_div(rows, tile_rows) * p->ksplit;
+            if (wg < 8 * kComputeUnits) {
+                const int64_t target = ceil_div(wg, kComputeUnits) * kComputeUnits;
+                const int64_t blocks = ceil_div(target, groups * p->ksplit);   // per group
+                rpb = ceil_div(rows, blocks);
+                if (rpb > tile_rows) rpb = tile_rows;
+            }
+        }
+        p->rows_per_block = rpb;
+        p->threads = v.W * kWave;
     }
+    p->row_blocks = ceil_div(rows, p->rows_per_block);
     p->groups = groups * p->row_blocks * p->ksplit;
     if (p->groups >= (int64_t(1) << 31)) return NVFP4_GEMV_ERR_BAD_SHAPE;
     p->ws_bytes = p->ksplit > 1
@@ -447,12 +494,13 @@ bool overlaps(const void *p, size_t pn, const void *q, size_t qn) {
 
 bool aligned_ptrs(const void *w, const void *sw, const void *v, const void *sv) {
     auto al = [](const void *p, uintptr_t n) { return reinterpret_cast<uintptr_t>(p) % n == 0; };
-    return al(w, 16) && al(v, 16) && al(sw, 2) && al(sv, 2);
+    return al(w, 16) && al(v, 16) && al(sw, 4) && al(sv, 4);
 }
 
 int launch(const Plan &p, bool grouped, MmaArgs a, hipStream_t stream) {
     a.kchunk = p.kchunk;
     a.row_blocks = p.row_blocks;
+    a.rows_per_block = p.rows_per_block;
     const void *fn;
     if (p.path == NVFP4_GEMV_PATH_FAST)
         fn = reinterpret_cast<const void *>(grouped ? fast_kernel<true>(p.variant)
@@ -560,7 +608,7 @@ int nvfp4_mma_variant_info(int v, int32_t *row_tiles_per_wave, int32_t *windows_
 }
 
 int nvfp4_gemm_smalln_plan(int64_t l, int64_t m, int64_t n, int64_t k, int aligned,
-                           const nvfp4_gemv_tuning_t *in, nvfp4_gemv_tuning_t *out,
+                           const nvfp4_mma_tuning_t *in, nvfp4_mma_tuning_t *out,
                            size_t *workspace_bytes) {
     if (!out || !workspace_bytes) return NVFP4_GEMV_ERR_NULL_POINTER;
     int s = check_dims(l, m, n, k, false);
@@ -571,7 +619,7 @@ int nvfp4_gemm_smalln_plan(int64_t l, int64_t m, int64_t n, int64_t k, int align
     out->path = p.path;
     out->variant = p.path == NVFP4_GEMV_PATH_FAST ? p.variant + 1 : 0;
     out->ksplit = static_cast<int32_t>(p.ksplit);
-    out->reserved = 0;
+    out->rows_per_block = p.path == NVFP4_GEMV_PATH_FAST ? static_cast<int32_t>(p.rows_per_block) : 0;
     *workspace_bytes = p.ws_bytes;
     return NVFP4_GEMV_OK;
 }
@@ -580,7 +628,7 @@ int nvfp4_gemm_smalln_launch_tuned(const uint8_t *A_packed, const uint8_t *sfA,
                                    const uint8_t *B_packed, const uint8_t *sfB,
                                    const float *alpha, uint16_t *c, int64_t l, int64_t m,
                                    int64_t n, int64_t k, int32_t out_type,
-                                   const nvfp4_gemv_tuning_t *tuning, void *workspace,
+                                   const nvfp4_mma_tuning_t *tuning, void *workspace,
                                    size_t workspace_bytes, void *stream) {
     int s = validate_smalln(A_packed, sfA, B_packed, sfB, alpha, c, l, m, n, k, out_type);
     if (s != NVFP4_GEMV_OK) return s;
@@ -622,7 +670,7 @@ int nvfp4_grouped_gemv_launch_tuned(const uint8_t *X_packed, const uint8_t *sfX,
                                     const uint8_t *W_packed, const uint8_t *sfW,
                                     const int32_t *offsets, const float *gs_x, const float *gs_w,
                                     uint16_t *c, int64_t tokens, int64_t experts, int64_t n,
-                                    int64_t k, int32_t out_type, const nvfp4_gemv_tuning_t *tuning,
+                                    int64_t k, int32_t out_type, const nvfp4_mma_tuning_t *tuning,
                                     void *stream) {
     int s = validate_grouped(X_packed, sfX, W_packed, sfW, offsets, gs_x, gs_w, c, tokens, experts,
                              n, k, out_type);

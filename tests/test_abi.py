@@ -248,6 +248,14 @@ def test_smalln_plans(lib):
     t, ws = pd.nvfp4_gemm_smalln_plan(1, 7168, 16, 16384)
     assert t.path == pd.NVFP4_GEMV_PATH_FAST and t.variant >= 1
     assert ws == (t.ksplit * 7168 * 16 * 4 if t.ksplit > 1 else 0)
+    # few workgroups: rows per workgroup chosen so every one of the 256 CUs gets the same number
+    blocks = -(-7168 // t.rows_per_block) * t.ksplit
+    assert blocks % 256 == 0 and 1 <= t.rows_per_block <= 32
+    t, _ = pd.nvfp4_gemm_smalln_plan(1, 7168, 16, 16384, tuning={"variant": 1, "rows_per_block": 9})
+    assert t.rows_per_block == 9 and t.ksplit >= 1
+    t, _ = pd.nvfp4_gemm_smalln_plan(64, 4096, 4, 4096)      # plenty of tiles: full 16-row tiles
+    r, _, _ = pd.nvfp4_mma_variant_info(t.variant)
+    assert t.rows_per_block == 16 * r and t.ksplit == 1
     t, ws = pd.nvfp4_gemm_smalln_plan(2, 100, 3, 48)           # k % 32 != 0
     assert t.path == pd.NVFP4_GEMV_PATH_GENERIC and t.ksplit == 1 and ws == 0
     t, _ = pd.nvfp4_gemm_smalln_plan(2, 100, 3, 64, aligned=False)
@@ -259,7 +267,9 @@ def test_smalln_plans(lib):
         t, ws = pd.nvfp4_gemm_smalln_plan(3, 100, 5, 4096, tuning={"variant": v, "ksplit": 3})
         assert t.variant == v and t.ksplit == 3 and ws == 3 * 3 * 100 * 5 * 4
     for bad in ({"variant": n + 1}, {"ksplit": 3, "path": pd.NVFP4_GEMV_PATH_GENERIC},
-                {"path": pd.NVFP4_GEMV_PATH_GENERIC, "variant": 1}, {"path": 3}):
+                {"path": pd.NVFP4_GEMV_PATH_GENERIC, "variant": 1}, {"path": 3},
+                {"rows_per_block": -1}, {"variant": 1, "rows_per_block": 33},
+                {"path": pd.NVFP4_GEMV_PATH_GENERIC, "rows_per_block": 8}):
         with pytest.raises(pd.Nvfp4GemvError):
             pd.nvfp4_gemm_smalln_plan(1, 64, 4, 4096, tuning=bad)
     with pytest.raises(pd.Nvfp4GemvError):
@@ -272,7 +282,7 @@ def test_smalln_plans(lib):
 
 def test_smalln_tuned_needs_workspace(lib):
     l, m, n, k = 1, 64, 4, 4096
-    t = _binding.Tuning(0, 0, 4, 0)
+    t = _binding.MmaTuning(0, 0, 4, 0)
     _, need = pd.nvfp4_gemm_smalln_plan(l, m, n, k, tuning=t)
     assert need == 4 * m * n * 4
     f = lib.nvfp4_gemm_smalln_launch_tuned
@@ -306,5 +316,6 @@ def test_grouped_validation(lib):
     assert gcall(c=A + 64) == pd.NVFP4_GEMV_ERR_ALIAS               # c inside the weights
     assert gcall(c=OF - 4) == pd.NVFP4_GEMV_ERR_ALIAS               # c's 512 bytes reach offsets
     assert gcall(c=GW) == pd.NVFP4_GEMV_ERR_ALIAS
-    assert gcall(tuning=_binding.Tuning(0, 0, 2, 0)) == pd.NVFP4_GEMV_ERR_BAD_TUNING   # no K split
-    assert gcall(tuning=_binding.Tuning(1, 0, 0, 0), k=48) == pd.NVFP4_GEMV_ERR_BAD_TUNING
+    assert gcall(tuning=_binding.MmaTuning(0, 0, 2, 0)) == pd.NVFP4_GEMV_ERR_BAD_TUNING  # no K split
+    assert gcall(tuning=_binding.MmaTuning(1, 0, 0, 0), k=48) == pd.NVFP4_GEMV_ERR_BAD_TUNING
+    assert gcall(tuning=_binding.MmaTuning(0, 1, 0, 17)) == pd.NVFP4_GEMV_ERR_BAD_TUNING  # > 16 rows

@@ -68,7 +68,7 @@ def test_smalln_configs_bit_exact(name, out_type):
 
 SMALLN_SHAPES = [
     (1, 1, 1, 32), (2, 80, 3, 256), (1, 17, 16, 2080), (3, 33, 5, 4096), (1, 100, 17, 1024),
-    (2, 48, 2, 160), (1, 7, 40, 512), (1, 300, 16, 16384),
+    (2, 48, 2, 160), (1, 7, 40, 512), (1, 300, 16, 16384), (2, 31, 9, 320), (1, 64, 4, 64),
 ]
 
 
@@ -82,7 +82,7 @@ def test_smalln_default_plan_shapes(l, m, n, k):
 @pytest.mark.parametrize("ksplit", [1, 3])
 def test_smalln_every_variant(variant, ksplit):
     assert pd.nvfp4_mma_num_variants() == 6
-    l, m, n, k = 2, 75, 11, 2080       # ragged rows, k not a multiple of the 128-element window
+    l, m, n, k = 2, 75, 11, 2112       # ragged rows, k not a multiple of the 256-element window
     ops = smalln_ops(l, m, n, k, seed=variant * 10 + ksplit)
     want = oracle_smalln(ops, l, m, n, k, pd.NVFP4_OUT_BF16)
     tuning = {"path": pd.NVFP4_GEMV_PATH_FAST, "variant": variant, "ksplit": ksplit}
@@ -225,7 +225,7 @@ def test_grouped_configs_bit_exact(name, out_type):
 
 @pytest.mark.parametrize("counts,n,k", [
     ([3, 0, 1, 5], 40, 256),          # an expert without tokens, ragged rows
-    ([0, 0, 37], 17, 2080),           # more than two passes of 16 tokens
+    ([0, 0, 37], 17, 2112),           # more than two passes of 16 tokens
     ([1], 1, 32),
     ([16, 16], 33, 512),
     ([2, 1, 0, 0, 4, 9], 96, 1024),
@@ -278,3 +278,26 @@ def test_grouped_zero_tokens_is_a_no_op():
     ops = grouped_ops([0, 0], 16, 64, seed=46)
     got = run_grouped(ops, 0, 2, 16, 64)
     assert got.size == 0
+
+
+@pytest.mark.parametrize("variant", range(1, 7))
+@pytest.mark.parametrize("rows_per_block,ksplit", [(1, 1), (7, 2), (14, 1), (16, 3), (32, 1)])
+def test_smalln_rows_per_block(variant, rows_per_block, ksplit):
+    r, _, _ = pd.nvfp4_mma_variant_info(variant)
+    if rows_per_block > 16 * r:
+        pytest.skip("more rows than the variant's tiles hold")
+    l, m, n, k = 2, 45, 5, 1088
+    ops = smalln_ops(l, m, n, k, seed=100 + variant * 7 + rows_per_block)
+    tuning = {"variant": variant, "ksplit": ksplit, "rows_per_block": rows_per_block}
+    got = run_smalln(ops, l, m, n, k, pd.NVFP4_OUT_BF16, tuning=tuning)
+    assert_bits_equal(got, oracle_smalln(ops, l, m, n, k, pd.NVFP4_OUT_BF16),
+                      f"v{variant} rpb {rows_per_block} ks {ksplit}", "bf16")
+
+
+@pytest.mark.parametrize("variant,rows_per_block", [(1, 5), (3, 20), (4, 31), (2, 16)])
+def test_grouped_rows_per_block(variant, rows_per_block):
+    counts, n, k = [3, 0, 18, 1], 70, 512
+    ops = grouped_ops(counts, n, k, seed=200 + rows_per_block)
+    want = oracle_grouped(ops, 22, 4, n, k)
+    got = run_grouped(ops, 22, 4, n, k, tuning={"variant": variant, "rows_per_block": rows_per_block})
+    assert_bits_equal(got, want, f"grouped v{variant} rpb {rows_per_block}", "bf16")
