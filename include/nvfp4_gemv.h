@@ -127,12 +127,13 @@ int nvfp4_gemv_num_variants(void);
 
 /*
  * Describes fast-kernel variant v (1-based): rows each wave streams at once,
- * 1 KiB K-iterations kept in flight per row, waves per workgroup, and whether
- * x is staged in LDS as packed codes (1) or as decoded fp16 (0).  Returns a
- * status.
+ * 1 KiB K-iterations kept in flight per row, waves per workgroup, and how x
+ * reaches the arithmetic: 0 = decoded to fp16 in LDS once per workgroup,
+ * 1 = staged in LDS as packed codes, 2 = not staged (each wave loads x's
+ * codes next to its rows of A every iteration).  Returns a status.
  */
 int nvfp4_gemv_variant_info(int v, int32_t *rows_per_wave, int32_t *iters_in_flight,
-                            int32_t *waves_per_group, int32_t *packed_x);
+                            int32_t *waves_per_group, int32_t *x_staging);
 
 /*
  * The plan the library would use: fills `out` with the resolved path, variant

@@ -198,7 +198,8 @@ def nvfp4_gemv_num_variants() -> int:
 
 
 def nvfp4_gemv_variant_info(v: int):
-    """(rows per wave, iterations in flight, waves per group, packed x)."""
+    """(rows per wave, iterations in flight, waves per group, x staging: 0 fp16 in LDS,
+    1 packed codes in LDS, 2 none)."""
     r, u, w, px = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
     _check(load().nvfp4_gemv_variant_info(v, ctypes.byref(r), ctypes.byref(u), ctypes.byref(w),
                                           ctypes.byref(px)), "nvfp4_gemv_variant_info")

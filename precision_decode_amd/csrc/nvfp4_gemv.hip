@@ -414,6 +414,108 @@ gemv_fastp(const uint8_t *__restrict__ A, const uint8_t *__restrict__ sfA,
     }
 }
 
+// ---------------------------------------------------------------- unstaged fast kernel
+// The packed-x arithmetic with no LDS at all: every wave loads x's codes and
+// scale pair for its iteration straight from memory (ordinary cached loads:
+// all workgroups read the same x, which stays in L2) next to its R rows of A.
+// No staging, no barrier: a wave starts consuming as soon as its first loads
+// land, and K needs no split for LDS capacity.  The x decode is shared by the
+// wave's R rows.
+template <int R, int U, int W>
+__global__ void __launch_bounds__(W * kWave)
+gemv_fastg(const uint8_t *__restrict__ A, const uint8_t *__restrict__ sfA,
+           const uint8_t *__restrict__ x, const uint8_t *__restrict__ sfx,
+           const float *__restrict__ alpha, uint16_t *__restrict__ c,
+           float *__restrict__ part, int64_t l, int64_t m, int64_t k,
+           int64_t kchunk, int64_t row_blocks) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+
+    int64_t g = blockIdx.x;
+    const int64_t rb = g % row_blocks;
+    g /= row_blocks;
+    const int64_t b = g % l;
+    const int64_t split = g / l;
+
+    const int64_t kb0 = split * kchunk;
+    const int klen = static_cast<int>((k - kb0 < kchunk) ? (k - kb0) : kchunk);
+    const int nit = (klen + static_cast<int>(kIterElems) - 1) / static_cast<int>(kIterElems);
+    const int nstage = (nit + U - 1) / U;
+    const int64_t row0 = rb * (W * R) + wave * R;
+
+    const __amdgpu_buffer_rsrc_t xbuf = buffer_of(x + b * (k / 2) + kb0 / 2, klen / 2);
+    const __amdgpu_buffer_rsrc_t sxbuf = buffer_of(sfx + b * (k / 16) + kb0 / 16, klen / 16);
+    __amdgpu_buffer_rsrc_t abuf_rs[R], sbuf_rs[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int64_t row = (row0 + r < m) ? row0 + r : m - 1;   // rows past m: read row m-1, never written
+        abuf_rs[r] = buffer_of(A + (b * m + row) * (k / 2) + kb0 / 2, klen / 2);
+        sbuf_rs[r] = buffer_of(sfA + (b * m + row) * (k / 16) + kb0 / 16, klen / 16);
+    }
+
+    u32x4 abuf[U][R], xq[U];
+    uint16_t sbuf[U][R], xs[U];
+    auto issue = [&](int it, int u) {
+        const int off = it * static_cast<int>(kIterElems / 2) + lane * 16;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            abuf[u][r] = __builtin_bit_cast(
+                u32x4, __builtin_amdgcn_raw_buffer_load_b128(abuf_rs[r], off, 0, kNonTemporal));
+            sbuf[u][r] = __builtin_amdgcn_raw_buffer_load_b16(sbuf_rs[r], off / 8, 0, kNonTemporal);
+        }
+        xq[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xbuf, off, 0, 0));
+        xs[u] = __builtin_amdgcn_raw_buffer_load_b16(sxbuf, off / 8, 0, 0);
+    };
+    auto consume = [&](int u, float (&acc)[R]) {
+        const f32x2 sx = e4m3x2_f32(xs[u]);
+#pragma unroll
+        for (int r = 0; r < R; ++r) acc[r] = chunk32_raw(abuf[u][r], sbuf[u][r], xq[u], sx, acc[r]);
+    };
+
+    float acc[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) acc[r] = 0.0f;
+
+    phase_fence();
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        issue(u, u);
+        phase_fence();
+    }
+    for (int st = 0; st + 1 < nstage; ++st) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            consume(u, acc);
+            issue(st * U + u + U, u);
+            phase_fence();
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        if ((nstage - 1) * U + u < nit) consume(u, acc);   // wave-uniform: skip iterations past K
+    }
+
+    float sum[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) sum[r] = wave_sum(acc[r]);
+
+    if (lane < R) {
+        float v = sum[0];
+#pragma unroll
+        for (int r = 1; r < R; ++r)
+            if (lane == r) v = sum[r];
+        const int64_t row = row0 + lane;
+        if (row < m) {
+            if (part != nullptr) {
+                part[(split * l + b) * m + row] = v;
+            } else {
+                const float al = alpha ? alpha[b] : 1.0f;
+                c[b * m + row] = f16_of_product(al, v);
+            }
+        }
+    }
+}
+
 // ---------------------------------------------------------------- generic kernel
 // Any k % 16 == 0 and any byte alignment of A, sfA, x, sfx.  One wave per
 // (split, batch, row); lanes take 16-element blocks; bytes are loaded singly
@@ -519,16 +621,22 @@ hbm_read_probe(const uint8_t *__restrict__ buf, int64_t n16, uint32_t *__restric
 }
 
 // ---------------------------------------------------------------- host side
+// x staging of a fast variant: fp16 x~ in LDS (gemv_fast), packed codes in LDS
+// (gemv_fastp), or no staging (gemv_fastg, x read next to A every iteration).
+enum XForm { kXHalf = 0, kXPacked = 1, kXGlobal = 2 };
+
 struct Variant {
     int R, U, W;
-    bool packed_x;   // x staged raw (gemv_fastp) rather than as fp16 x~ (gemv_fast)
+    int xform;
 };
-// Listed as {rows per wave, iterations in flight, waves, packed x}.
+// Listed as {rows per wave, iterations in flight, waves, x staging}.
 constexpr Variant kVariants[] = {
-    {2, 4, 7, false}, {1, 8, 4, false}, {2, 4, 4, false}, {2, 2, 4, false}, {4, 2, 4, false},
-    {2, 4, 8, false}, {1, 8, 8, false}, {4, 1, 4, false}, {2, 1, 8, false}, {1, 4, 4, false},
-    {2, 2, 4, true},  {4, 1, 4, true},  {4, 2, 4, true},  {2, 4, 8, true},  {4, 2, 8, true},
-    {1, 4, 8, true},
+    {2, 4, 7, kXHalf},    {1, 8, 4, kXHalf},    {2, 4, 4, kXHalf},    {2, 2, 4, kXHalf},
+    {4, 2, 4, kXHalf},    {2, 4, 8, kXHalf},    {1, 8, 8, kXHalf},    {4, 1, 4, kXHalf},
+    {2, 1, 8, kXHalf},    {1, 4, 4, kXHalf},    {2, 2, 4, kXPacked},  {4, 1, 4, kXPacked},
+    {4, 2, 4, kXPacked},  {2, 4, 8, kXPacked},  {4, 2, 8, kXPacked},  {1, 4, 8, kXPacked},
+    {2, 4, 7, kXGlobal},  {2, 2, 7, kXGlobal},  {4, 2, 7, kXGlobal},  {2, 4, 4, kXGlobal},
+    {1, 8, 7, kXGlobal},  {4, 1, 8, kXGlobal},
 };
 constexpr int kNumVariants = static_cast<int>(sizeof(kVariants) / sizeof(kVariants[0]));
 
@@ -554,6 +662,12 @@ FastKernel fast_kernel(int v) {
     case 13: return gemv_fastp<2, 4, 8>;
     case 14: return gemv_fastp<4, 2, 8>;
     case 15: return gemv_fastp<1, 4, 8>;
+    case 16: return gemv_fastg<2, 4, 7>;
+    case 17: return gemv_fastg<2, 2, 7>;
+    case 18: return gemv_fastg<4, 2, 7>;
+    case 19: return gemv_fastg<2, 4, 4>;
+    case 20: return gemv_fastg<1, 8, 7>;
+    case 21: return gemv_fastg<4, 1, 8>;
     default: return nullptr;
     }
 }
@@ -593,8 +707,8 @@ int check_shape(int64_t l, int64_t m, int64_t k) {
     return NVFP4_GEMV_OK;
 }
 
-// K split: one LDS stage (16384 elements) per workgroup at most for the fast
-// kernel; an explicit split must leave every split at least one granule (32
+// K split: one LDS stage (16384 elements) per workgroup at most for the
+// staged fast kernels; an explicit split must leave every split at least one granule (32
 // elements for the fast kernel, 16 for the generic one) and fit one stage.
 int split_k(int64_t k, int64_t ks_req, int64_t ks_auto, int64_t granule, bool staged,
             int64_t *ks_out, int64_t *kchunk_out) {
@@ -641,7 +755,8 @@ int make_plan(int64_t l, int64_t m, int64_t k, bool aligned, const nvfp4_gemv_tu
     const bool fast = p->path == NVFP4_GEMV_PATH_FAST;
     const int64_t granule = fast ? 32 : 16;
 
-    int64_t ks_auto = fast ? ceil_div(k, kMaxChunk) : 1;
+    const bool staged = fast && kVariants[p->variant].xform != kXGlobal;
+    int64_t ks_auto = staged ? ceil_div(k, kMaxChunk) : 1;
     if (groups1 * ks_auto < kTargetGroups) {
         const int64_t want = ceil_div(kTargetGroups, groups1);
         int64_t most = k / kMinSplitChunk;
@@ -650,17 +765,17 @@ int make_plan(int64_t l, int64_t m, int64_t k, bool aligned, const nvfp4_gemv_tu
         if (pick > ks_auto) ks_auto = pick;
     }
     int64_t ks, kchunk;
-    const int st = split_k(k, tun.ksplit, ks_auto, granule, fast, &ks, &kchunk);
+    const int st = split_k(k, tun.ksplit, ks_auto, granule, staged, &ks, &kchunk);
     if (st != NVFP4_GEMV_OK) return st;
     p->ksplit = ks;
     p->kchunk = kchunk;
     p->groups = groups1 * ks;
     if (p->groups >= (int64_t(1) << 31)) return NVFP4_GEMV_ERR_BAD_SHAPE;
-    if (fast) {
+    if (staged) {
         const Variant &v = kVariants[p->variant];
         const int64_t slots = ceil_div(ceil_div(kchunk, kIterElems), v.U) * v.U;
         // per slot and lane: 64 bytes of fp16 x~, or 16 bytes of codes + 4 of scales
-        p->lds_bytes = static_cast<size_t>(slots) * kWave * (v.packed_x ? 20 : 64);
+        p->lds_bytes = static_cast<size_t>(slots) * kWave * (v.xform == kXPacked ? 20 : 64);
     } else {
         p->lds_bytes = 0;
     }
@@ -769,14 +884,14 @@ const char *nvfp4_gemv_status_string(int status) {
 int nvfp4_gemv_num_variants(void) { return kNumVariants; }
 
 int nvfp4_gemv_variant_info(int v, int32_t *rows_per_wave, int32_t *iters_in_flight,
-                            int32_t *waves_per_group, int32_t *packed_x) {
-    if (!rows_per_wave || !iters_in_flight || !waves_per_group || !packed_x)
+                            int32_t *waves_per_group, int32_t *x_staging) {
+    if (!rows_per_wave || !iters_in_flight || !waves_per_group || !x_staging)
         return NVFP4_GEMV_ERR_NULL_POINTER;
     if (v < 1 || v > kNumVariants) return NVFP4_GEMV_ERR_BAD_TUNING;
     *rows_per_wave = kVariants[v - 1].R;
     *iters_in_flight = kVariants[v - 1].U;
     *waves_per_group = kVariants[v - 1].W;
-    *packed_x = kVariants[v - 1].packed_x ? 1 : 0;
+    *x_staging = kVariants[v - 1].xform;
     return NVFP4_GEMV_OK;
 }
 

@@ -126,14 +126,14 @@ def test_plan_rejects_bad_tuning(lib):
 def test_plan_explicit_choices(lib):
     n = pd.nvfp4_gemv_num_variants()
     assert n >= 1
-    packed = 0
+    forms = set()
     for v in range(1, n + 1):
         r, u, w, px = pd.nvfp4_gemv_variant_info(v)
-        assert r >= 1 and u >= 1 and 1 <= w <= 16 and px in (0, 1)
-        packed += px
+        assert r >= 1 and u >= 1 and 1 <= w <= 16 and px in (0, 1, 2)
+        forms.add(px)
         t, _ = pd.nvfp4_gemv_plan(3, 100, 4096, tuning={"variant": v, "ksplit": 2})
         assert t.path == pd.NVFP4_GEMV_PATH_FAST and t.variant == v and t.ksplit == 2
-    assert 0 < packed < n          # both x staging forms are available
+    assert forms == {0, 1, 2}      # every x staging form is available
     with pytest.raises(pd.Nvfp4GemvError):
         pd.nvfp4_gemv_variant_info(n + 1)
     with pytest.raises(pd.Nvfp4GemvError):

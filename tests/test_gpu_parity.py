@@ -128,11 +128,16 @@ def test_generic_kernel(l, m, k, ksplit):
     assert_bits_equal(run_gpu(to_device(ops), l, m, k, tuning=tun), want, "generic")
 
 
-@pytest.mark.parametrize("variant", range(1, 17))
+NUM_VARIANTS = 22
+
+
+def test_variant_count():
+    assert pd.nvfp4_gemv_num_variants() == NUM_VARIANTS
+
+
+@pytest.mark.parametrize("variant", range(1, NUM_VARIANTS + 1))
 @pytest.mark.parametrize("ksplit", [1, 2, 5])
 def test_every_variant_and_split(variant, ksplit):
-    if variant > pd.nvfp4_gemv_num_variants():
-        pytest.skip("variant not built")
     l, m, k = 2, 77, 10240
     ops = workloads.integer_coded(l, m, k, seed=variant * 10 + ksplit, alpha="uniform")
     want = oracle_out(ops, l, m, k)
