@@ -53,6 +53,7 @@ constexpr int64_t kIterElems = 2048;    // K elements one wave covers per row pe
 constexpr int64_t kMaxChunk = 16384;    // K elements staged in LDS per workgroup (32 KiB)
 constexpr int64_t kMinSplitChunk = 2048;
 constexpr int64_t kTargetGroups = 512;  // workgroups wanted before splitting K
+constexpr int64_t kComputeUnits = 256;  // MI355X: 8 XCDs x 32 CUs
 constexpr int kReduceThreads = 256;
 constexpr int kGenericWaves = 4;
 constexpr int kProbeThreads = 256;
@@ -516,6 +517,143 @@ gemv_fastg(const uint8_t *__restrict__ A, const uint8_t *__restrict__ sfA,
     }
 }
 
+// ---------------------------------------------------------------- row-tile kernel
+// A workgroup owns a tile of 16 rows of one batch and the K-range of its
+// split; its W waves share the tile and take K slices of 2048 elements
+// (1 KiB of every row) in turn: wave w takes slices w, w + W, ...  For one
+// slice a wave issues, back to back, x's 16 bytes and scale pair per lane
+// and then one 16-byte load per lane for each of the 16 rows (1 KiB of a row
+// per instruction) with the row's scale pair, so 16 KiB of A per wave are
+// in flight at once and every load is row-contiguous.  x~ of the lane's 32
+// elements is decoded once into registers and serves all 16 rows; no LDS
+// holds x, and nothing waits at a barrier before the arithmetic.  A row is
+// consumed as soon as its load lands, in issue order.
+//
+// Reduction: the 16 per-lane partial sums are halved twice by swapping the
+// 32-lane halves and then the 16-lane rows of the wave (each lane keeps the
+// rows its half or row is responsible for and adds its partner's values),
+// then summed inside each 16-lane row by DPP.  The waves' row sums meet in
+// LDS and wave 0 adds them in wave order, so the result does not depend on
+// timing.
+constexpr int kTileRows = 16;
+constexpr int kTileMaxWaves = 8;
+
+template <int W>
+__global__ void __launch_bounds__(W * kWave)
+gemv_tile(const uint8_t *__restrict__ A, const uint8_t *__restrict__ sfA,
+          const uint8_t *__restrict__ x, const uint8_t *__restrict__ sfx,
+          const float *__restrict__ alpha, uint16_t *__restrict__ c,
+          float *__restrict__ part, int64_t l, int64_t m, int64_t k,
+          int64_t kchunk, int64_t row_blocks) {
+    static_assert(W >= 1 && W <= kTileMaxWaves, "waves per tile");
+    __shared__ float red[W * kTileRows];
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+
+    int64_t g = blockIdx.x;
+    const int64_t rb = g % row_blocks;
+    g /= row_blocks;
+    const int64_t b = g % l;
+    const int64_t split = g / l;
+
+    const int64_t kb0 = split * kchunk;
+    const int klen = static_cast<int>((k - kb0 < kchunk) ? (k - kb0) : kchunk);
+    const int nsl = (klen + static_cast<int>(kIterElems) - 1) / static_cast<int>(kIterElems);
+    const int64_t row0 = rb * kTileRows;
+    const int nrows = static_cast<int>((m - row0 < kTileRows) ? (m - row0) : kTileRows);
+    const int half = static_cast<int>(k / 2), sixteenth = static_cast<int>(k / 16);
+
+    // One descriptor per operand over the tile's rows, from the split's first
+    // element: row r's bytes start at r * half (codes) and r * sixteenth
+    // (scales).  Offsets of rows past the tile's end, and of lanes past the
+    // K-range, are past the descriptor's range and read zeros.
+    const __amdgpu_buffer_rsrc_t ad = buffer_of(A + (b * m + row0) * half + kb0 / 2, nrows * half);
+    const __amdgpu_buffer_rsrc_t sd =
+        buffer_of(sfA + (b * m + row0) * sixteenth + kb0 / 16, nrows * sixteenth);
+    const __amdgpu_buffer_rsrc_t xbuf = buffer_of(x + b * half + kb0 / 2, klen / 2);
+    const __amdgpu_buffer_rsrc_t sxbuf = buffer_of(sfx + b * sixteenth + kb0 / 16, klen / 16);
+
+    float acc[kTileRows];
+#pragma unroll
+    for (int r = 0; r < kTileRows; ++r) acc[r] = 0.0f;
+
+    for (int s = wave; s < nsl; s += W) {
+        const int e0 = s * static_cast<int>(kIterElems) + 32 * lane;   // lane's first element
+        const int xo = e0 / 2;
+        const uint32_t lo = e0 < klen ? static_cast<uint32_t>(xo) : kOutOfRange;
+        const uint32_t lso = e0 < klen ? static_cast<uint32_t>(e0 / 16) : kOutOfRange;
+
+        phase_fence();
+        const u32x4 xv = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xbuf, xo, 0, 0));
+        const uint16_t xs2 = __builtin_amdgcn_raw_buffer_load_b16(sxbuf, e0 / 16, 0, 0);
+        u32x4 av[kTileRows];
+        uint16_t sv[kTileRows];
+#pragma unroll
+        for (int r = 0; r < kTileRows; ++r) {
+            av[r] = __builtin_bit_cast(
+                u32x4, __builtin_amdgcn_raw_buffer_load_b128(ad, lo + r * half, 0, kNonTemporal));
+            sv[r] = __builtin_amdgcn_raw_buffer_load_b16(sd, lso + r * sixteenth, 0, kNonTemporal);
+            phase_fence();   // row by row, in the order the rows are consumed
+        }
+
+        u32x4 xq[4];
+        decode_x32(xv, xs2, xq);
+#pragma unroll
+        for (int r = 0; r < kTileRows; ++r) acc[r] = chunk32(av[r], sv[r], xq, acc[r]);
+    }
+
+    // Halve across the 32-lane halves: the low half keeps rows 0..7, the high
+    // half rows 8..15.
+    float h8[8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+        const auto t = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, acc[r]),
+                                                        __builtin_bit_cast(unsigned, acc[r + 8]),
+                                                        false, false);
+        h8[r] = __builtin_bit_cast(float, static_cast<unsigned>(t[0])) +
+                __builtin_bit_cast(float, static_cast<unsigned>(t[1]));
+    }
+    // Halve across 16-lane rows: even rows keep values 0..3, odd rows 4..7.
+    float h4[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const auto t = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, h8[r]),
+                                                        __builtin_bit_cast(unsigned, h8[r + 4]),
+                                                        false, false);
+        h4[r] = __builtin_bit_cast(float, static_cast<unsigned>(t[0])) +
+                __builtin_bit_cast(float, static_cast<unsigned>(t[1]));
+    }
+    // Sum inside each 16-lane row.
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        float v = h4[r];
+        v += dpp<0xB1>(v);    // quad_perm [1,0,3,2]
+        v += dpp<0x4E>(v);    // quad_perm [2,3,0,1]
+        v += dpp<0x141>(v);   // row_half_mirror
+        v += dpp<0x140>(v);   // row_mirror
+        h4[r] = v;
+    }
+    // Lane j < 4 of 16-lane row q (q = lane / 16) holds tile row j + 4 (q & 1) + 8 (q >> 1).
+    const int j = lane & 15, q = lane >> 4;
+    if (j < 4) {
+        const float v = j == 0 ? h4[0] : j == 1 ? h4[1] : j == 2 ? h4[2] : h4[3];
+        red[wave * kTileRows + j + 4 * (q & 1) + 8 * (q >> 1)] = v;
+    }
+    __syncthreads();
+    if (wave == 0 && lane < nrows) {
+        float v = red[lane];
+#pragma unroll
+        for (int w = 1; w < W; ++w) v += red[w * kTileRows + lane];
+        const int64_t row = row0 + lane;
+        if (part != nullptr) {
+            part[(split * l + b) * m + row] = v;
+        } else {
+            const float al = alpha ? alpha[b] : 1.0f;
+            c[b * m + row] = f16_of_product(al, v);
+        }
+    }
+}
+
 // ---------------------------------------------------------------- generic kernel
 // Any k % 16 == 0 and any byte alignment of A, sfA, x, sfx.  One wave per
 // (split, batch, row); lanes take 16-element blocks; bytes are loaded singly
@@ -622,8 +760,14 @@ hbm_read_probe(const uint8_t *__restrict__ buf, int64_t n16, uint32_t *__restric
 
 // ---------------------------------------------------------------- host side
 // x staging of a fast variant: fp16 x~ in LDS (gemv_fast), packed codes in LDS
-// (gemv_fastp), or no staging (gemv_fastg, x read next to A every iteration).
-enum XForm { kXHalf = 0, kXPacked = 1, kXGlobal = 2 };
+// (gemv_fastp), no staging (gemv_fastg, x read next to A every iteration), or
+// 16-row tiles whose waves split K and keep x~ of their slice in registers
+// (gemv_tile).
+enum XForm { kXHalf = 0, kXPacked = 1, kXGlobal = 2, kXTile = 3 };
+
+// The row-tile kernel addresses a tile's 16 rows through one descriptor with
+// 32-bit offsets; it takes K up to this bound.
+constexpr int64_t kTileMaxK = int64_t(1) << 26;
 
 struct Variant {
     int R, U, W;
@@ -636,7 +780,8 @@ constexpr Variant kVariants[] = {
     {2, 1, 8, kXHalf},    {1, 4, 4, kXHalf},    {2, 2, 4, kXPacked},  {4, 1, 4, kXPacked},
     {4, 2, 4, kXPacked},  {2, 4, 8, kXPacked},  {4, 2, 8, kXPacked},  {1, 4, 8, kXPacked},
     {2, 4, 7, kXGlobal},  {2, 2, 7, kXGlobal},  {4, 2, 7, kXGlobal},  {2, 4, 4, kXGlobal},
-    {1, 8, 7, kXGlobal},  {4, 1, 8, kXGlobal},
+    {1, 8, 7, kXGlobal},  {4, 1, 8, kXGlobal},  {16, 1, 8, kXTile},   {16, 1, 4, kXTile},
+    {16, 1, 2, kXTile},   {16, 1, 1, kXTile},
 };
 constexpr int kNumVariants = static_cast<int>(sizeof(kVariants) / sizeof(kVariants[0]));
 
@@ -668,6 +813,10 @@ FastKernel fast_kernel(int v) {
     case 19: return gemv_fastg<2, 4, 4>;
     case 20: return gemv_fastg<1, 8, 7>;
     case 21: return gemv_fastg<4, 1, 8>;
+    case 22: return gemv_tile<8>;
+    case 23: return gemv_tile<4>;
+    case 24: return gemv_tile<2>;
+    case 25: return gemv_tile<1>;
     default: return nullptr;
     }
 }
@@ -677,14 +826,15 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // Default fast variant (0-based) by the number of 1 KiB K-iterations per row
 // of one workgroup's K-range, from MI355X measurements on the decode, batched,
 // Gaussian and short-K workloads: long rows want more rows in flight per
-// workgroup, short rows more rows per wave; with 2 to 5 iterations per row
-// the packed-x kernel's smaller LDS footprint wins.
+// workgroup; with 3 to 5 iterations per row x read next to A beats staging it;
+// rows of one or two iterations are best read as 16-row tiles, whose 16 loads
+// per wave are all in flight at once.
 int default_variant(int64_t k) {
     const int64_t nit = ceil_div(k < kMaxChunk ? k : kMaxChunk, kIterElems);
     if (nit >= 6) return 0;    // {2, 4, 7}
-    if (nit >= 3) return 2;    // {2, 4, 4}
-    if (nit == 2) return 11;   // {4, 1, 4} packed x
-    return 7;                  // {4, 1, 4}
+    if (nit >= 3) return 19;   // {2, 4, 4} x read next to A
+    if (nit == 2) return 24;   // 16-row tile, 2 waves
+    return 25;                 // 16-row tile, 1 wave
 }
 
 struct Plan {
@@ -743,7 +893,8 @@ int make_plan(int64_t l, int64_t m, int64_t k, bool aligned, const nvfp4_gemv_tu
     int64_t rows_per_group;
     if (p->path == NVFP4_GEMV_PATH_FAST) {
         const Variant &v = kVariants[p->variant];
-        rows_per_group = static_cast<int64_t>(v.R) * v.W;
+        if (v.xform == kXTile && k > kTileMaxK) return NVFP4_GEMV_ERR_BAD_TUNING;
+        rows_per_group = v.xform == kXTile ? kTileRows : static_cast<int64_t>(v.R) * v.W;
         p->threads = v.W * kWave;
     } else {
         p->variant = 0;
@@ -755,11 +906,17 @@ int make_plan(int64_t l, int64_t m, int64_t k, bool aligned, const nvfp4_gemv_tu
     const bool fast = p->path == NVFP4_GEMV_PATH_FAST;
     const int64_t granule = fast ? 32 : 16;
 
-    const bool staged = fast && kVariants[p->variant].xform != kXGlobal;
+    const int xform = fast ? kVariants[p->variant].xform : -1;
+    const bool staged = xform == kXHalf || xform == kXPacked;
     int64_t ks_auto = staged ? ceil_div(k, kMaxChunk) : 1;
-    if (groups1 * ks_auto < kTargetGroups) {
-        const int64_t want = ceil_div(kTargetGroups, groups1);
-        int64_t most = k / kMinSplitChunk;
+    // A tile's waves already split K: split it across workgroups only while
+    // the tiles leave compute units idle, and only as far as every split
+    // keeps a slice for each wave.
+    const int64_t target = xform == kXTile ? kComputeUnits : kTargetGroups;
+    if (groups1 * ks_auto < target) {
+        const int64_t want = ceil_div(target, groups1);
+        int64_t most = xform == kXTile ? ceil_div(k, kIterElems) / kVariants[p->variant].W
+                                       : k / kMinSplitChunk;
         if (most < 1) most = 1;
         const int64_t pick = want < most ? want : most;
         if (pick > ks_auto) ks_auto = pick;

@@ -129,11 +129,11 @@ def test_plan_explicit_choices(lib):
     forms = set()
     for v in range(1, n + 1):
         r, u, w, px = pd.nvfp4_gemv_variant_info(v)
-        assert r >= 1 and u >= 1 and 1 <= w <= 16 and px in (0, 1, 2)
+        assert r >= 1 and u >= 1 and 1 <= w <= 16 and px in (0, 1, 2, 3)
         forms.add(px)
         t, _ = pd.nvfp4_gemv_plan(3, 100, 4096, tuning={"variant": v, "ksplit": 2})
         assert t.path == pd.NVFP4_GEMV_PATH_FAST and t.variant == v and t.ksplit == 2
-    assert forms == {0, 1, 2}      # every x staging form is available
+    assert forms == {0, 1, 2, 3}   # every x staging form is available
     with pytest.raises(pd.Nvfp4GemvError):
         pd.nvfp4_gemv_variant_info(n + 1)
     with pytest.raises(pd.Nvfp4GemvError):
@@ -143,6 +143,26 @@ def test_plan_explicit_choices(lib):
     t, ws = pd.nvfp4_gemv_plan(3, 100, 4096, tuning={"path": pd.NVFP4_GEMV_PATH_GENERIC, "ksplit": 5})
     assert t.path == pd.NVFP4_GEMV_PATH_GENERIC and t.ksplit == 5 and ws == 5 * 300 * 4
 
+
+
+def test_tile_variants_plan(lib):
+    """16-row tile variants: K bound, no K split while waves cover the slices."""
+    tiles = [v for v in range(1, pd.nvfp4_gemv_num_variants() + 1)
+             if pd.nvfp4_gemv_variant_info(v)[3] == 3]
+    assert tiles
+    for v in tiles:
+        r, u, w, _ = pd.nvfp4_gemv_variant_info(v)
+        assert r == 16 and u == 1
+        with pytest.raises(pd.Nvfp4GemvError):
+            pd.nvfp4_gemv_plan(1, 64, 2 ** 26 + 32, tuning={"variant": v})
+        t, ws = pd.nvfp4_gemv_plan(1, 64, 2 ** 26, tuning={"variant": v, "ksplit": 1})
+        assert t.ksplit == 1 and ws == 0
+        # 448 tiles fill the 256 compute units: no split
+        t, _ = pd.nvfp4_gemv_plan(1, 7168, 16384, tuning={"variant": v})
+        assert t.ksplit == 1
+        # 8 tiles: split while each split keeps a slice for every wave
+        t, _ = pd.nvfp4_gemv_plan(1, 128, 16384, tuning={"variant": v})
+        assert t.ksplit == max(1, 8 // w)
 
 def test_probe_validation(lib):
     assert lib.nvfp4_hbm_read_probe(None, 1024, C, None) == pd.NVFP4_GEMV_ERR_NULL_POINTER
