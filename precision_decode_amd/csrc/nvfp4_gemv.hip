@@ -104,6 +104,19 @@ __device__ __forceinline__ u32x4 load_nt16(const uint8_t *p) {
 }
 
 
+// (row block, batch, split) of this workgroup, row block fastest.  The plan
+// keeps the workgroup count below 2^31, so 32-bit division suffices (much
+// shorter than 64-bit division, which every workgroup would run first).
+__device__ __forceinline__ void group_index(int64_t row_blocks, int64_t l, int64_t *rb,
+                                            int64_t *b, int64_t *split) {
+    const uint32_t g = blockIdx.x;
+    const uint32_t rbs = static_cast<uint32_t>(row_blocks), ls = static_cast<uint32_t>(l);
+    const uint32_t q = g / rbs;
+    *rb = g - q * rbs;
+    *b = q % ls;
+    *split = q / ls;
+}
+
 // ---------------------------------------------------------------- fast kernel
 // Workgroup = W waves; wave w streams rows rb*W*R + w*R .. +R-1 of batch b over
 // the K-range [split*kchunk, min(k, (split+1)*kchunk)).  blockIdx.x enumerates
@@ -143,11 +156,8 @@ gemv_fast(const uint8_t *__restrict__ A, const uint8_t *__restrict__ sfA,
     const int lane = tid & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
 
-    int64_t g = blockIdx.x;
-    const int64_t rb = g % row_blocks;
-    g /= row_blocks;
-    const int64_t b = g % l;
-    const int64_t split = g / l;
+    int64_t rb, b, split;
+    group_index(row_blocks, l, &rb, &b, &split);
 
     const int64_t kb0 = split * kchunk;
     const int klen = static_cast<int>((k - kb0 < kchunk) ? (k - kb0) : kchunk);
@@ -307,11 +317,8 @@ gemv_fastp(const uint8_t *__restrict__ A, const uint8_t *__restrict__ sfA,
     const int lane = tid & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
 
-    int64_t g = blockIdx.x;
-    const int64_t rb = g % row_blocks;
-    g /= row_blocks;
-    const int64_t b = g % l;
-    const int64_t split = g / l;
+    int64_t rb, b, split;
+    group_index(row_blocks, l, &rb, &b, &split);
 
     const int64_t kb0 = split * kchunk;
     const int klen = static_cast<int>((k - kb0 < kchunk) ? (k - kb0) : kchunk);
@@ -432,11 +439,8 @@ gemv_fastg(const uint8_t *__restrict__ A, const uint8_t *__restrict__ sfA,
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
 
-    int64_t g = blockIdx.x;
-    const int64_t rb = g % row_blocks;
-    g /= row_blocks;
-    const int64_t b = g % l;
-    const int64_t split = g / l;
+    int64_t rb, b, split;
+    group_index(row_blocks, l, &rb, &b, &split);
 
     const int64_t kb0 = split * kchunk;
     const int klen = static_cast<int>((k - kb0 < kchunk) ? (k - kb0) : kchunk);
@@ -550,11 +554,8 @@ gemv_tile(const uint8_t *__restrict__ A, const uint8_t *__restrict__ sfA,
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
 
-    int64_t g = blockIdx.x;
-    const int64_t rb = g % row_blocks;
-    g /= row_blocks;
-    const int64_t b = g % l;
-    const int64_t split = g / l;
+    int64_t rb, b, split;
+    group_index(row_blocks, l, &rb, &b, &split);
 
     const int64_t kb0 = split * kchunk;
     const int klen = static_cast<int>((k - kb0 < kchunk) ? (k - kb0) : kchunk);
@@ -679,11 +680,8 @@ gemv_generic(const uint8_t *__restrict__ A, const uint8_t *__restrict__ sfA,
              int64_t row_blocks) {
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
-    int64_t g = blockIdx.x;
-    const int64_t rb = g % row_blocks;
-    g /= row_blocks;
-    const int64_t b = g % l;
-    const int64_t split = g / l;
+    int64_t rb, b, split;
+    group_index(row_blocks, l, &rb, &b, &split);
     const int64_t row = rb * kGenericWaves + wave;
     if (row >= m) return;
 

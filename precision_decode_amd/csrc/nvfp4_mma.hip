@@ -156,11 +156,13 @@ __global__ void __launch_bounds__(W * kWave) mma_stream(const MmaArgs a) {
     const int li = lane & (kTile - 1);
     const int kq = lane >> 4;
 
-    int64_t gi = blockIdx.x;
-    const int64_t rb = gi % a.row_blocks;
-    gi /= a.row_blocks;
-    const int64_t grp = gi % a.groups;
-    const int64_t split = gi / a.groups;
+    // the plan keeps the workgroup count below 2^31: 32-bit division
+    const uint32_t gi = blockIdx.x;
+    const uint32_t rbs = static_cast<uint32_t>(a.row_blocks), gs = static_cast<uint32_t>(a.groups);
+    const uint32_t q = gi / rbs;
+    const int64_t rb = gi - q * rbs;
+    const int64_t grp = q % gs;
+    const int64_t split = q / gs;
 
     int64_t v0, v1;
     vector_range<GROUPED>(a, grp, &v0, &v1);
@@ -315,8 +317,9 @@ template <bool GROUPED>
 __global__ void __launch_bounds__(kGenericWaves * kWave) mma_generic(const MmaArgs a) {
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
-    const int64_t rb = blockIdx.x % a.row_blocks;
-    const int64_t grp = blockIdx.x / a.row_blocks;
+    const uint32_t rbs = static_cast<uint32_t>(a.row_blocks);
+    const int64_t rb = blockIdx.x % rbs;
+    const int64_t grp = blockIdx.x / rbs;
     const int64_t row = rb * kGenericWaves + wave;
     if (row >= a.rows) return;
     int64_t v0, v1;
