@@ -20,34 +20,33 @@
 //
 // Work mapping: one lane per 16-element block (32 bytes of bf16 in, 8 bytes of
 // codes and 1 scale byte out), blocks numbered across rows so any row length
-// that is a multiple of 16 keeps the wave's loads and stores contiguous.  Divisions by the global and block scales use one
-// reciprocal per block and fused residual corrections, which round exactly as
-// IEEE division does in the range the kernel checks for; the E2M1 rounding
-// uses gfx950's FP4 conversion where a rule allows.
+// that is a multiple of 16 keeps the wave's loads and stores contiguous.  A
+// wave reads its 64 blocks (2 KiB) with two 16-byte loads per lane that each
+// cover 1 KiB contiguously, and hands every lane its block through LDS.  The
+// divisions round exactly as IEEE division does without its cost: x / g as
+// an fp64 product with 1/g (the quotient of a bf16 by an fp32 never lies
+// within 2^-49 of an fp32 rounding midpoint, the fp64 product is within
+// 2^-52), x_n / s as one reciprocal and one fused residual correction (the
+// block scale has 4 significant bits, so quotients stay 2^-29 away from
+// midpoints); blocks outside the range this holds for take IEEE divisions.
+// The E2M1 rounding of every rule runs on gfx950's FP4 conversion.
 #include <hip/hip_runtime.h>
 
 #include <cstddef>
 #include <cstdint>
 
+#include "device_common.h"
 #include "nvfp4_gemv.h"
 #include "nvfp4_quantize.h"
 
 namespace {
 
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+using nvfp4dev::kWave;
+using nvfp4dev::u32x4;
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kQuantThreads = 256;
-
-// The page's half-step table (doubled, rounded magnitude 0..12 -> E2M1 index),
-// four bits per entry.
-constexpr uint64_t half_step_table() {
-    constexpr uint8_t t[13] = {0, 1, 2, 3, 4, 4, 5, 5, 6, 6, 6, 7, 7};
-    uint64_t r = 0;
-    for (int i = 0; i < 13; ++i) r |= static_cast<uint64_t>(t[i]) << (4 * i);
-    return r;
-}
-constexpr uint64_t kHalfStep = half_step_table();
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
 
@@ -72,154 +71,127 @@ __device__ __forceinline__ float e4m3_value_pos(uint32_t s) {
     return __uint_as_float((((s >> 3) + 120u) << 23) | ((s & 7u) << 20));
 }
 
-template <int RULE>
-__device__ __forceinline__ uint32_t e2m1_index(float v) {
-    float a = __builtin_fabsf(v);
-    if (a != a) a = 0.0f;                          // NaN -> index 0
-    if constexpr (RULE == NVFP4_ROUND_HALF_STEP) {
-        const float h = __builtin_rintf((a < 6.0f ? a : 6.0f) * 2.0f);   // 0..12, exact
-        const uint32_t hi = static_cast<uint32_t>(h);
-        return static_cast<uint32_t>(kHalfStep >> (4 * hi)) & 7u;
-    } else if constexpr (RULE == NVFP4_ROUND_NEAREST_EVEN) {
-        // count the midpoints below a; on a midpoint take the even neighbour
-        return static_cast<uint32_t>(a > 0.25f) + static_cast<uint32_t>(a >= 0.75f) +
-               static_cast<uint32_t>(a > 1.25f) + static_cast<uint32_t>(a >= 1.75f) +
-               static_cast<uint32_t>(a > 2.5f) + static_cast<uint32_t>(a >= 3.5f) +
-               static_cast<uint32_t>(a > 5.0f);
-    } else {
-        // argmin over fp32 distances, first index on ties
-        constexpr float g[8] = {0.0f, 0.5f, 1.0f, 1.5f, 2.0f, 3.0f, 4.0f, 6.0f};
-        uint32_t best = 0;
-        float bd = a;
-#pragma unroll
-        for (int j = 1; j < 8; ++j) {
-            const float d = __builtin_fabsf(a - g[j]);
-            if (d < bd) {
-                bd = d;
-                best = static_cast<uint32_t>(j);
-            }
-        }
-        return best;
-    }
+// RN32(a / b) from y = RN64(1/b) as RN32(RN64(a * y)): exact whenever a/b,
+// if not representable, lies more than 2^-51 (relative) from every fp32
+// rounding midpoint and is not a subnormal fp32 number.
+__device__ __forceinline__ float quot_f64(float a, double y) {
+    return static_cast<float>(static_cast<double>(a) * y);
 }
 
-// a / b rounded to nearest even, given y = RN(1/b): q = a*y, then two
-// residual corrections q += (a - b*q)*y with exact fused residuals.  After the
-// first correction q is within an ulp of a/b, so the second one rounds
-// correctly (Markstein's theorem for round-to-nearest).  The caller keeps b,
-// 1/b and the quotient inside the normal range (see `fast` below); a zero
-// quotient comes out as +0.
-__device__ __forceinline__ float div_rn(float a, float b, float y) {
-    float q = a * y;
-    float e = __builtin_fmaf(-b, q, a);
-    q = __builtin_fmaf(e, y, q);
-    e = __builtin_fmaf(-b, q, a);
+// RN32(a / b) for b with at most 4 significant bits, from y within 2^-22 of
+// 1/b: q = RN(a*y) is within 2^-21 of a/b, the residual a - b*q is exact, and
+// one correction lands within 2^-42 of a/b, far closer than the 2^-29 that
+// separates a/b from any rounding midpoint; a zero quotient comes out as +0.
+__device__ __forceinline__ float quot_short(float a, float b, float y) {
+    const float q = a * y;
+    const float e = __builtin_fmaf(-b, q, a);
     return __builtin_fmaf(e, y, q);
 }
 
 // Codes of 16 values v[i] (element i at nibble i of the 64-bit result) under
-// the rule, sign bit 8 for v < 0, NaN -> 0.
-//  * nearest-even: the gfx950 FP4 conversion rounds to nearest even on the
-//    E2M1 grid and saturates at 6, with the sign of v; only -0 (code 8, not 0)
-//    and NaN differ from the rule, and the caller removes both;
-//  * nearest-lower (argmin of fp32 distances, first on ties): the same
-//    conversion, one step down at the three ties whose even neighbour is the
-//    upper one (0.75, 1.75, 3.5).  For |v| <= 2^20, which every block here
-//    satisfies (|v| <= 6.25, or < 6e5 when the block scale rounds to zero),
-//    the fp32 distances are exact near every tie, so the argmin is the nearest
-//    value with ties down, and 6 beyond the grid;
-//  * half-step: the page's table on rint(2 min(|v|, 6)).
+// the rule, sign bit 8 for v < 0, NaN -> 0, all on the gfx950 FP4 conversion,
+// which rounds to nearest even on the E2M1 grid and saturates at 6, with the
+// sign of v.  It differs from the rules only at -0 (code 8, not 0) and NaN,
+// which the caller rules out.
+//  * nearest-even: the conversion itself;
+//  * nearest-lower (argmin of fp32 distances, first on ties): the ties where
+//    nearest-even goes up (0.75, 1.75, 3.5) are exactly the grid midpoints
+//    whose fp32 pattern has mantissa bit 22 set and bits 20..0 clear; those
+//    values, and only ever values whose rounding one ulp down cannot change
+//    (grid points, non-midpoints), move one ulp towards zero first.  For
+//    |v| <= 2^20, which every block satisfies (|v| <= 6.25, or < 6e5 when the
+//    block scale rounds to zero), the fp32 distances are exact near every tie,
+//    so the argmin is the nearest value with ties down, and 6 beyond the grid;
+//  * half-step (the page's table on rint(2 min(|v|, 6))): below 2 the table is
+//    nearest-even on the grid; from 2 its cut points 2.75, 3.75 and 5.25 sit
+//    0.25 above the grid midpoints 2.5, 3.5 and 5, so |v| - 0.25 (exact there)
+//    is rounded instead, clamped below at 2 (med3), and the one cut whose tie
+//    goes the other way, |v| = 2.75, maps to 3.
 template <int RULE>
 __device__ __forceinline__ u32x2 block_codes(const float (&v)[16]) {
-    u32x2 out;
-    if constexpr (RULE == NVFP4_ROUND_HALF_STEP) {
-        uint32_t packed[2] = {0u, 0u};
+    float t[16];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const uint32_t code = e2m1_index<RULE>(v[i]) | (v[i] < 0.0f ? 8u : 0u);
-            packed[i >> 3] |= code << (4 * (i & 7));
-        }
-        out.x = packed[0];
-        out.y = packed[1];
-    } else {
-        uint32_t w[2] = {0u, 0u};
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            w[j] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w[j], v[8 * j + 0], v[8 * j + 1], 1.0f, 0);
-            w[j] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w[j], v[8 * j + 2], v[8 * j + 3], 1.0f, 1);
-            w[j] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w[j], v[8 * j + 4], v[8 * j + 5], 1.0f, 2);
-            w[j] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w[j], v[8 * j + 6], v[8 * j + 7], 1.0f, 3);
-        }
+    for (int i = 0; i < 16; ++i) {
         if constexpr (RULE == NVFP4_ROUND_NEAREST_LOWER) {
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const float a = __builtin_fabsf(v[i]);
-                const bool down = a == 0.75f || a == 1.75f || a == 3.5f;
-                w[i >> 3] -= down ? (1u << (4 * (i & 7))) : 0u;   // index >= 2 there: no borrow
-            }
+            const uint32_t b = __float_as_uint(v[i]);
+            t[i] = __uint_as_float(b - ((b & 0x005FFFFFu) == 0x00400000u ? 1u : 0u));
+        } else if constexpr (RULE == NVFP4_ROUND_HALF_STEP) {
+            const float a = __builtin_fabsf(v[i]);
+            float m = __builtin_amdgcn_fmed3f(a - 0.25f, a, 2.0f);
+            m = a == 2.75f ? 3.0f : m;
+            t[i] = __builtin_copysignf(m, v[i]);
+        } else {
+            t[i] = v[i];
         }
-        out.x = w[0];
-        out.y = w[1];
     }
-    return out;
+    uint32_t w[2] = {0u, 0u};
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        w[j] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w[j], t[8 * j + 0], t[8 * j + 1], 1.0f, 0);
+        w[j] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w[j], t[8 * j + 2], t[8 * j + 3], 1.0f, 1);
+        w[j] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w[j], t[8 * j + 4], t[8 * j + 5], 1.0f, 2);
+        w[j] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w[j], t[8 * j + 6], t[8 * j + 7], 1.0f, 3);
+    }
+    return u32x2{w[0], w[1]};
 }
 
 // One 16-element block: bf16 words w0, w1 (elements 2i, 2i+1 in word i) with
 // global scale g -> 8 bytes of codes and the E4M3 scale code.
 //
-// Fast path: with the global scale in [2^-40, 2^30] and every nonzero input
-// at least 2^-100 in magnitude, x/g and xn/den stay inside the range where
-// div_rn rounds correctly (a tiny quotient's exact value never changes its
-// code: only its sign counts there), so both divisions take one reciprocal
-// per block and five fused operations per element.  Other blocks (rare: a
-// subnormal input, an extreme or non-finite scale) take IEEE divisions.
+// The block amax of |x/g| is RN(max|x| / |g|) (rounding is monotonic), taken
+// on the bf16 magnitude patterns (NaN patterns sort above +Inf, so a NaN
+// wins).  Fast path, for g in [2^-40, 2^30] and every nonzero |x| >= 2^-100:
+// x/g through quot_f64 and, unless the block scale rounded to zero, v = x_n / s
+// through quot_short, which round as IEEE division does here (a quotient too
+// small for the fp32 normal range only ever counts by its sign, which both
+// keep).  Other blocks (a subnormal input, an extreme or non-finite scale)
+// take IEEE divisions.
 template <int RULE>
 __device__ __forceinline__ void quantize_one(u32x4 w0, u32x4 w1, float g, u32x2 *codes,
                                              uint32_t *scale) {
     const uint32_t w[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
-    // smallest nonzero magnitude pattern (bf16 bits - 1, zero wraps to the top)
-    uint32_t tiny = 0xFFFFFFFFu;
+    // largest magnitude pattern and smallest nonzero one (pattern - 1, zero
+    // wraps to the top), two bf16 values per 16-bit lane pair
+    u16x2 mx = {0, 0}, mn = {0xFFFF, 0xFFFF};
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-        const uint32_t lo = (w[i] & 0x7FFFu) - 1u, hi = ((w[i] >> 16) & 0x7FFFu) - 1u;
-        tiny = lo < tiny ? lo : tiny;
-        tiny = hi < tiny ? hi : tiny;
+        const u16x2 m = __builtin_bit_cast(u16x2, w[i] & 0x7FFF7FFFu);
+        mx = __builtin_elementwise_max(mx, m);
+        mn = __builtin_elementwise_min(mn, static_cast<u16x2>(m - u16x2{1, 1}));
     }
+    const uint32_t maxp = mx.x > mx.y ? mx.x : mx.y;
+    const uint32_t tiny = mn.x < mn.y ? mn.x : mn.y;
     const bool fast = g >= 0x1p-40f && g <= 0x1p30f && tiny >= (27u << 7) - 1u;   // 2^-100
 
     float xn[16];
+    float am;
     if (fast) {
-        const float yg = 1.0f / g;
+        const double yg = 1.0 / static_cast<double>(g);
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            xn[2 * i] = div_rn(bf16_to_f32(w[i] & 0xFFFFu), g, yg);
-            xn[2 * i + 1] = div_rn(bf16_to_f32(w[i] >> 16), g, yg);
+            xn[2 * i] = quot_f64(bf16_to_f32(w[i] & 0xFFFFu), yg);
+            xn[2 * i + 1] = quot_f64(__uint_as_float(w[i] & 0xFFFF0000u), yg);
         }
+        am = quot_f64(bf16_to_f32(maxp), yg);
     } else {
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             xn[2 * i] = bf16_to_f32(w[i] & 0xFFFFu) / g;
-            xn[2 * i + 1] = bf16_to_f32(w[i] >> 16) / g;
+            xn[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u) / g;
         }
+        am = bf16_to_f32(maxp) / __builtin_fabsf(g);
     }
-    // max |xn| on the bit patterns: NaN patterns sort above +Inf, so a NaN wins
-    uint32_t amb = 0u;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        const uint32_t a = __float_as_uint(xn[i]) & 0x7FFFFFFFu;
-        amb = a > amb ? a : amb;
-    }
-    float am = __uint_as_float(amb);
     am = am < 1e-8f ? 1e-8f : am;                  // NaN stays NaN
-    const uint32_t s = e4m3_code_pos(am / 6.0f);
+    // am / 6 with am >= 1e-8: quot_f64 is exact (6 has 2 significant bits)
+    const uint32_t s = e4m3_code_pos(quot_f64(am, 1.0 / 6.0));
     const float sv = e4m3_value_pos(s);
     const float den = sv < 1e-8f ? 1e-8f : sv;     // NaN stays NaN
 
     float v[16];
-    if (fast) {
-        const float yd = 1.0f / den;
+    if (fast && s != 0u) {   // s == 0: den is the 1e-8 floor, not a 4-bit number
+        const float yd = __builtin_amdgcn_rcpf(den);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) v[i] = div_rn(xn[i], den, yd);
+        for (int i = 0; i < 16; ++i) v[i] = quot_short(xn[i], den, yd);
     } else {
 #pragma unroll
         for (int i = 0; i < 16; ++i) v[i] = xn[i] / den + 0.0f;   // -0 -> +0: its code is 0
@@ -231,29 +203,58 @@ __device__ __forceinline__ void quantize_one(u32x4 w0, u32x4 w1, float g, u32x2 
 }
 
 // One lane quantises one 16-element block; blocks are numbered across rows
-// (block b is block b % bpr of row b / bpr).  `x` 16-byte aligned, `q` 8-byte
-// aligned; gs_stride 0 (one scale) or 1 (one scale per row).  Lanes below
-// `rows` also write alpha[row] = f32(other[row] * gs[row]) (or gs[row] when
-// `other` is NULL) when `alpha` is not NULL.
+// (block b is block b % bpr of row b / bpr).  A wave's 64 blocks are 2 KiB of
+// x: each lane loads 16 bytes of each 1 KiB half (every load instruction
+// reads 1 KiB contiguously), the wave stages them in LDS and every lane reads
+// back the 32 bytes of its block.  `x` 16-byte aligned, `q` 8-byte aligned;
+// gs_stride 0 (one scale) or 1 (one scale per row).  Lanes below `rows` also
+// write alpha[row] = f32(other[row] * gs[row]) (or gs[row] when `other` is
+// NULL) when `alpha` is not NULL.
 template <int RULE>
 __global__ __launch_bounds__(kQuantThreads) void quantize_blocks(
     const uint16_t *__restrict__ x, const float *__restrict__ gs, int64_t gs_stride,
     uint8_t *__restrict__ q, uint8_t *__restrict__ sf, int64_t nblocks, int64_t bpr,
     const float *__restrict__ other, float *__restrict__ alpha, int64_t rows) {
+    __shared__ u32x4 stage[2 * kQuantThreads];
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int64_t b = static_cast<int64_t>(blockIdx.x) * kQuantThreads + threadIdx.x;
     if (alpha != nullptr && b < rows) {
         const float g = gs[b * gs_stride];
         alpha[b] = other != nullptr ? other[b] * g : g;
     }
-    if (b >= nblocks) return;
-    const u32x4 *src = reinterpret_cast<const u32x4 *>(x) + 2 * b;
-    const u32x4 w0 = __builtin_nontemporal_load(src);
-    const u32x4 w1 = __builtin_nontemporal_load(src + 1);
+    const int64_t b0 = static_cast<int64_t>(blockIdx.x) * kQuantThreads + wave * kWave;   // the wave's first block
+    if (b0 >= nblocks) return;                     // wave-uniform
+    const int nvalid = static_cast<int>(nblocks - b0 < kWave ? nblocks - b0 : kWave);
     // block numbers stay below 2^31 (checked on the host): a 32-bit division
-    const uint32_t row = static_cast<uint32_t>(b) / static_cast<uint32_t>(bpr);
+    const int64_t bb = b < nblocks ? b : nblocks - 1;
+    const uint32_t row = static_cast<uint32_t>(bb) / static_cast<uint32_t>(bpr);
+    // the wave's blocks (loads past the last block read zeros), then the
+    // block's global scale, all in flight together
+    const __amdgpu_buffer_rsrc_t xr = nvfp4dev::buffer_of(
+        reinterpret_cast<const uint8_t *>(x + b0 * 16), nvalid * 32);
+    nvfp4dev::phase_fence();
+    const u32x4 h0 = __builtin_bit_cast(
+        u32x4, __builtin_amdgcn_raw_buffer_load_b128(xr, 16 * lane, 0, nvfp4dev::kNonTemporal));
+    const u32x4 h1 = __builtin_bit_cast(
+        u32x4, __builtin_amdgcn_raw_buffer_load_b128(xr, 1024 + 16 * lane, 0, nvfp4dev::kNonTemporal));
+    const float g = gs[row * gs_stride];
+    nvfp4dev::phase_fence();
+    __asm__ volatile("" ::"v"(g));                 // keeps the load here, not after the staging
+    u32x4 *st = stage + 2 * kWave * wave;          // the wave's 2 KiB
+    st[lane] = h0;
+    st[kWave + lane] = h1;
+    // LDS operations of one wave complete in order; the fences keep the
+    // compiler from moving the reads above the other lanes' writes.
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const u32x4 w0 = st[2 * lane];
+    const u32x4 w1 = st[2 * lane + 1];
+    if (b >= nblocks) return;
     u32x2 codes;
     uint32_t s;
-    quantize_one<RULE>(w0, w1, gs[row * gs_stride], &codes, &s);
+    quantize_one<RULE>(w0, w1, g, &codes, &s);
     *reinterpret_cast<u32x2 *>(q + b * 8) = codes;
     sf[b] = static_cast<uint8_t>(s);
 }

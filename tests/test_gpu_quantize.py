@@ -100,6 +100,41 @@ def test_every_bf16_pattern(rule):
     check_quant(bits[:, rng.permutation(4096)], np.float32(0.75), rule, "all patterns, shuffled")
 
 
+
+# Every E2M1 cut point of the three rules (grid midpoints and the half-step
+# table's cuts).
+CUTS = [0.25, 0.75, 1.25, 1.75, 2.25, 2.5, 2.75, 3.25, 3.5, 3.75, 4.25, 4.5, 4.75, 5.0, 5.25,
+        5.75, 6.0]
+
+
+def near_cut_blocks(g, den):
+    """Blocks whose largest element makes the block scale `den` (6 * den * g),
+    the other 15 the bf16 neighbours (below, nearest, above, negated) of
+    cut * den * g, so x/g/den lands on or next to the cut points."""
+    cand = []
+    for t in CUTS:
+        v = np.float32(t * den * g)
+        b = int(np.array([v], dtype=np.float32).view(np.uint32)[0] >> 16)
+        for nb in (b - 1, b, b + 1):
+            cand += [nb, nb | 0x8000]
+    top = int(np.array([np.float32(6.0 * den * g)], dtype=np.float32).view(np.uint32)[0] >> 16)
+    blocks = []
+    for i in range(0, len(cand), 15):
+        chunk = cand[i:i + 15]
+        chunk += [0] * (15 - len(chunk))
+        blocks.append([top] + chunk)
+    return np.array(blocks, dtype=np.uint32).astype(np.uint16).reshape(1, -1)
+
+
+@pytest.mark.parametrize("rule", RULES)
+def test_values_on_and_next_to_every_cut(rule):
+    """Ties and their neighbours after both divisions, for global scales that
+    are and are not powers of two and block scales across E4M3's range
+    (normal, subnormal), so each rounding rule's tie handling is exercised."""
+    for g in (1.0, 0.0037, 1.3, 7.77e-3, 2.0 ** -20, 123.0):
+        for den in (1.0, 0.875, 1.25, 0.0625, 3.0 * 2.0 ** -9, 448.0, 0.6875):
+            check_quant(near_cut_blocks(g, den), np.float32(g), rule, f"g={g} den={den}")
+
 def test_negative_subnormals_keep_their_sign():
     """bf16 subnormals stay subnormal in fp32; a flush to zero would turn
     their negative codes (8 + index) into code 0."""
