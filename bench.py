@@ -81,6 +81,9 @@ def parse_args(argv=None):
     p.add_argument("--ksplit", type=int, default=0, help="K split (0 = default plan)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-probe", action="store_true")
+    p.add_argument("--single-launches", type=int, default=50,
+                   help="GEMV: single launches, each after a 512 MiB scratch write, for per-launch "
+                        "latency percentiles (0 = skip)")
     p.add_argument("--copy-mib", type=int, default=0,
                    help="after timing, run 4 plain device copies of this many MiB (the "
                         "known-size reference for HBM byte counters)")
@@ -104,6 +107,32 @@ def recorded_traffic(config: str, kernel: str = "gemv_fast"):
     if not h or not t or h.group(1) != kernel_source_hash(kernel):
         return None
     return float(t.group(1))
+
+
+def single_launch_percentiles(torch, stream, step, n):
+    """p10/p50/p90 of single launches (HIP events on the launch stream around one
+    step), each after a 512 MiB write that evicts the operands from L2 and the
+    Infinity Cache, so each launch starts cold and alone."""
+    if n <= 0:
+        return None
+    scratch = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    times = []
+    for i in range(n):
+        scratch.fill_(i & 0xFF)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        step(i)
+        e1.record(stream)
+        e1.synchronize()
+        times.append(e0.elapsed_time(e1) * 1e3)
+    del scratch
+    times.sort()
+
+    def pct(q):
+        return round(times[min(len(times) - 1, int(q * (len(times) - 1) + 0.5))], 2)
+
+    return {"p10": pct(0.1), "p50": pct(0.5), "p90": pct(0.9), "launches": n}
 
 
 class Timer:
@@ -220,6 +249,11 @@ def bench_gemv(args, torch, np, pd, workloads):
     warm_gbs = nbytes / (warm_ms / nw * 1e-3) / 1e9
     print(f"[bench] cache-resident (same buffers every step): {warm_gbs:.1f} GB/s", flush=True)
 
+    single = single_launch_percentiles(torch, stream, step, args.single_launches)
+    if single:
+        print(f"[bench] single launches after a 512 MiB scratch write: p10 {single['p10']} us, "
+              f"p50 {single['p50']} us, p90 {single['p90']} us", flush=True)
+
     probe_gbs = probe_ws_gbs = None
     if not args.no_probe:
         pbytes = 1 << 30
@@ -268,6 +302,7 @@ def bench_gemv(args, torch, np, pd, workloads):
                      "plan": {"path": plan.path, "variant": plan.variant, "ksplit": plan.ksplit}}
     out["roofline"] = roofline(gbs, recorded_traffic(cfg.name), probe_read_gbs=probe_gbs,
                                probe_read_same_size_gbs=probe_ws_gbs, cache_resident_gbs=warm_gbs)
+    out["single_launch_us"] = single
     out["cpu_baseline"] = cpu
     return out
 

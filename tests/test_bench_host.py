@@ -1,0 +1,91 @@
+"""Host-side logic of bench.py (no GPU): argument defaults, the one-GPU rule,
+the roofline fields and the lookup of recorded HBM traffic."""
+import os
+
+import pytest
+
+import bench
+
+
+def test_defaults_time_the_decode_gemv():
+    a = bench.parse_args([])
+    assert a.gpus == 1 and a.path == "gemv" and a.config == "decode"
+    assert a.steps > 0 and a.warmup > 0 and a.single_launches > 0
+
+
+def test_more_than_one_gpu_exits_with_a_message(capsys):
+    assert bench.main(["--gpus", "2"]) == 2
+    assert "one GPU" in capsys.readouterr().err
+
+
+def test_world_size_above_one_exits(monkeypatch):
+    monkeypatch.setenv("WORLD_SIZE", "4")
+    assert bench.main([]) == 2
+
+
+def test_roofline_fields():
+    r = bench.roofline(6000.0, 123.0, probe_read_gbs=5000.123)
+    assert r["bound"] == "hbm" and r["peak"] == bench.HBM_PEAK_GBS and r["unit"] == "GB/s"
+    assert r["frac"] == round(6000.0 / bench.HBM_PEAK_GBS, 4) and r["traffic"] == 123.0
+    assert r["probe_read_gbs"] == 5000.12
+
+
+def test_recorded_traffic_needs_the_current_source(tmp_path, monkeypatch):
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path))
+    assert bench.recorded_traffic("decode") is None                     # no file
+    h = bench.kernel_source_hash("gemv_fast")
+    f = tmp_path / "gemv_fast_decode_hbm_counters.txt"
+    f.write_text(f"kernel_source_sha256_16: {h}\nhbm_bytes_per_launch: 66291018\n")
+    assert bench.recorded_traffic("decode") == 66291018.0
+    f.write_text("kernel_source_sha256_16: 0000000000000000\nhbm_bytes_per_launch: 1\n")
+    assert bench.recorded_traffic("decode") is None                     # stale kernel source
+
+
+def test_committed_profiles_name_their_source_hash():
+    for name in os.listdir(bench.PROFILES):
+        if name.endswith("_hbm_counters.txt"):
+            text = open(os.path.join(bench.PROFILES, name)).read()
+            assert "kernel_source_sha256_16:" in text and "hbm_bytes_per_launch:" in text, name
+
+
+def test_single_launch_percentiles_skip_when_zero():
+    assert bench.single_launch_percentiles(None, None, None, 0) is None
+
+
+@pytest.mark.parametrize("n", [1, 7, 50])
+def test_single_launch_percentiles_order(n, monkeypatch):
+    """The percentile picking on a fake clock: p10 <= p50 <= p90, all from the samples."""
+
+    class FakeEvent:
+        t = 0.0
+
+        def __init__(self, enable_timing=True):
+            self.at = None
+
+        def record(self, stream):
+            FakeEvent.t += 0.001 * (1 + (FakeEvent.t * 7919) % 3)
+            self.at = FakeEvent.t
+
+        def synchronize(self):
+            pass
+
+        def elapsed_time(self, other):
+            return other.at - self.at
+
+    class FakeTensor:
+        def fill_(self, v):
+            return self
+
+    class FakeCuda:
+        Event = FakeEvent
+
+    class FakeTorch:
+        cuda = FakeCuda
+        uint8 = "u8"
+
+        @staticmethod
+        def empty(*a, **k):
+            return FakeTensor()
+
+    r = bench.single_launch_percentiles(FakeTorch, None, lambda i: None, n)
+    assert r["launches"] == n and r["p10"] <= r["p50"] <= r["p90"]
