@@ -206,3 +206,42 @@ def test_bf16x_gemv_against_oracle(name, rule):
     assert np.array_equal(alpha.view(np.uint32), want_alpha.view(np.uint32))
     assert_within_tolerance(c, want_c, what=name)
     print(f"{name}: {float(np.mean(c == want_c)):.6f} of outputs bit-identical to the oracle")
+
+
+@pytest.mark.parametrize("l,m,k", [(2, 300, 20480), (3, 77, 2080), (1, 9, 64), (5, 130, 16384)])
+@pytest.mark.parametrize("rule", RULES)
+def test_bf16x_fused_shapes(l, m, k, rule):
+    """The one-kernel path (activation quantised inside the GEMV): ragged rows,
+    K split across workgroups (k > 16384), K shorter than one iteration; every
+    workgroup quantises the activation itself and row block 0 writes it out."""
+    ops = workloads.integer_coded(l, m, k, seed=l * 1000 + m + k + rule)
+    xv = workloads.gaussian_bf16(l, 1, k, seed=k + rule)["x"]
+    x_scale = (np.abs(xv).max(axis=1) / np.float32(2688.0)).astype(np.float32)
+    A_scale = np.linspace(0.5, 2.0, l).astype(np.float32)
+    want_c, want_q, want_sf, want_alpha = oq.activation_gemv(ops["A"], ops["sfA"], A_scale, xv,
+                                                             x_scale, rule, l, m, k)
+    d = to_device({"A": ops["A"], "sfA": ops["sfA"]})
+    c, xq, sfx, alpha = run_bf16x(d["A"], d["sfA"], A_scale, bf16_bits(xv), x_scale, rule, l, m, k)
+    assert np.array_equal(sfx, want_sf) and np.array_equal(xq, want_q)
+    assert np.array_equal(alpha.view(np.uint32), want_alpha.view(np.uint32))
+    assert_within_tolerance(c, want_c, what=f"{(l, m, k)} rule {rule}")
+
+
+def test_bf16x_misaligned_weights_take_two_kernels():
+    """A weight pointer off the fast kernel's alignment: the quantiser and the
+    generic GEMV run instead, with the same results."""
+    l, m, k = 2, 40, 512
+    ops = workloads.integer_coded(l, m, k, seed=77)
+    xv = workloads.gaussian_bf16(l, 1, k, seed=78)["x"]
+    x_scale = (np.abs(xv).max(axis=1) / np.float32(2688.0)).astype(np.float32)
+    rule = pd.NVFP4_ROUND_NEAREST_EVEN
+    want_c, want_q, want_sf, want_alpha = oq.activation_gemv(ops["A"], ops["sfA"], None, xv,
+                                                             x_scale, rule, l, m, k)
+    buf = torch.zeros(ops["A"].size + 8, dtype=torch.uint8, device="cuda")
+    dA = buf[8:]                                   # 8-byte aligned, not 16
+    dA.copy_(torch.from_numpy(ops["A"].reshape(-1)).cuda())
+    dsf = torch.from_numpy(ops["sfA"].reshape(-1).copy()).cuda()
+    c, xq, sfx, alpha = run_bf16x(dA, dsf, None, bf16_bits(xv), x_scale, rule, l, m, k)
+    assert np.array_equal(sfx, want_sf) and np.array_equal(xq, want_q)
+    assert np.array_equal(alpha.view(np.uint32), want_alpha.view(np.uint32))
+    assert_within_tolerance(c, want_c, what="misaligned weights")
