@@ -67,6 +67,30 @@ int nvfp4_quantize_activation(const uint16_t *x_bf16, const float *global_scale,
                               int64_t rows, int64_t d, int32_t rule, void *stream);
 
 /*
+ * Offline weight quantiser: the bridge page's weight quantiser (section
+ * "Quantization") on the device, for `groups` tensors of [rows][d] each
+ * (e.g. the experts of a MoE layer; groups = 1 for one matrix), stored one
+ * after the other in w_bf16 [groups][rows][d].  Each tensor's global scale is
+ * computed from its own amax:
+ *
+ *   global_scale[e] = f32( max(max |T_e|, 1e-8) / (6 * 448) )   (NaN propagates)
+ *
+ * and the tensor is then quantised with it as nvfp4_quantize_activation does,
+ * under `rule` (the page's weight quantiser is NVFP4_ROUND_NEAREST_LOWER):
+ * w_packed [groups][rows][d/2], sf [groups][rows][d/16].  global_scale
+ * [groups] (float, 4-byte aligned, device) is an output: the weights' global
+ * scales for the GEMV's alpha.  Three kernels are enqueued on `stream`; their
+ * scratch (groups * 256 bytes + 4 bytes per row) is the library-owned
+ * per-(device, stream) workspace of nvfp4_gemv_launch, allocated on first need.
+ * Shape and alignment rules as for nvfp4_quantize_activation over groups*rows
+ * rows.  Returns NVFP4_GEMV_OK, NULL_POINTER, BAD_ARGUMENT, BAD_SHAPE,
+ * ALIGNMENT, ALIAS, DEVICE, WORKSPACE or LAUNCH.
+ */
+int nvfp4_quantize_weight(const uint16_t *w_bf16, int64_t groups, int64_t rows, int64_t d,
+                          int32_t rule, uint8_t *w_packed, uint8_t *sf, float *global_scale,
+                          void *stream);
+
+/*
  * The batched GEMV of nvfp4_gemv.h with a bf16 activation: quantises x_bf16
  * [l][k] with one global scale per batch (x_scale [l]) into x_packed [l][k/2]
  * and sfx [l][k/16], writes alpha[b] = f32(A_scale[b] * x_scale[b]) (A_scale

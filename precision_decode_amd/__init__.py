@@ -52,5 +52,6 @@ from ._binding import (  # noqa: F401
     nvfp4_mma_num_variants,
     nvfp4_mma_variant_info,
     nvfp4_quantize_activation,
+    nvfp4_quantize_weight,
     quantize_activation,
 )

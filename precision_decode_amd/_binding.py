@@ -49,6 +49,7 @@ EXPORTED = (
     "nvfp4_gemv_launch_tuned",
     "nvfp4_hbm_read_probe",
     "nvfp4_quantize_activation",
+    "nvfp4_quantize_weight",
     "nvfp4_gemv_bf16x_launch",
     "nvfp4_gemm_smalln_launch",
     "nvfp4_mma_num_variants",
@@ -121,6 +122,8 @@ def load():
     lib.nvfp4_quantize_activation.restype = ctypes.c_int
     lib.nvfp4_quantize_activation.argtypes = [_P, _P, ctypes.c_int32, _P, _P, _I64, _I64,
                                               ctypes.c_int32, _P]
+    lib.nvfp4_quantize_weight.restype = ctypes.c_int
+    lib.nvfp4_quantize_weight.argtypes = [_P, _I64, _I64, _I64, ctypes.c_int32, _P, _P, _P, _P]
     lib.nvfp4_gemv_bf16x_launch.restype = ctypes.c_int
     lib.nvfp4_gemv_bf16x_launch.argtypes = [_P, _P, _P, _P, _P, ctypes.c_int32, _P, _P, _P, _P,
                                             _I64, _I64, _I64, _P]
@@ -251,6 +254,12 @@ def nvfp4_quantize_activation(x_bf16, global_scale, scale_per_row, x_packed, sf,
     _check(load().nvfp4_quantize_activation(_ptr(x_bf16), _ptr(global_scale), int(scale_per_row),
                                             _ptr(x_packed), _ptr(sf), rows, d, int(rule),
                                             _stream(stream)), "nvfp4_quantize_activation")
+
+
+def nvfp4_quantize_weight(w_bf16, groups, rows, d, rule, w_packed, sf, global_scale, stream=None):
+    _check(load().nvfp4_quantize_weight(_ptr(w_bf16), groups, rows, d, int(rule), _ptr(w_packed),
+                                        _ptr(sf), _ptr(global_scale), _stream(stream)),
+           "nvfp4_quantize_weight")
 
 
 def nvfp4_gemv_bf16x_launch(A_packed, sfA, A_scale, x_bf16, x_scale, rule, x_packed, sfx, alpha, c,

@@ -259,6 +259,72 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_blocks(
     sf[b] = static_cast<uint8_t>(s);
 }
 
+// ---------------------------------------------------------------- tensor amax
+// Global scale of each of `groups` tensors of `per_group` bf16 elements, as
+// the bridge page's weight quantiser computes it (section "Quantization"):
+// g = max(max |T|, 1e-8) / (6 * 448) in fp32.  Pass 1: workgroup j of group
+// e reads every kAmaxGroups-th 16-byte chunk of the group's tensor and
+// writes the largest bf16 magnitude pattern it saw (NaN patterns sort above
+// +Inf, so a NaN wins) to part[e][j].  Pass 2: one workgroup per group
+// reduces the partials, writes g[e], and g[e] for each of the group's rows
+// into the per-row scale array that the quantiser then reads.
+constexpr int kAmaxThreads = 256;
+constexpr int kAmaxGroups = 64;        // pass-1 workgroups per tensor
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+    for (int o = kWave / 2; o >= 1; o >>= 1) {
+        const uint32_t t = static_cast<uint32_t>(__shfl_xor(static_cast<int>(v), o, kWave));
+        v = t > v ? t : v;
+    }
+    return v;
+}
+
+__global__ __launch_bounds__(kAmaxThreads) void amax_partial(const uint16_t *__restrict__ x,
+                                                             int64_t per_group,
+                                                             uint32_t *__restrict__ part) {
+    __shared__ uint32_t wmax[kAmaxThreads / kWave];
+    const int64_t e = blockIdx.x / kAmaxGroups;
+    const int64_t j = blockIdx.x % kAmaxGroups;
+    const u32x4 *src = reinterpret_cast<const u32x4 *>(x + e * per_group);
+    const int64_t nchunks = per_group / 8;   // 16-byte chunks (per_group % 16 == 0)
+    u16x2 mx = {0, 0};
+    for (int64_t i = j * kAmaxThreads + threadIdx.x; i < nchunks; i += kAmaxGroups * kAmaxThreads) {
+        const u32x4 w = __builtin_nontemporal_load(src + i);
+        const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+            mx = __builtin_elementwise_max(mx, __builtin_bit_cast(u16x2, wd[t] & 0x7FFF7FFFu));
+    }
+    uint32_t m = mx.x > mx.y ? mx.x : mx.y;
+    m = wave_max_u32(m);
+    if ((threadIdx.x & (kWave - 1)) == 0) wmax[threadIdx.x / kWave] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t all = 0u;
+        for (int w = 0; w < kAmaxThreads / kWave; ++w) all = wmax[w] > all ? wmax[w] : all;
+        part[e * kAmaxGroups + j] = all;
+    }
+}
+
+__global__ __launch_bounds__(kWave) void amax_finalize(const uint32_t *__restrict__ part,
+                                                       int64_t rows_per_group,
+                                                       float *__restrict__ g_out,
+                                                       float *__restrict__ row_scale) {
+    const int64_t e = blockIdx.x;
+    uint32_t m = 0u;
+    for (int j = threadIdx.x; j < kAmaxGroups; j += kWave) {
+        const uint32_t v = part[e * kAmaxGroups + j];
+        m = v > m ? v : m;
+    }
+    m = wave_max_u32(m);
+    float amax = __uint_as_float(m << 16);
+    amax = amax < 1e-8f ? 1e-8f : amax;          // NaN stays NaN
+    const float g = amax / 2688.0f;              // 6 * 448, one fp32 division
+    if (threadIdx.x == 0) g_out[e] = g;
+    for (int64_t r = threadIdx.x; r < rows_per_group; r += kWave) row_scale[e * rows_per_group + r] = g;
+}
+
 typedef void (*QuantKernel)(const uint16_t *, const float *, int64_t, uint8_t *, uint8_t *,
                             int64_t, int64_t, const float *, float *, int64_t);
 
@@ -358,6 +424,48 @@ int nvfp4_gemv_bf16x_launch(const uint8_t *A_packed, const uint8_t *sfA, const f
     s = launch_quant(x_bf16, x_scale, 1, x_packed, sfx, l, k, rule, A_scale, alpha, st);
     if (s != NVFP4_GEMV_OK) return s;
     return nvfp4_gemv_launch(A_packed, sfA, x_packed, sfx, alpha, c, l, m, k, stream);
+}
+
+int nvfp4_quantize_weight(const uint16_t *w_bf16, int64_t groups, int64_t rows, int64_t d,
+                          int32_t rule, uint8_t *w_packed, uint8_t *sf, float *global_scale,
+                          void *stream) {
+    if (!global_scale) return NVFP4_GEMV_ERR_NULL_POINTER;
+    if (groups < 1 || rows < 1 || groups > kMaxBlocks / rows) return NVFP4_GEMV_ERR_BAD_SHAPE;
+    const int64_t total_rows = groups * rows;
+    // shape, rule, alignment of x / packed output and the aliasing of the
+    // outputs with the input are the quantiser's rules over all rows
+    int s = check_quant(w_bf16, global_scale, 0, w_packed, sf, total_rows, d, rule);
+    if (s != NVFP4_GEMV_OK) return s;
+    if (misaligned(global_scale, 4)) return NVFP4_GEMV_ERR_ALIGNMENT;
+    const size_t n = static_cast<size_t>(total_rows) * static_cast<size_t>(d);
+    const size_t gn = static_cast<size_t>(groups) * 4;
+    if (overlaps(global_scale, gn, w_bf16, n * 2) || overlaps(global_scale, gn, w_packed, n / 2) ||
+        overlaps(global_scale, gn, sf, n / 16))
+        return NVFP4_GEMV_ERR_ALIAS;
+    if (groups > (int64_t(1) << 31) / kAmaxGroups) return NVFP4_GEMV_ERR_BAD_SHAPE;
+    // workspace: the pass-1 partials, then one fp32 scale per row
+    const size_t part_bytes = static_cast<size_t>(groups) * kAmaxGroups * sizeof(uint32_t);
+    const size_t ws_bytes = part_bytes + static_cast<size_t>(total_rows) * sizeof(float);
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return NVFP4_GEMV_ERR_DEVICE;
+    uint8_t *ws = static_cast<uint8_t *>(nvfp4_stream_workspace(dev, stream, ws_bytes));
+    if (!ws) return NVFP4_GEMV_ERR_WORKSPACE;
+    uint32_t *part = reinterpret_cast<uint32_t *>(ws);
+    float *row_scale = reinterpret_cast<float *>(ws + part_bytes);
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    int64_t per_group = rows * d;
+    void *a1[] = {&w_bf16, &per_group, &part};
+    hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(amax_partial),
+                                   dim3(static_cast<uint32_t>(groups * kAmaxGroups)),
+                                   dim3(kAmaxThreads), a1, 0, st);
+    if (e != hipSuccess) return NVFP4_GEMV_ERR_LAUNCH;
+    const uint32_t *cpart = part;
+    int64_t rpg = rows;
+    void *a2[] = {&cpart, &rpg, &global_scale, &row_scale};
+    e = hipLaunchKernel(reinterpret_cast<const void *>(amax_finalize),
+                        dim3(static_cast<uint32_t>(groups)), dim3(kWave), a2, 0, st);
+    if (e != hipSuccess) return NVFP4_GEMV_ERR_LAUNCH;
+    return launch_quant(w_bf16, row_scale, 1, w_packed, sf, total_rows, d, rule, nullptr, nullptr, st);
 }
 
 }  // extern "C"

@@ -220,6 +220,28 @@ def test_quantize_validation(lib):
     assert qcall(sf=Q + 63) == pd.NVFP4_GEMV_ERR_ALIAS          # q holds 64 bytes
 
 
+
+def wcall(groups=2, rows=2, d=64, x=XB, rule=2, q=Q, sf=SF, g=GS):
+    return pd.load().nvfp4_quantize_weight(x, groups, rows, d, rule, q, sf, g, None)
+
+
+def test_weight_quantize_validation(lib):
+    """Every rejection happens before any HIP call (this machine has no GPU)."""
+    for kw in ("x", "q", "sf", "g"):
+        assert wcall(**{kw: None}) == pd.NVFP4_GEMV_ERR_NULL_POINTER, kw
+    for rule in (-1, 3):
+        assert wcall(rule=rule) == pd.NVFP4_GEMV_ERR_BAD_ARGUMENT
+    for groups, rows, d in ((0, 2, 64), (2, 0, 64), (2, 2, 8), (2, 2, 40), (-3, 2, 64),
+                            (1 << 20, 1 << 12, 1 << 8)):
+        assert wcall(groups=groups, rows=rows, d=d) == pd.NVFP4_GEMV_ERR_BAD_SHAPE, (groups, rows, d)
+    assert wcall(x=XB + 8) == pd.NVFP4_GEMV_ERR_ALIGNMENT
+    assert wcall(q=Q + 4) == pd.NVFP4_GEMV_ERR_ALIGNMENT
+    assert wcall(g=GS + 2) == pd.NVFP4_GEMV_ERR_ALIGNMENT
+    assert wcall(q=XB + 64) == pd.NVFP4_GEMV_ERR_ALIAS          # inside the 2*2*64 bf16 values
+    assert wcall(g=Q + 60) == pd.NVFP4_GEMV_ERR_ALIAS           # the packed output holds 128 bytes
+    assert wcall(g=SF + 12) == pd.NVFP4_GEMV_ERR_ALIAS          # sf holds 16 bytes
+    assert wcall(g=XB + 508) == pd.NVFP4_GEMV_ERR_ALIAS         # the scales overlap x's last bytes
+
 def bcall(l=2, m=8, k=64, a=A, sa=SA, asc=AL, x=XB, xs=GS, rule=0, q=Q, sf=SF, al=C + 4096, c=C):
     return pd.load().nvfp4_gemv_bf16x_launch(a, sa, asc, x, xs, rule, q, sf, al, c, l, m, k, None)
 

@@ -245,3 +245,45 @@ def test_bf16x_misaligned_weights_take_two_kernels():
     assert np.array_equal(sfx, want_sf) and np.array_equal(xq, want_q)
     assert np.array_equal(alpha.view(np.uint32), want_alpha.view(np.uint32))
     assert_within_tolerance(c, want_c, what="misaligned weights")
+
+
+def run_weight(bits, groups, rows, d, rule):
+    x = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16).reshape(-1).copy()).cuda()
+    q = torch.full((groups * rows, d // 2), 0xA5, dtype=torch.uint8, device="cuda")
+    sf = torch.full((groups * rows, d // 16), 0xA5, dtype=torch.uint8, device="cuda")
+    g = torch.full((groups,), -1.0, dtype=torch.float32, device="cuda")
+    pd.nvfp4_quantize_weight(x, groups, rows, d, rule, q, sf, g)
+    torch.cuda.synchronize()
+    return (q.cpu().numpy().reshape(groups, rows, d // 2), sf.cpu().numpy().reshape(groups, rows, d // 16),
+            g.cpu().numpy())
+
+
+def to_bf16_bits(vals):
+    """float32 -> bf16 bit patterns, round to nearest even (torch's cast)."""
+    t = torch.from_numpy(np.ascontiguousarray(vals, dtype=np.float32)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+@pytest.mark.parametrize("rule", RULES)
+@pytest.mark.parametrize("groups,rows,d", [(5, 37, 272), (8, 256, 2048), (1, 3, 16)])
+def test_weight_quantizer_against_oracle(rule, groups, rows, d):
+    """Per-tensor amax global scales computed on the device, then the codes:
+    bytes and scales bit-identical to the oracle's amax quantiser, tensor by
+    tensor; a tensor of zeros (amax floor 1e-8) and one holding a NaN (NaN
+    scale, every code 0) among them."""
+    rng = np.random.default_rng(groups * 100 + rows + d + rule)
+    mags = np.float32(10.0) ** rng.uniform(-3, 3, size=groups).astype(np.float32)
+    vals = (rng.standard_normal((groups, rows, d)).astype(np.float32) * mags[:, None, None])
+    if groups > 2:
+        vals[1] = 0.0
+        vals[2, rows // 2, d // 3] = np.nan
+    bits = to_bf16_bits(vals)
+    got_q, got_sf, got_g = run_weight(bits, groups, rows, d, rule)
+    for e in range(groups):
+        want_q, want_sf, want_g = oq.quantize_nvfp4(bits_to_f32(bits[e]), rule)
+        if np.isnan(want_g):
+            assert np.isnan(got_g[e]), e
+        else:
+            assert got_g[e].view(np.uint32) == np.float32(want_g).view(np.uint32), (e, got_g[e], want_g)
+        assert np.array_equal(got_sf[e], want_sf), f"tensor {e}: scale bytes differ"
+        assert np.array_equal(got_q[e], want_q), f"tensor {e}: code bytes differ"
