@@ -130,10 +130,11 @@ int nvfp4_gemv_num_variants(void);
  * 1 KiB K-iterations kept in flight per row, waves per workgroup, and how x
  * reaches the arithmetic: 0 = decoded to fp16 in LDS once per workgroup,
  * 1 = staged in LDS as packed codes, 2 = not staged (each wave loads x's
- * codes next to its rows of A every iteration), 3 = 16-row tiles: the
- * workgroup's waves share 16 rows and take turns over K slices of 2048
- * elements, each wave keeping x~ of its slice in registers (these variants
- * take k <= 2^26; BAD_TUNING above).  Returns a status.
+ * codes next to its rows of A every iteration), 3 = row tiles: the
+ * workgroup's waves share a tile of rows_per_wave rows (16, 8 or 4) and take
+ * turns over K slices of 2048 elements, each wave keeping x~ of its slice in
+ * registers (these variants take k <= 2^26; BAD_TUNING above).  Returns a
+ * status.
  */
 int nvfp4_gemv_variant_info(int v, int32_t *rows_per_wave, int32_t *iters_in_flight,
                             int32_t *waves_per_group, int32_t *x_staging);

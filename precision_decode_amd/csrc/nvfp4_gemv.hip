@@ -522,27 +522,28 @@ gemv_fastg(const uint8_t *__restrict__ A, const uint8_t *__restrict__ sfA,
 }
 
 // ---------------------------------------------------------------- row-tile kernel
-// A workgroup owns a tile of 16 rows of one batch and the K-range of its
-// split; its W waves share the tile and take K slices of 2048 elements
-// (1 KiB of every row) in turn: wave w takes slices w, w + W, ...  For one
-// slice a wave issues, back to back, x's 16 bytes and scale pair per lane
-// and then one 16-byte load per lane for each of the 16 rows (1 KiB of a row
-// per instruction) with the row's scale pair, so 16 KiB of A per wave are
-// in flight at once and every load is row-contiguous.  x~ of the lane's 32
-// elements is decoded once into registers and serves all 16 rows; no LDS
+// A workgroup owns a tile of TR rows (16, 8 or 4) of one batch and the
+// K-range of its split; its W waves share the tile and take K slices of 2048
+// elements (1 KiB of every row) in turn: wave w takes slices w, w + W, ...
+// For one slice a wave issues, back to back, x's 16 bytes and scale pair per
+// lane and then one 16-byte load per lane for each of the TR rows (1 KiB of
+// a row per instruction) with the row's scale pair, so TR KiB of A per wave
+// are in flight at once and every load is row-contiguous.  x~ of the lane's
+// 32 elements is decoded once into registers and serves all TR rows; no LDS
 // holds x, and nothing waits at a barrier before the arithmetic.  A row is
-// consumed as soon as its load lands, in issue order.
+// consumed as soon as its load lands, in issue order.  Fewer rows per tile
+// mean more waves for the same rows and less arithmetic left per wave when
+// its last load lands.
 //
-// Reduction: the 16 per-lane partial sums are halved twice by swapping the
+// Reduction: the TR per-lane partial sums are halved twice by swapping the
 // 32-lane halves and then the 16-lane rows of the wave (each lane keeps the
 // rows its half or row is responsible for and adds its partner's values),
-// then summed inside each 16-lane row by DPP.  The waves' row sums meet in
-// LDS and wave 0 adds them in wave order, so the result does not depend on
-// timing.
-constexpr int kTileRows = 16;
+// then the TR/4 values left are summed inside each 16-lane row by DPP.  The
+// waves' row sums meet in LDS and wave 0 adds them in wave order, so the
+// result does not depend on timing.
 constexpr int kTileMaxWaves = 8;
 
-template <int W>
+template <int W, int TR>
 __global__ void __launch_bounds__(W * kWave)
 gemv_tile(const uint8_t *__restrict__ A, const uint8_t *__restrict__ sfA,
           const uint8_t *__restrict__ x, const uint8_t *__restrict__ sfx,
@@ -550,7 +551,8 @@ gemv_tile(const uint8_t *__restrict__ A, const uint8_t *__restrict__ sfA,
           float *__restrict__ part, int64_t l, int64_t m, int64_t k,
           int64_t kchunk, int64_t row_blocks) {
     static_assert(W >= 1 && W <= kTileMaxWaves, "waves per tile");
-    __shared__ float red[W * kTileRows];
+    static_assert(TR == 16 || TR == 8 || TR == 4, "rows per tile");
+    __shared__ float red[W * TR];
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
 
@@ -560,8 +562,8 @@ gemv_tile(const uint8_t *__restrict__ A, const uint8_t *__restrict__ sfA,
     const int64_t kb0 = split * kchunk;
     const int klen = static_cast<int>((k - kb0 < kchunk) ? (k - kb0) : kchunk);
     const int nsl = (klen + static_cast<int>(kIterElems) - 1) / static_cast<int>(kIterElems);
-    const int64_t row0 = rb * kTileRows;
-    const int nrows = static_cast<int>((m - row0 < kTileRows) ? (m - row0) : kTileRows);
+    const int64_t row0 = rb * TR;
+    const int nrows = static_cast<int>((m - row0 < TR) ? (m - row0) : TR);
     const int half = static_cast<int>(k / 2), sixteenth = static_cast<int>(k / 16);
 
     // One descriptor per operand over the tile's rows, from the split's first
@@ -574,9 +576,9 @@ gemv_tile(const uint8_t *__restrict__ A, const uint8_t *__restrict__ sfA,
     const __amdgpu_buffer_rsrc_t xbuf = buffer_of(x + b * half + kb0 / 2, klen / 2);
     const __amdgpu_buffer_rsrc_t sxbuf = buffer_of(sfx + b * sixteenth + kb0 / 16, klen / 16);
 
-    float acc[kTileRows];
+    float acc[TR];
 #pragma unroll
-    for (int r = 0; r < kTileRows; ++r) acc[r] = 0.0f;
+    for (int r = 0; r < TR; ++r) acc[r] = 0.0f;
 
     for (int s = wave; s < nsl; s += W) {
         const int e0 = s * static_cast<int>(kIterElems) + 32 * lane;   // lane's first element
@@ -587,10 +589,10 @@ gemv_tile(const uint8_t *__restrict__ A, const uint8_t *__restrict__ sfA,
         phase_fence();
         const u32x4 xv = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xbuf, xo, 0, 0));
         const uint16_t xs2 = __builtin_amdgcn_raw_buffer_load_b16(sxbuf, e0 / 16, 0, 0);
-        u32x4 av[kTileRows];
-        uint16_t sv[kTileRows];
+        u32x4 av[TR];
+        uint16_t sv[TR];
 #pragma unroll
-        for (int r = 0; r < kTileRows; ++r) {
+        for (int r = 0; r < TR; ++r) {
             av[r] = __builtin_bit_cast(
                 u32x4, __builtin_amdgcn_raw_buffer_load_b128(ad, lo + r * half, 0, kNonTemporal));
             sv[r] = __builtin_amdgcn_raw_buffer_load_b16(sd, lso + r * sixteenth, 0, kNonTemporal);
@@ -600,33 +602,34 @@ gemv_tile(const uint8_t *__restrict__ A, const uint8_t *__restrict__ sfA,
         u32x4 xq[4];
         decode_x32(xv, xs2, xq);
 #pragma unroll
-        for (int r = 0; r < kTileRows; ++r) acc[r] = chunk32(av[r], sv[r], xq, acc[r]);
+        for (int r = 0; r < TR; ++r) acc[r] = chunk32(av[r], sv[r], xq, acc[r]);
     }
 
-    // Halve across the 32-lane halves: the low half keeps rows 0..7, the high
-    // half rows 8..15.
-    float h8[8];
+    // Halve across the 32-lane halves: the low half keeps rows 0 .. TR/2 - 1,
+    // the high half the rest.
+    constexpr int H = TR / 2, Q = TR / 4;
+    float h2[H];
 #pragma unroll
-    for (int r = 0; r < 8; ++r) {
+    for (int r = 0; r < H; ++r) {
         const auto t = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, acc[r]),
-                                                        __builtin_bit_cast(unsigned, acc[r + 8]),
+                                                        __builtin_bit_cast(unsigned, acc[r + H]),
                                                         false, false);
-        h8[r] = __builtin_bit_cast(float, static_cast<unsigned>(t[0])) +
+        h2[r] = __builtin_bit_cast(float, static_cast<unsigned>(t[0])) +
                 __builtin_bit_cast(float, static_cast<unsigned>(t[1]));
     }
-    // Halve across 16-lane rows: even rows keep values 0..3, odd rows 4..7.
-    float h4[4];
+    // Halve across 16-lane rows: even rows keep values 0 .. TR/4 - 1, odd rows the rest.
+    float h4[Q];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const auto t = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, h8[r]),
-                                                        __builtin_bit_cast(unsigned, h8[r + 4]),
+    for (int r = 0; r < Q; ++r) {
+        const auto t = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, h2[r]),
+                                                        __builtin_bit_cast(unsigned, h2[r + Q]),
                                                         false, false);
         h4[r] = __builtin_bit_cast(float, static_cast<unsigned>(t[0])) +
                 __builtin_bit_cast(float, static_cast<unsigned>(t[1]));
     }
     // Sum inside each 16-lane row.
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
+    for (int r = 0; r < Q; ++r) {
         float v = h4[r];
         v += dpp<0xB1>(v);    // quad_perm [1,0,3,2]
         v += dpp<0x4E>(v);    // quad_perm [2,3,0,1]
@@ -634,17 +637,21 @@ gemv_tile(const uint8_t *__restrict__ A, const uint8_t *__restrict__ sfA,
         v += dpp<0x140>(v);   // row_mirror
         h4[r] = v;
     }
-    // Lane j < 4 of 16-lane row q (q = lane / 16) holds tile row j + 4 (q & 1) + 8 (q >> 1).
+    // Lane j < TR/4 of 16-lane row q (q = lane / 16) holds tile row
+    // j + (TR/4) (q & 1) + (TR/2) (q >> 1).
     const int j = lane & 15, q = lane >> 4;
-    if (j < 4) {
-        const float v = j == 0 ? h4[0] : j == 1 ? h4[1] : j == 2 ? h4[2] : h4[3];
-        red[wave * kTileRows + j + 4 * (q & 1) + 8 * (q >> 1)] = v;
+    if (j < Q) {
+        float v = h4[0];
+#pragma unroll
+        for (int r = 1; r < Q; ++r)
+            if (j == r) v = h4[r];
+        red[wave * TR + j + Q * (q & 1) + H * (q >> 1)] = v;
     }
     __syncthreads();
     if (wave == 0 && lane < nrows) {
         float v = red[lane];
 #pragma unroll
-        for (int w = 1; w < W; ++w) v += red[w * kTileRows + lane];
+        for (int w = 1; w < W; ++w) v += red[w * TR + lane];
         const int64_t row = row0 + lane;
         if (part != nullptr) {
             part[(split * l + b) * m + row] = v;
@@ -759,11 +766,11 @@ hbm_read_probe(const uint8_t *__restrict__ buf, int64_t n16, uint32_t *__restric
 // ---------------------------------------------------------------- host side
 // x staging of a fast variant: fp16 x~ in LDS (gemv_fast), packed codes in LDS
 // (gemv_fastp), no staging (gemv_fastg, x read next to A every iteration), or
-// 16-row tiles whose waves split K and keep x~ of their slice in registers
-// (gemv_tile).
+// row tiles (16, 8 or 4 rows) whose waves split K and keep x~ of their slice
+// in registers (gemv_tile).
 enum XForm { kXHalf = 0, kXPacked = 1, kXGlobal = 2, kXTile = 3 };
 
-// The row-tile kernel addresses a tile's 16 rows through one descriptor with
+// The row-tile kernel addresses a tile's rows through one descriptor with
 // 32-bit offsets; it takes K up to this bound.
 constexpr int64_t kTileMaxK = int64_t(1) << 26;
 
@@ -779,7 +786,8 @@ constexpr Variant kVariants[] = {
     {4, 2, 4, kXPacked},  {2, 4, 8, kXPacked},  {4, 2, 8, kXPacked},  {1, 4, 8, kXPacked},
     {2, 4, 7, kXGlobal},  {2, 2, 7, kXGlobal},  {4, 2, 7, kXGlobal},  {2, 4, 4, kXGlobal},
     {1, 8, 7, kXGlobal},  {4, 1, 8, kXGlobal},  {16, 1, 8, kXTile},   {16, 1, 4, kXTile},
-    {16, 1, 2, kXTile},   {16, 1, 1, kXTile},
+    {16, 1, 2, kXTile},   {16, 1, 1, kXTile},   {8, 1, 1, kXTile},    {8, 1, 2, kXTile},
+    {4, 1, 1, kXTile},    {4, 1, 2, kXTile},
 };
 constexpr int kNumVariants = static_cast<int>(sizeof(kVariants) / sizeof(kVariants[0]));
 
@@ -811,10 +819,14 @@ FastKernel fast_kernel(int v) {
     case 19: return gemv_fastg<2, 4, 4>;
     case 20: return gemv_fastg<1, 8, 7>;
     case 21: return gemv_fastg<4, 1, 8>;
-    case 22: return gemv_tile<8>;
-    case 23: return gemv_tile<4>;
-    case 24: return gemv_tile<2>;
-    case 25: return gemv_tile<1>;
+    case 22: return gemv_tile<8, 16>;
+    case 23: return gemv_tile<4, 16>;
+    case 24: return gemv_tile<2, 16>;
+    case 25: return gemv_tile<1, 16>;
+    case 26: return gemv_tile<1, 8>;
+    case 27: return gemv_tile<2, 8>;
+    case 28: return gemv_tile<1, 4>;
+    case 29: return gemv_tile<2, 4>;
     default: return nullptr;
     }
 }
@@ -825,14 +837,16 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // of one workgroup's K-range, from MI355X measurements on the decode, batched,
 // Gaussian and short-K workloads: long rows want more rows in flight per
 // workgroup; with 3 to 5 iterations per row x read next to A beats staging it;
-// rows of one or two iterations are best read as 16-row tiles, whose 16 loads
-// per wave are all in flight at once.
+// rows of one or two iterations are best read as row tiles, whose loads are
+// all in flight at once: rows of one iteration as 4-row tiles of one wave
+// (many small waves, little arithmetic left in each when its last load lands),
+// rows of two as 16-row tiles of two waves.
 int default_variant(int64_t k) {
     const int64_t nit = ceil_div(k < kMaxChunk ? k : kMaxChunk, kIterElems);
     if (nit >= 6) return 0;    // {2, 4, 7}
     if (nit >= 3) return 19;   // {2, 4, 4} x read next to A
     if (nit == 2) return 24;   // 16-row tile, 2 waves
-    return 25;                 // 16-row tile, 1 wave
+    return 28;                 // 4-row tile, 1 wave
 }
 
 struct Plan {
@@ -892,7 +906,7 @@ int make_plan(int64_t l, int64_t m, int64_t k, bool aligned, const nvfp4_gemv_tu
     if (p->path == NVFP4_GEMV_PATH_FAST) {
         const Variant &v = kVariants[p->variant];
         if (v.xform == kXTile && k > kTileMaxK) return NVFP4_GEMV_ERR_BAD_TUNING;
-        rows_per_group = v.xform == kXTile ? kTileRows : static_cast<int64_t>(v.R) * v.W;
+        rows_per_group = v.xform == kXTile ? v.R : static_cast<int64_t>(v.R) * v.W;
         p->threads = v.W * kWave;
     } else {
         p->variant = 0;

@@ -146,21 +146,21 @@ def test_plan_explicit_choices(lib):
 
 
 def test_tile_variants_plan(lib):
-    """16-row tile variants: K bound, no K split while waves cover the slices."""
+    """Row-tile variants (16, 8 or 4 rows): K bound, no K split while waves cover the slices."""
     tiles = [v for v in range(1, pd.nvfp4_gemv_num_variants() + 1)
              if pd.nvfp4_gemv_variant_info(v)[3] == 3]
     assert tiles
     for v in tiles:
         r, u, w, _ = pd.nvfp4_gemv_variant_info(v)
-        assert r == 16 and u == 1
+        assert r in (16, 8, 4) and u == 1
         with pytest.raises(pd.Nvfp4GemvError):
             pd.nvfp4_gemv_plan(1, 64, 2 ** 26 + 32, tuning={"variant": v})
         t, ws = pd.nvfp4_gemv_plan(1, 64, 2 ** 26, tuning={"variant": v, "ksplit": 1})
         assert t.ksplit == 1 and ws == 0
-        # 448 tiles fill the 256 compute units: no split
+        # 448 to 1792 tiles fill the 256 compute units: no split
         t, _ = pd.nvfp4_gemv_plan(1, 7168, 16384, tuning={"variant": v})
         assert t.ksplit == 1
-        # 8 tiles: split while each split keeps a slice for every wave
+        # 8 to 32 tiles: split while each split keeps a slice for every wave
         t, _ = pd.nvfp4_gemv_plan(1, 128, 16384, tuning={"variant": v})
         assert t.ksplit == max(1, 8 // w)
 
@@ -361,3 +361,13 @@ def test_grouped_validation(lib):
     assert gcall(tuning=_binding.MmaTuning(0, 0, 2, 0)) == pd.NVFP4_GEMV_ERR_BAD_TUNING  # no K split
     assert gcall(tuning=_binding.MmaTuning(1, 0, 0, 0), k=48) == pd.NVFP4_GEMV_ERR_BAD_TUNING
     assert gcall(tuning=_binding.MmaTuning(0, 1, 0, 17)) == pd.NVFP4_GEMV_ERR_BAD_TUNING  # > 16 rows
+
+
+@pytest.mark.parametrize("l,m,k,variant", [(1, 7168, 16384, 1), (8, 4096, 7168, 20),
+                                           (4, 7168, 2048, 29), (16, 2048, 4096, 25)])
+def test_default_plans_of_the_benchmark_workloads(lib, l, m, k, variant):
+    """The measured defaults: (2, 4, 7) staged for long rows, x read next to A
+    for 3-5 slices, the 2-wave 16-row tile for 2 slices, the 1-wave 4-row tile
+    for 1 slice; none of these workloads splits K."""
+    t, ws = pd.nvfp4_gemv_plan(l, m, k)
+    assert t.path == pd.NVFP4_GEMV_PATH_FAST and t.variant == variant and t.ksplit == 1 and ws == 0

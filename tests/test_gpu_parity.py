@@ -128,7 +128,7 @@ def test_generic_kernel(l, m, k, ksplit):
     assert_bits_equal(run_gpu(to_device(ops), l, m, k, tuning=tun), want, "generic")
 
 
-NUM_VARIANTS = 26
+NUM_VARIANTS = 30
 
 
 def test_variant_count():
