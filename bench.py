@@ -23,7 +23,7 @@ Other paths (--path), each printing its own JSON line of the same form:
                batch (--act-config tokens | decode_x)
   gemv_bf16x   the GEMV fed by a bf16 activation: quantiser + GEMV per step
   smalln       the small-N GEMM: one weight matrix against n vectors
-               (--smalln-config decode_n4 | decode_n16 | tiny_n3)
+               (--smalln-config decode_n2 | decode_n4 | decode_n16 | tiny_n3)
   grouped      the grouped (MoE) GEMV: routed tokens against their experts'
                weights (--moe-config moe_decode | moe_tiny)
 
@@ -50,7 +50,7 @@ CSRC = os.path.join(ROOT, "precision_decode_amd", "csrc")
 PROFILES = os.path.join(ROOT, "profiles")
 # counter summaries under profiles/ are valid only for the source they were taken on
 KERNEL_SOURCES = {"gemv_fast": "nvfp4_gemv.hip", "quantize_blocks": "nvfp4_quantize.hip",
-                  "mma_stream": "nvfp4_mma.hip"}
+                  "mma_stream": "nvfp4_mma.hip", "vec_tile": "nvfp4_mma.hip"}
 
 
 def parse_args(argv=None):
@@ -479,8 +479,12 @@ def bench_smalln(args, torch, np, pd, workloads):
                      "bytes_per_step": nbytes, "replicas": reps,
                      "operands": "HBM (rotated over >= 1 GB of copies)",
                      "plan": {"path": plan.path, "variant": plan.variant, "ksplit": plan.ksplit}}
-    out["roofline"] = roofline(gbs, recorded_traffic(cfg.name, "mma_stream"),
-                               mfma_tflops=flops / (ms_step * 1e-3) / 1e12)
+    # the plan's kernel: matrix cores (mma_stream) or VALU row tiles (vec_tile)
+    valu = plan.path == pd.NVFP4_GEMV_PATH_FAST and \
+        pd.nvfp4_mma_variant_form(plan.variant) == pd.NVFP4_MMA_FORM_VALU_TILES
+    kernel = "vec_tile" if valu else "mma_stream"
+    extra = {} if valu else {"mfma_tflops": flops / (ms_step * 1e-3) / 1e12}
+    out["roofline"] = roofline(gbs, recorded_traffic(cfg.name, kernel), kernel=kernel, **extra)
     out["cpu_baseline"] = cpu
     return out
 

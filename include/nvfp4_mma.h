@@ -78,7 +78,8 @@ typedef struct nvfp4_mma_tuning_t {
     int32_t ksplit;         /* K split across workgroups, 0 = default, >= 1 explicit;
                                the grouped GEMV takes 0 or 1 only                     */
     int32_t rows_per_block; /* weight rows per workgroup, 0 = default, 1 .. 16 x the
-                               variant's row tiles per wave                            */
+                               variant's row tiles per wave (VALU row tiles: 1 .. the
+                               tile's rows)                                            */
 } nvfp4_mma_tuning_t;
 
 /*
@@ -94,16 +95,30 @@ int nvfp4_gemm_smalln_launch(const uint8_t *A_packed, const uint8_t *sfA,
                              int64_t l, int64_t m, int64_t n, int64_t k,
                              int32_t out_type, void *stream);
 
+#define NVFP4_MMA_FORM_MATRIX_CORES 0
+#define NVFP4_MMA_FORM_VALU_TILES 1
+
 /*
  * Number of fast small-N / grouped kernel variants, and the shape of variant
- * v (1-based): MFMA row tiles of 16 weight rows per wave, K windows of 256
- * elements (128 bytes of every row) kept in flight per wave, waves per
- * workgroup (each wave takes every waves-th window of the workgroup's K
- * range).  Returns a status.
+ * v (1-based).  Its form (nvfp4_mma_variant_form) says how the three numbers
+ * read:
+ *  - NVFP4_MMA_FORM_MATRIX_CORES: MFMA row tiles of 16 weight rows per wave,
+ *    K windows of 256 elements (128 bytes of every row) kept in flight per
+ *    wave, waves per workgroup (each wave takes every waves-th window of the
+ *    workgroup's K range);
+ *  - NVFP4_MMA_FORM_VALU_TILES: weight rows per workgroup tile, vectors per
+ *    pass over the tile, waves per workgroup (each wave takes every waves-th
+ *    K slice of 2048 elements, 1 KiB of every row per load).  The products
+ *    run on the VALU; more vectors than one pass holds mean another pass over
+ *    the tile's rows.  These variants never split K: an explicit ksplit above
+ *    1 or rows_per_block above the tile's rows is BAD_TUNING.
+ * Each returns a status (BAD_TUNING for v outside 1 .. num_variants,
+ * NULL_POINTER for a NULL output).
  */
 int nvfp4_mma_num_variants(void);
 int nvfp4_mma_variant_info(int v, int32_t *row_tiles_per_wave, int32_t *windows_in_flight,
                            int32_t *waves_per_group);
+int nvfp4_mma_variant_form(int v, int32_t *form);
 
 /*
  * The small-N plan the library would use (path, variant, K split, rows per

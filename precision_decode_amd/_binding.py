@@ -33,6 +33,9 @@ NVFP4_ROUND_NEAREST_LOWER = 2
 NVFP4_OUT_F16 = 0
 NVFP4_OUT_BF16 = 1
 
+NVFP4_MMA_FORM_MATRIX_CORES = 0
+NVFP4_MMA_FORM_VALU_TILES = 1
+
 NVFP4_GEMV_PATH_AUTO = 0
 NVFP4_GEMV_PATH_FAST = 1
 NVFP4_GEMV_PATH_GENERIC = 2
@@ -54,6 +57,7 @@ EXPORTED = (
     "nvfp4_gemm_smalln_launch",
     "nvfp4_mma_num_variants",
     "nvfp4_mma_variant_info",
+    "nvfp4_mma_variant_form",
     "nvfp4_gemm_smalln_plan",
     "nvfp4_gemm_smalln_launch_tuned",
     "nvfp4_grouped_gemv_launch",
@@ -134,6 +138,8 @@ def load():
     lib.nvfp4_mma_num_variants.argtypes = []
     lib.nvfp4_mma_variant_info.restype = ctypes.c_int
     lib.nvfp4_mma_variant_info.argtypes = [ctypes.c_int] + [ctypes.POINTER(ctypes.c_int32)] * 3
+    lib.nvfp4_mma_variant_form.restype = ctypes.c_int
+    lib.nvfp4_mma_variant_form.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_int32)]
     lib.nvfp4_gemm_smalln_plan.restype = ctypes.c_int
     lib.nvfp4_gemm_smalln_plan.argtypes = [_I64, _I64, _I64, _I64, ctypes.c_int,
                                            ctypes.POINTER(MmaTuning), ctypes.POINTER(MmaTuning),
@@ -282,11 +288,20 @@ def nvfp4_mma_num_variants() -> int:
 
 
 def nvfp4_mma_variant_info(v: int):
-    """(row tiles of 16 per wave, windows in flight, waves per group)."""
+    """Matrix-core variants: (row tiles of 16 per wave, windows in flight, waves
+    per group); VALU row-tile variants: (rows per tile, vectors per pass, waves
+    per group)."""
     r, u, w = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
     _check(load().nvfp4_mma_variant_info(v, ctypes.byref(r), ctypes.byref(u), ctypes.byref(w)),
            "nvfp4_mma_variant_info")
     return r.value, u.value, w.value
+
+
+def nvfp4_mma_variant_form(v: int) -> int:
+    """NVFP4_MMA_FORM_MATRIX_CORES (0) or NVFP4_MMA_FORM_VALU_TILES (1)."""
+    f = ctypes.c_int32()
+    _check(load().nvfp4_mma_variant_form(v, ctypes.byref(f)), "nvfp4_mma_variant_form")
+    return f.value
 
 
 def nvfp4_gemm_smalln_plan(l, m, n, k, aligned=True, tuning=None):

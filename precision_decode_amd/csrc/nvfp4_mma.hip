@@ -57,6 +57,7 @@ constexpr int64_t kMaxFastK = int64_t(1) << 26;   // keeps 32-row descriptors wi
 constexpr int64_t kComputeUnits = 256;            // CUs of an MI355X (8 XCDs x 32)
 constexpr int kReduceThreads = 256;
 constexpr int kGenericWaves = 4;
+constexpr int64_t kSliceElems = 2048;   // VALU tiles: K elements of one slice, 1 KiB of a row
 
 struct MmaArgs {
     const uint8_t *W, *sW;      // weights [groups][rows][k/2], scales [groups][rows][k/16]
@@ -297,6 +298,188 @@ __global__ void __launch_bounds__(W * kWave) mma_stream(const MmaArgs a) {
     }
 }
 
+// ---------------------------------------------------------------- VALU row tiles
+// For few vectors per weight matrix (small-N GEMM with n <= 4, experts with a
+// handful of tokens) the products fit the VALU, and the weights are better
+// read row-contiguously than in the 16-rows x 64-bytes pattern the matrix
+// cores want.  A workgroup owns a tile of TR weight rows of one group; its W
+// waves take K slices of 2048 elements (1 KiB of every row) in turn.  The
+// group's vectors are taken in passes of up to T: for one slice a wave loads
+// the pass's vectors (16 bytes and a scale pair per lane each, cached: every
+// workgroup of the group reads them) and then one 16-byte non-temporal load
+// per lane for each of the TR rows, back to back; decodes each vector once to
+// fp16 (e2m1 * e4m3, exact), each row's codes once, and takes the T dot
+// products of the row with v_dot2_f32_f16, scaling each 16-element block sum
+// by its weight scale in fp32.  Vectors past the pass's count read zeros
+// and are skipped (wave-uniform).  Per pass, the TR x T per-lane sums are
+// halved across the 32-lane halves and the 16-lane rows of the wave, summed
+// inside each 16-lane row by DPP, and the waves' sums meet in LDS in wave
+// order.  More than T vectors mean another pass over the tile's rows.
+template <int TR, int T, int W, bool GROUPED>
+__global__ void __launch_bounds__(W * kWave) vec_tile(const MmaArgs a) {
+    constexpr int NV = TR * T;   // sums per pass
+    static_assert(NV >= 4 && (NV & (NV - 1)) == 0, "TR * T: a power of two, at least 4");
+    constexpr int H = NV / 2, Q = NV / 4;
+    __shared__ float red[W * NV];
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+
+    // the plan keeps the workgroup count below 2^31: 32-bit division
+    const uint32_t gi = blockIdx.x;
+    const uint32_t rbs = static_cast<uint32_t>(a.row_blocks);
+    const uint32_t grp32 = gi / rbs;
+    const int64_t rb = gi - grp32 * rbs;
+    const int64_t grp = grp32;
+
+    int64_t v0, v1;
+    vector_range<GROUPED>(a, grp, &v0, &v1);
+    if (v1 <= v0) return;   // workgroup-uniform: an expert without tokens
+
+    const int64_t k = a.k;
+    const uint32_t half = static_cast<uint32_t>(k / 2);
+    const uint32_t sixteenth = static_cast<uint32_t>(k / 16);
+    const int nsl = static_cast<int>((k + kSliceElems - 1) / kSliceElems);
+    const int64_t row0 = rb * a.rows_per_block;
+    const int nrows = static_cast<int>((a.rows - row0 < a.rows_per_block) ? a.rows - row0
+                                                                           : a.rows_per_block);
+    const __amdgpu_buffer_rsrc_t wdesc =
+        buffer_of(a.W + (grp * a.rows + row0) * (k / 2), nrows * static_cast<int>(half));
+    const __amdgpu_buffer_rsrc_t swdesc =
+        buffer_of(a.sW + (grp * a.rows + row0) * (k / 16), nrows * static_cast<int>(sixteenth));
+    const float al = group_alpha(a, grp, GROUPED);
+
+    for (int64_t vp = v0; vp < v1; vp += T) {
+        const int nv = static_cast<int>((v1 - vp < T) ? v1 - vp : T);
+        const __amdgpu_buffer_rsrc_t vdesc =
+            buffer_of(a.V + vp * (k / 2), nv * static_cast<int>(half));
+        const __amdgpu_buffer_rsrc_t svdesc =
+            buffer_of(a.sV + vp * (k / 16), nv * static_cast<int>(sixteenth));
+
+        float acc[TR][T];
+#pragma unroll
+        for (int r = 0; r < TR; ++r)
+#pragma unroll
+            for (int j = 0; j < T; ++j) acc[r][j] = 0.0f;
+
+        for (int sl = wave; sl < nsl; sl += W) {
+            const int64_t e0 = static_cast<int64_t>(sl) * kSliceElems + 32 * lane;
+            const uint32_t lo = e0 < k ? static_cast<uint32_t>(e0 / 2) : kOutOfRange;
+            const uint32_t lso = e0 < k ? static_cast<uint32_t>(e0 / 16) : kOutOfRange;
+
+            phase_fence();
+            u32x4 xv[T];
+            uint32_t xs[T];
+#pragma unroll
+            for (int j = 0; j < T; ++j) {
+                xv[j] = __builtin_bit_cast(
+                    u32x4, __builtin_amdgcn_raw_buffer_load_b128(vdesc, lo + j * half, 0, 0));
+                xs[j] = __builtin_amdgcn_raw_buffer_load_b16(svdesc, lso + j * sixteenth, 0, 0);
+            }
+            u32x4 av[TR];
+            uint32_t sv[TR];
+#pragma unroll
+            for (int r = 0; r < TR; ++r) {
+                av[r] = __builtin_bit_cast(
+                    u32x4, __builtin_amdgcn_raw_buffer_load_b128(wdesc, lo + r * half, 0, kNonTemporal));
+                sv[r] = __builtin_amdgcn_raw_buffer_load_b16(swdesc, lso + r * sixteenth, 0,
+                                                             kNonTemporal);
+                phase_fence();   // row by row, in the order the rows are consumed
+            }
+
+            u32x4 xq[T][4];   // x~ pairs: xq[j][i / 4][i % 4] holds elements 2i, 2i + 1
+#pragma unroll
+            for (int j = 0; j < T; ++j) {
+                f16x8 o[4];
+                decode32(xv[j], xs[j], o);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) xq[j][q] = __builtin_bit_cast(u32x4, o[q]);
+            }
+#pragma unroll
+            for (int r = 0; r < TR; ++r) {
+                const uint32_t aw[4] = {av[r].x, av[r].y, av[r].z, av[r].w};
+                f16x2 ad[16];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    ad[4 * q + 0] = e2m1x2_f16<0>(aw[q]);
+                    ad[4 * q + 1] = e2m1x2_f16<1>(aw[q]);
+                    ad[4 * q + 2] = e2m1x2_f16<2>(aw[q]);
+                    ad[4 * q + 3] = e2m1x2_f16<3>(aw[q]);
+                }
+                const f32x2 sa = e4m3x2_f32(sv[r]);
+#pragma unroll
+                for (int j = 0; j < T; ++j) {
+                    if (j < nv) {   // wave-uniform
+                        float b0 = 0.0f, b1 = 0.0f;
+#pragma unroll
+                        for (int i = 0; i < 8; ++i)
+                            b0 = __builtin_amdgcn_fdot2(ad[i], halves(xq[j][i / 4][i % 4]), b0, false);
+#pragma unroll
+                        for (int i = 8; i < 16; ++i)
+                            b1 = __builtin_amdgcn_fdot2(ad[i], halves(xq[j][i / 4][i % 4]), b1, false);
+                        acc[r][j] = __builtin_fmaf(b0, sa.x, acc[r][j]);
+                        acc[r][j] = __builtin_fmaf(b1, sa.y, acc[r][j]);
+                    }
+                }
+            }
+        }
+
+        // Sum i = r * T + j.  Halve across the 32-lane halves (the low half
+        // keeps sums 0 .. H - 1), then across 16-lane rows (even rows keep
+        // 0 .. Q - 1 of their half's), then inside each 16-lane row.
+        float h2[H];
+#pragma unroll
+        for (int i = 0; i < H; ++i) {
+            const auto t = __builtin_amdgcn_permlane32_swap(
+                __builtin_bit_cast(unsigned, acc[i / T][i % T]),
+                __builtin_bit_cast(unsigned, acc[(i + H) / T][(i + H) % T]), false, false);
+            h2[i] = __builtin_bit_cast(float, static_cast<unsigned>(t[0])) +
+                    __builtin_bit_cast(float, static_cast<unsigned>(t[1]));
+        }
+        float h4[Q];
+#pragma unroll
+        for (int i = 0; i < Q; ++i) {
+            const auto t = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, h2[i]),
+                                                            __builtin_bit_cast(unsigned, h2[i + Q]),
+                                                            false, false);
+            h4[i] = __builtin_bit_cast(float, static_cast<unsigned>(t[0])) +
+                    __builtin_bit_cast(float, static_cast<unsigned>(t[1]));
+        }
+#pragma unroll
+        for (int i = 0; i < Q; ++i) {
+            float v = h4[i];
+            v += dpp<0xB1>(v);    // quad_perm [1,0,3,2]
+            v += dpp<0x4E>(v);    // quad_perm [2,3,0,1]
+            v += dpp<0x141>(v);   // row_half_mirror
+            v += dpp<0x140>(v);   // row_mirror
+            h4[i] = v;
+        }
+        // Lane jj < Q of 16-lane row q holds sum jj + Q (q & 1) + H (q >> 1).
+        const int jj = lane & 15, q = lane >> 4;
+        if (jj < Q) {
+            float v = h4[0];
+#pragma unroll
+            for (int i = 1; i < Q; ++i)
+                if (jj == i) v = h4[i];
+            red[wave * NV + jj + Q * (q & 1) + H * (q >> 1)] = v;
+        }
+        __syncthreads();
+        if (wave == 0 && lane < NV) {
+            const int r = lane / T, j = lane % T;
+            float v = red[lane];
+#pragma unroll
+            for (int w = 1; w < W; ++w) v += red[w * NV + lane];
+            if (r < nrows && j < nv) {
+                if (GROUPED)
+                    a.c[(vp + j) * a.rows + row0 + r] = round_out(al, v, a.out_bf16);
+                else
+                    a.c[(grp * a.rows + row0 + r) * a.nvec + (vp - v0 + j)] =
+                        round_out(al, v, a.out_bf16);
+            }
+        }
+        if (vp + T < v1) __syncthreads();   // before the next pass reuses `red`
+    }
+}
+
 // ---------------------------------------------------------------- generic kernel
 // Any k % 16 == 0 and any byte alignment.  One wave per (group, weight row);
 // lanes take 16-element blocks; bytes are loaded singly; vectors one by one.
@@ -365,18 +548,31 @@ mma_splitk_reduce(const float *__restrict__ part, const float *__restrict__ alph
 }
 
 // ---------------------------------------------------------------- host side
+enum Form { kMatrixCores = 0, kValuTiles = 1 };
 struct Variant {
     int R, U, W;
+    int form;
 };
-// {row tiles per wave, windows in flight, waves per workgroup}
+// Matrix cores (mma_stream): {row tiles of 16 per wave, windows in flight,
+// waves per workgroup}.  VALU row tiles (vec_tile): {rows per tile, vectors
+// per pass, waves per workgroup}.
 constexpr Variant kVariants[] = {
-    {1, 2, 4}, {1, 2, 8}, {2, 2, 4}, {2, 1, 8}, {1, 3, 4}, {2, 2, 8},
+    {1, 2, 4, kMatrixCores}, {1, 2, 8, kMatrixCores}, {2, 2, 4, kMatrixCores},
+    {2, 1, 8, kMatrixCores}, {1, 3, 4, kMatrixCores}, {2, 2, 8, kMatrixCores},
+    {4, 2, 4, kValuTiles},   {8, 2, 4, kValuTiles},   {4, 4, 4, kValuTiles},
+    {8, 4, 4, kValuTiles},
 };
 constexpr int kNumVariants = static_cast<int>(sizeof(kVariants) / sizeof(kVariants[0]));
 // Defaults from MI355X sweeps of every variant: {2, 2, 4} on the decode-style
-// small-N workloads (one 7168 x 16384 weight against 4 or 16 vectors), {2, 1, 8}
-// on the grouped decode workload (64 experts of 2048 x 7168, 128 tokens).
+// small-N workloads (one 7168 x 16384 weight against 3 to 16 vectors), the
+// VALU tiles {4, 2, 4} against 1 or 2 vectors (12.9 and 13.8 us against 17.8
+// and 18.0 on the matrix cores, which pad the vectors to 16), {2, 1, 8} on the
+// grouped decode workload (64 experts of 2048 x 7168, 128 tokens; the VALU
+// tiles were no faster there, with up to 6 tokens per expert).  The VALU tiles
+// never split K, so they are the default only while their tiles fill the GPU.
 constexpr int kDefaultSmallN = 2;
+constexpr int kDefaultSmallNFew = 6;
+constexpr int64_t kFewVectors = 2;
 constexpr int kDefaultGrouped = 3;
 
 typedef void (*MmaKernel)(const MmaArgs);
@@ -390,6 +586,10 @@ MmaKernel fast_kernel(int v) {
     case 3: return mma_stream<2, 1, 8, G>;
     case 4: return mma_stream<1, 3, 4, G>;
     case 5: return mma_stream<2, 2, 8, G>;
+    case 6: return vec_tile<4, 2, 4, G>;
+    case 7: return vec_tile<8, 2, 4, G>;
+    case 8: return vec_tile<4, 4, 4, G>;
+    case 9: return vec_tile<8, 4, 4, G>;
     default: return nullptr;
     }
 }
@@ -449,8 +649,30 @@ int make_plan(int64_t groups, int64_t rows, int64_t nvec_per_group, int64_t k, b
         p->rows_per_block = kGenericWaves;
         p->threads = kGenericWaves * kWave;
     } else {
-        p->variant = tun.variant > 0 ? tun.variant - 1 : (grouped ? kDefaultGrouped : kDefaultSmallN);
+        if (tun.variant > 0) {
+            p->variant = tun.variant - 1;
+        } else if (grouped) {
+            p->variant = kDefaultGrouped;
+        } else {
+            const int64_t tiles = groups * ceil_div(rows, int64_t(kVariants[kDefaultSmallNFew].R));
+            p->variant = (nvec_per_group <= kFewVectors && tiles >= 4 * kComputeUnits)
+                             ? kDefaultSmallNFew
+                             : kDefaultSmallN;
+        }
         const Variant &v = kVariants[p->variant];
+        if (v.form == kValuTiles) {
+            // a workgroup per tile of v.R rows (or fewer on request), no K split
+            if (tun.rows_per_block > v.R || tun.ksplit > 1) return NVFP4_GEMV_ERR_BAD_TUNING;
+            p->ksplit = 1;
+            p->kchunk = k;
+            p->rows_per_block = tun.rows_per_block > 0 ? tun.rows_per_block : v.R;
+            p->threads = v.W * kWave;
+            p->row_blocks = ceil_div(rows, p->rows_per_block);
+            p->groups = groups * p->row_blocks;
+            if (p->groups >= (int64_t(1) << 31)) return NVFP4_GEMV_ERR_BAD_SHAPE;
+            p->ws_bytes = 0;
+            return NVFP4_GEMV_OK;
+        }
         const int64_t tile_rows = int64_t(v.R) * kTile;
         if (tun.rows_per_block > tile_rows) return NVFP4_GEMV_ERR_BAD_TUNING;
         int64_t ks = 1;
@@ -607,6 +829,13 @@ int nvfp4_mma_variant_info(int v, int32_t *row_tiles_per_wave, int32_t *windows_
     *row_tiles_per_wave = kVariants[v - 1].R;
     *windows_in_flight = kVariants[v - 1].U;
     *waves_per_group = kVariants[v - 1].W;
+    return NVFP4_GEMV_OK;
+}
+
+int nvfp4_mma_variant_form(int v, int32_t *form) {
+    if (!form) return NVFP4_GEMV_ERR_NULL_POINTER;
+    if (v < 1 || v > kNumVariants) return NVFP4_GEMV_ERR_BAD_TUNING;
+    *form = kVariants[v - 1].form;
     return NVFP4_GEMV_OK;
 }
 

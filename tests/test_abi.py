@@ -303,11 +303,30 @@ def test_smalln_plans(lib):
     t, _ = pd.nvfp4_gemm_smalln_plan(2, 100, 3, 64, aligned=False)
     assert t.path == pd.NVFP4_GEMV_PATH_GENERIC
     n = pd.nvfp4_mma_num_variants()
+    forms = set()
     for v in range(1, n + 1):
         r, u, w = pd.nvfp4_mma_variant_info(v)
-        assert r in (1, 2) and u >= 1 and 1 <= w <= 16
-        t, ws = pd.nvfp4_gemm_smalln_plan(3, 100, 5, 4096, tuning={"variant": v, "ksplit": 3})
-        assert t.variant == v and t.ksplit == 3 and ws == 3 * 3 * 100 * 5 * 4
+        form = pd.nvfp4_mma_variant_form(v)
+        forms.add(form)
+        if form == pd.NVFP4_MMA_FORM_MATRIX_CORES:
+            assert r in (1, 2) and u >= 1 and 1 <= w <= 16
+            t, ws = pd.nvfp4_gemm_smalln_plan(3, 100, 5, 4096, tuning={"variant": v, "ksplit": 3})
+            assert t.variant == v and t.ksplit == 3 and ws == 3 * 3 * 100 * 5 * 4
+        else:
+            # VALU row tiles: r rows per workgroup, u vectors per pass, never a K split
+            assert form == pd.NVFP4_MMA_FORM_VALU_TILES
+            assert r in (4, 8) and u in (2, 4) and 1 <= w <= 16
+            t, ws = pd.nvfp4_gemm_smalln_plan(3, 100, 5, 4096, tuning={"variant": v})
+            assert t.variant == v and t.ksplit == 1 and ws == 0 and t.rows_per_block == r
+            t, _ = pd.nvfp4_gemm_smalln_plan(3, 100, 5, 4096, tuning={"variant": v, "rows_per_block": 3})
+            assert t.rows_per_block == 3
+            for bad in ({"variant": v, "ksplit": 3}, {"variant": v, "rows_per_block": r + 1}):
+                with pytest.raises(pd.Nvfp4GemvError):
+                    pd.nvfp4_gemm_smalln_plan(3, 100, 5, 4096, tuning=bad)
+    assert forms == {pd.NVFP4_MMA_FORM_MATRIX_CORES, pd.NVFP4_MMA_FORM_VALU_TILES}
+    for bad_v in (0, n + 1):
+        with pytest.raises(pd.Nvfp4GemvError):
+            pd.nvfp4_mma_variant_form(bad_v)
     for bad in ({"variant": n + 1}, {"ksplit": 3, "path": pd.NVFP4_GEMV_PATH_GENERIC},
                 {"path": pd.NVFP4_GEMV_PATH_GENERIC, "variant": 1}, {"path": 3},
                 {"rows_per_block": -1}, {"variant": 1, "rows_per_block": 33},
@@ -371,3 +390,16 @@ def test_default_plans_of_the_benchmark_workloads(lib, l, m, k, variant):
     for 1 slice; none of these workloads splits K."""
     t, ws = pd.nvfp4_gemv_plan(l, m, k)
     assert t.path == pd.NVFP4_GEMV_PATH_FAST and t.variant == variant and t.ksplit == 1 and ws == 0
+
+
+def test_smalln_default_form_by_vector_count(lib):
+    """One or two vectors against a weight that fills the GPU with 4-row tiles
+    go to the VALU tiles; more vectors, or too few tiles, to the matrix cores."""
+    for n in (1, 2):
+        t, ws = pd.nvfp4_gemm_smalln_plan(1, 7168, n, 16384)
+        assert pd.nvfp4_mma_variant_form(t.variant) == pd.NVFP4_MMA_FORM_VALU_TILES
+        assert pd.nvfp4_mma_variant_info(t.variant) == (4, 2, 4)
+        assert t.ksplit == 1 and ws == 0 and t.rows_per_block == 4
+    for l, m, n, k in ((1, 7168, 3, 16384), (1, 7168, 16, 16384), (1, 256, 2, 16384)):
+        t, _ = pd.nvfp4_gemm_smalln_plan(l, m, n, k)
+        assert pd.nvfp4_mma_variant_form(t.variant) == pd.NVFP4_MMA_FORM_MATRIX_CORES, (l, m, n, k)

@@ -78,11 +78,25 @@ def test_smalln_default_plan_shapes(l, m, n, k):
     assert_bits_equal(run_smalln(ops, l, m, n, k), oracle_smalln(ops, l, m, n, k), f"{(l, m, n, k)}")
 
 
-@pytest.mark.parametrize("variant", range(1, 7))
+NUM_MMA_VARIANTS = 10
+
+
+def valu_tiles(v):
+    return pd.nvfp4_mma_variant_form(v) == pd.NVFP4_MMA_FORM_VALU_TILES
+
+
+def test_mma_variant_count():
+    assert pd.nvfp4_mma_num_variants() == NUM_MMA_VARIANTS
+
+
+@pytest.mark.parametrize("variant", range(1, NUM_MMA_VARIANTS + 1))
 @pytest.mark.parametrize("ksplit", [1, 3])
 def test_smalln_every_variant(variant, ksplit):
-    assert pd.nvfp4_mma_num_variants() == 6
-    l, m, n, k = 2, 75, 11, 2112       # ragged rows, k not a multiple of the 256-element window
+    if ksplit > 1 and valu_tiles(variant):
+        pytest.skip("VALU row tiles never split K")
+    # ragged rows, k not a multiple of the 256-element window nor of the
+    # 2048-element slice, 11 vectors: three passes of 4 for the VALU tiles
+    l, m, n, k = 2, 75, 11, 2112
     ops = smalln_ops(l, m, n, k, seed=variant * 10 + ksplit)
     want = oracle_smalln(ops, l, m, n, k, pd.NVFP4_OUT_BF16)
     tuning = {"path": pd.NVFP4_GEMV_PATH_FAST, "variant": variant, "ksplit": ksplit}
@@ -230,7 +244,7 @@ def test_grouped_configs_bit_exact(name, out_type):
     ([16, 16], 33, 512),
     ([2, 1, 0, 0, 4, 9], 96, 1024),
 ])
-@pytest.mark.parametrize("variant", [0, 1, 2, 3, 4, 5, 6])
+@pytest.mark.parametrize("variant", range(0, NUM_MMA_VARIANTS + 1))
 def test_grouped_shapes_every_variant(counts, n, k, variant):
     ops = grouped_ops(counts, n, k, seed=sum(counts) + n + variant)
     tokens, experts = int(sum(counts)), len(counts)
@@ -280,12 +294,15 @@ def test_grouped_zero_tokens_is_a_no_op():
     assert got.size == 0
 
 
-@pytest.mark.parametrize("variant", range(1, 7))
-@pytest.mark.parametrize("rows_per_block,ksplit", [(1, 1), (7, 2), (14, 1), (16, 3), (32, 1)])
+@pytest.mark.parametrize("variant", range(1, NUM_MMA_VARIANTS + 1))
+@pytest.mark.parametrize("rows_per_block,ksplit", [(1, 1), (3, 1), (7, 2), (14, 1), (16, 3), (32, 1)])
 def test_smalln_rows_per_block(variant, rows_per_block, ksplit):
     r, _, _ = pd.nvfp4_mma_variant_info(variant)
-    if rows_per_block > 16 * r:
+    most = r if valu_tiles(variant) else 16 * r
+    if rows_per_block > most:
         pytest.skip("more rows than the variant's tiles hold")
+    if ksplit > 1 and valu_tiles(variant):
+        pytest.skip("VALU row tiles never split K")
     l, m, n, k = 2, 45, 5, 1088
     ops = smalln_ops(l, m, n, k, seed=100 + variant * 7 + rows_per_block)
     tuning = {"variant": variant, "ksplit": ksplit, "rows_per_block": rows_per_block}
@@ -294,7 +311,8 @@ def test_smalln_rows_per_block(variant, rows_per_block, ksplit):
                       f"v{variant} rpb {rows_per_block} ks {ksplit}", "bf16")
 
 
-@pytest.mark.parametrize("variant,rows_per_block", [(1, 5), (3, 20), (4, 31), (2, 16)])
+@pytest.mark.parametrize("variant,rows_per_block", [(1, 5), (3, 20), (4, 31), (2, 16), (7, 3),
+                                                    (8, 5), (10, 1)])
 def test_grouped_rows_per_block(variant, rows_per_block):
     counts, n, k = [3, 0, 18, 1], 70, 512
     ops = grouped_ops(counts, n, k, seed=200 + rows_per_block)

@@ -199,6 +199,8 @@ class SmallNConfig:
 
 SMALLN_CONFIGS = {
     "tiny_n3": SmallNConfig("tiny_n3", 2, 80, 3, 256, note="tiny, ragged rows"),
+    "decode_n2": SmallNConfig("decode_n2", 1, 7168, 2, 16384,
+                              note="the decode weight against 2 vectors (one speculative token)"),
     "decode_n4": SmallNConfig("decode_n4", 1, 7168, 4, 16384,
                               note="the decode weight against 4 vectors (speculative tokens)"),
     "decode_n16": SmallNConfig("decode_n16", 1, 7168, 16, 16384,
