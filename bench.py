@@ -178,6 +178,13 @@ def roofline(gbs, traffic, **extra):
     return r
 
 
+def with_speedup(cpu, gbs):
+    """The CPU baseline with the GPU's throughput ratio to it (None stays None)."""
+    if cpu is None:
+        return None
+    return dict(cpu, gpu_speedup=round(gbs / cpu["value"], 1))
+
+
 def common_fields(args, gbs, ms_step, dtype):
     return {"value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
             "warmup": args.warmup, "ms_per_step": round(ms_step, 6),
@@ -289,7 +296,9 @@ def bench_gemv(args, torch, np, pd, workloads):
         cpu = {"value": round(nbytes / t_med / 1e9, 4), "unit": "GB/s", "cores": threads,
                "kind": "oracle",
                "sample": f"the whole {cfg.name} workload (l={l}, m={m}, k={k}), median of 3 runs "
-                         f"of {t_med:.3f}s, fp64 sums + fp32/fp16 epilogue, inputs in host memory"}
+                         f"of {t_med:.3f}s, fp64 sums + fp32/fp16 epilogue, inputs in host memory",
+               "seconds": round(t_med, 4),
+               "elements_per_s_per_core": round(l * m * k / t_med / threads, 1)}
         print(f"[bench] CPU oracle: {t_med:.3f}s per GEMV on {threads} threads", flush=True)
 
     out = {"metric": "achieved HBM GB/s for the NVFP4 block-scaled batched GEMV (us/call and % of "
@@ -303,7 +312,7 @@ def bench_gemv(args, torch, np, pd, workloads):
     out["roofline"] = roofline(gbs, recorded_traffic(cfg.name), probe_read_gbs=probe_gbs,
                                probe_read_same_size_gbs=probe_ws_gbs, cache_resident_gbs=warm_gbs)
     out["single_launch_us"] = single
-    out["cpu_baseline"] = cpu
+    out["cpu_baseline"] = with_speedup(cpu, gbs)
     return out
 
 
@@ -355,7 +364,7 @@ def bench_quantize(args, torch, np, pd, workloads):
                      "rows": rows, "d": d, "rule": args.rule, "bytes_per_step": nbytes,
                      "replicas": reps, "operands": "HBM (rotated over >= 1 GB of copies)"}
     out["roofline"] = roofline(gbs, recorded_traffic(cfg.name, "quantize_blocks"))
-    out["cpu_baseline"] = cpu
+    out["cpu_baseline"] = with_speedup(cpu, gbs)
     return out
 
 
@@ -417,7 +426,7 @@ def bench_bf16x(args, torch, np, pd, workloads):
                      "l": l, "m": m, "k": k, "rule": args.rule, "bytes_per_step": nbytes,
                      "replicas": reps, "operands": "HBM (rotated over >= 1 GB of copies)"}
     out["roofline"] = roofline(gbs, None)
-    out["cpu_baseline"] = cpu
+    out["cpu_baseline"] = with_speedup(cpu, gbs)
     return out
 
 
@@ -485,7 +494,7 @@ def bench_smalln(args, torch, np, pd, workloads):
     kernel = "vec_tile" if valu else "mma_stream"
     extra = {} if valu else {"mfma_tflops": flops / (ms_step * 1e-3) / 1e12}
     out["roofline"] = roofline(gbs, recorded_traffic(cfg.name, kernel), kernel=kernel, **extra)
-    out["cpu_baseline"] = cpu
+    out["cpu_baseline"] = with_speedup(cpu, gbs)
     return out
 
 
@@ -542,7 +551,7 @@ def bench_grouped(args, torch, np, pd, workloads):
                      "out": "bf16" if out_type else "f16", "bytes_per_step": nbytes,
                      "replicas": reps, "operands": "HBM (rotated over >= 1 GB of copies)"}
     out["roofline"] = roofline(gbs, recorded_traffic(cfg.name, "mma_stream"))
-    out["cpu_baseline"] = cpu
+    out["cpu_baseline"] = with_speedup(cpu, gbs)
     return out
 
 

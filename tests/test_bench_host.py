@@ -89,3 +89,10 @@ def test_single_launch_percentiles_order(n, monkeypatch):
 
     r = bench.single_launch_percentiles(FakeTorch, None, lambda i: None, n)
     assert r["launches"] == n and r["p10"] <= r["p50"] <= r["p90"]
+
+
+def test_cpu_baseline_speedup():
+    assert bench.with_speedup(None, 5000.0) is None
+    cpu = {"value": 0.5, "unit": "GB/s", "cores": 16, "kind": "oracle", "sample": "s"}
+    r = bench.with_speedup(cpu, 5000.0)
+    assert r["gpu_speedup"] == 10000.0 and r["value"] == 0.5 and "gpu_speedup" not in cpu
