@@ -178,6 +178,21 @@ def roofline(gbs, traffic, **extra):
     return r
 
 
+def parity_summary(np, got, want):
+    """fp16 outputs of the GPU against the oracle's: how many are bit-identical
+    and the largest distance in fp16 ulps (over the ordered bit patterns)."""
+    got = np.asarray(got, dtype=np.uint16).reshape(-1)
+    want = np.asarray(want, dtype=np.uint16).reshape(-1)
+
+    def ordered(b):
+        b = b.astype(np.int64)
+        return np.where(b & 0x8000, -(b & 0x7FFF), b & 0x7FFF)
+
+    dist = np.abs(ordered(got) - ordered(want))
+    return {"outputs": int(got.size), "bit_identical": int(np.count_nonzero(got == want)),
+            "max_ulp": int(dist.max()) if dist.size else 0}
+
+
 def with_speedup(cpu, gbs):
     """The CPU baseline with the GPU's throughput ratio to it (None stays None)."""
     if cpu is None:
@@ -291,14 +306,19 @@ def bench_gemv(args, torch, np, pd, workloads):
         from oracle import reference as ref
 
         threads = ref.default_threads()
-        t_med = cpu_time(lambda: ref.gemv(ops["A"], ops["sfA"], ops["x"], ops["sfx"], ops["alpha"],
-                                          l, m, k, nthreads=threads))
+        results = []
+        t_med = cpu_time(lambda: results.append(ref.gemv(ops["A"], ops["sfA"], ops["x"], ops["sfx"],
+                                                         ops["alpha"], l, m, k, nthreads=threads)))
+        torch.cuda.synchronize()
+        parity = parity_summary(np, c.cpu().numpy().view(np.uint16), results[-1])
+        print(f"[bench] parity of the last timed call with the oracle: {parity}", flush=True)
         cpu = {"value": round(nbytes / t_med / 1e9, 4), "unit": "GB/s", "cores": threads,
                "kind": "oracle",
                "sample": f"the whole {cfg.name} workload (l={l}, m={m}, k={k}), median of 3 runs "
                          f"of {t_med:.3f}s, fp64 sums + fp32/fp16 epilogue, inputs in host memory",
                "seconds": round(t_med, 4),
-               "elements_per_s_per_core": round(l * m * k / t_med / threads, 1)}
+               "elements_per_s_per_core": round(l * m * k / t_med / threads, 1),
+               "parity": parity}
         print(f"[bench] CPU oracle: {t_med:.3f}s per GEMV on {threads} threads", flush=True)
 
     out = {"metric": "achieved HBM GB/s for the NVFP4 block-scaled batched GEMV (us/call and % of "

@@ -96,3 +96,12 @@ def test_cpu_baseline_speedup():
     cpu = {"value": 0.5, "unit": "GB/s", "cores": 16, "kind": "oracle", "sample": "s"}
     r = bench.with_speedup(cpu, 5000.0)
     assert r["gpu_speedup"] == 10000.0 and r["value"] == 0.5 and "gpu_speedup" not in cpu
+
+
+def test_parity_summary_counts_ulps():
+    import numpy as np
+    want = np.array([0x3C00, 0x0000, 0x8001, 0xBC00], dtype=np.uint16)   # 1, +0, -tiny, -1
+    got = np.array([0x3C00, 0x8000, 0x0001, 0xBC02], dtype=np.uint16)    # 1, -0, +tiny, -1 - 2 ulp
+    r = bench.parity_summary(np, got, want)
+    assert r == {"outputs": 4, "bit_identical": 1, "max_ulp": 2}
+    assert bench.parity_summary(np, want, want)["bit_identical"] == 4
