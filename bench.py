@@ -26,9 +26,11 @@ Other paths (--path), each printing its own JSON line of the same form:
                (--smalln-config decode_n2 | decode_n4 | decode_n16 | tiny_n3)
   grouped      the grouped (MoE) GEMV: routed tokens against their experts'
                weights (--moe-config moe_decode | moe_tiny)
+  --packed     with smalln / grouped: the weights are packed once into the
+               matrix-core tile layout (not timed) and the packed calls timed
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config decode]
-                       [--path gemv|quantize|gemv_bf16x|smalln|grouped]
+                       [--path gemv|quantize|gemv_bf16x|smalln|grouped] [--packed]
 """
 from __future__ import annotations
 
@@ -50,7 +52,8 @@ CSRC = os.path.join(ROOT, "precision_decode_amd", "csrc")
 PROFILES = os.path.join(ROOT, "profiles")
 # counter summaries under profiles/ are valid only for the source they were taken on
 KERNEL_SOURCES = {"gemv_fast": "nvfp4_gemv.hip", "quantize_blocks": "nvfp4_quantize.hip",
-                  "mma_stream": "nvfp4_mma.hip", "vec_tile": "nvfp4_mma.hip"}
+                  "mma_stream": "nvfp4_mma.hip", "vec_tile": "nvfp4_mma.hip",
+                  "mma_stream_packed": "nvfp4_mma.hip"}
 
 
 def parse_args(argv=None):
@@ -79,6 +82,9 @@ def parse_args(argv=None):
     p.add_argument("--variant", type=int, default=0,
                    help="fast-kernel variant of the chosen path (0 = default plan)")
     p.add_argument("--ksplit", type=int, default=0, help="K split (0 = default plan)")
+    p.add_argument("--packed", action="store_true",
+                   help="--path smalln / grouped: weights pre-packed once (nvfp4_mma_pack_weight, "
+                        "outside the timed region) and the packed launches timed")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-probe", action="store_true")
     p.add_argument("--single-launches", type=int, default=50,
@@ -159,6 +165,20 @@ class Timer:
 def replicate(torch, base, nbytes, reps_arg):
     reps = reps_arg or max(1, -(-1_000_000_000 // nbytes))
     return [base] + [{n: t.clone() for n, t in base.items()} for _ in range(reps - 1)], reps
+
+
+def pack_replicas(torch, pd, replicas, wkey, skey, groups, rows, k):
+    """Adds the packed form of each replica's weights (an offline step, before
+    any timing); the row-major weights are dropped so only packed bytes rotate."""
+    cb, sb = pd.nvfp4_mma_packed_sizes(groups, rows, k)
+    for r in replicas:
+        wp = torch.empty(cb, dtype=torch.uint8, device="cuda")
+        swp = torch.empty(sb, dtype=torch.uint8, device="cuda")
+        pd.nvfp4_mma_pack_weight(r[wkey], r[skey], groups, rows, k, wp, swp)
+        r[wkey + "_packed"], r[skey + "_packed"] = wp, swp
+    torch.cuda.synchronize()
+    for r in replicas:
+        del r[wkey], r[skey]
 
 
 def run_copies(torch, mib):
@@ -469,17 +489,24 @@ def bench_smalln(args, torch, np, pd, workloads):
     tuning = {"variant": args.variant, "ksplit": args.ksplit}
     plan, ws_bytes = pd.nvfp4_gemm_smalln_plan(l, m, n, k, tuning=tuning if tuned else None)
     ws = torch.empty(max(ws_bytes, 4), dtype=torch.uint8, device="cuda")
+    if args.packed:
+        pack_replicas(torch, pd, replicas, "A", "sfA", l, m, k)
 
     def step(i):
         r = replicas[i % reps]
-        if tuned:
+        if args.packed:
+            pd.nvfp4_gemm_smalln_launch_packed(r["A_packed"], r["sfA_packed"], r["B"], r["sfB"],
+                                               r["alpha"], c, l, m, n, k, out_type,
+                                               tuning if tuned else None, sptr)
+        elif tuned:
             pd.nvfp4_gemm_smalln_launch_tuned(r["A"], r["sfA"], r["B"], r["sfB"], r["alpha"], c, l, m,
                                               n, k, out_type, tuning, ws, ws_bytes, sptr)
         else:
             pd.nvfp4_gemm_smalln_launch(r["A"], r["sfA"], r["B"], r["sfB"], r["alpha"], c, l, m, n, k,
                                         out_type, sptr)
 
-    print(f"[bench] plan path={plan.path} variant={plan.variant} ksplit={plan.ksplit}; "
+    print(f"[bench] plan path={plan.path} variant={plan.variant} ksplit={plan.ksplit}"
+          f"{' (row-major plan; packed weights)' if args.packed else ''}; "
           f"{reps} replicas ({reps * nbytes / 1e9:.2f} GB)", flush=True)
     ms_step, gbs = timed_steps(args, timer, step, nbytes, "smalln")
     run_copies(torch, args.copy_mib)
@@ -507,11 +534,15 @@ def bench_smalln(args, torch, np, pd, workloads):
                      "l": l, "m": m, "n": n, "k": k, "out": "bf16" if out_type else "f16",
                      "bytes_per_step": nbytes, "replicas": reps,
                      "operands": "HBM (rotated over >= 1 GB of copies)",
-                     "plan": {"path": plan.path, "variant": plan.variant, "ksplit": plan.ksplit}}
+                     "plan": {"path": plan.path, "variant": plan.variant, "ksplit": plan.ksplit},
+                     "weights": "packed once by nvfp4_mma_pack_weight (not timed)" if args.packed
+                                else "row-major"}
+    if args.packed:
+        del out["config"]["plan"]
     # the plan's kernel: matrix cores (mma_stream) or VALU row tiles (vec_tile)
-    valu = plan.path == pd.NVFP4_GEMV_PATH_FAST and \
+    valu = not args.packed and plan.path == pd.NVFP4_GEMV_PATH_FAST and \
         pd.nvfp4_mma_variant_form(plan.variant) == pd.NVFP4_MMA_FORM_VALU_TILES
-    kernel = "vec_tile" if valu else "mma_stream"
+    kernel = "mma_stream_packed" if args.packed else "vec_tile" if valu else "mma_stream"
     extra = {} if valu else {"mfma_tflops": flops / (ms_step * 1e-3) / 1e12}
     out["roofline"] = roofline(gbs, recorded_traffic(cfg.name, kernel), kernel=kernel, **extra)
     out["cpu_baseline"] = with_speedup(cpu, gbs)
@@ -535,11 +566,19 @@ def bench_grouped(args, torch, np, pd, workloads):
     sptr = stream.cuda_stream
     timer = Timer(torch, stream)
     tuning = {"variant": args.variant}
+    if args.packed:
+        pack_replicas(torch, pd, replicas, "W", "sfW", E, n, k)
 
     def step(i):
         r = replicas[i % reps]
-        pd.nvfp4_grouped_gemv_launch_tuned(r["X"], r["sfX"], r["W"], r["sfW"], r["offsets"], r["gs_x"],
-                                           r["gs_w"], c, T, E, n, k, out_type, tuning, sptr)
+        if args.packed:
+            pd.nvfp4_grouped_gemv_launch_packed(r["X"], r["sfX"], r["W_packed"], r["sfW_packed"],
+                                                r["offsets"], r["gs_x"], r["gs_w"], c, T, E, n, k,
+                                                out_type, tuning, sptr)
+        else:
+            pd.nvfp4_grouped_gemv_launch_tuned(r["X"], r["sfX"], r["W"], r["sfW"], r["offsets"],
+                                               r["gs_x"], r["gs_w"], c, T, E, n, k, out_type, tuning,
+                                               sptr)
 
     print(f"[bench] variant={args.variant or 'default'}; {reps} replicas "
           f"({reps * nbytes / 1e9:.2f} GB)", flush=True)
@@ -569,8 +608,11 @@ def bench_grouped(args, torch, np, pd, workloads):
                                  f"({cfg.note})",
                      "experts": E, "active_experts": active, "n": n, "k": k, "tokens": T,
                      "out": "bf16" if out_type else "f16", "bytes_per_step": nbytes,
-                     "replicas": reps, "operands": "HBM (rotated over >= 1 GB of copies)"}
-    out["roofline"] = roofline(gbs, recorded_traffic(cfg.name, "mma_stream"))
+                     "replicas": reps, "operands": "HBM (rotated over >= 1 GB of copies)",
+                     "weights": "packed once by nvfp4_mma_pack_weight (not timed)" if args.packed
+                                else "row-major"}
+    out["roofline"] = roofline(gbs, recorded_traffic(
+        cfg.name, "mma_stream_packed" if args.packed else "mma_stream"))
     out["cpu_baseline"] = with_speedup(cpu, gbs)
     return out
 

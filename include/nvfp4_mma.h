@@ -163,6 +163,64 @@ int nvfp4_grouped_gemv_launch_tuned(const uint8_t *X_packed, const uint8_t *sfX,
                                     int64_t experts, int64_t n, int64_t k, int32_t out_type,
                                     const nvfp4_mma_tuning_t *tuning, void *stream);
 
+/*
+ * Packed weights.  The matrix cores take a weight tile as 16 rows x 32 K
+ * elements spread over the 16-lane groups of a wave, so read from the
+ * row-major layout each load instruction covers 16 rows x 64 bytes.  Weights
+ * are static in inference, so they can be re-laid out once, offline, in the
+ * order the kernel's lanes read them; every load instruction then reads 1 KiB
+ * of contiguous memory.  This is the same idea as the pages' 128 x 4 scale
+ * swizzle for the library GEMM ("nvFP4 Batch GEMV算子系列(下)", section
+ * "关键的to_blocked函数理解"), applied to the codes and scales of the weight.
+ *
+ * Layout, for `groups` matrices of rows x k (codes [groups][rows][k/2],
+ * scales [groups][rows][k/16] as above): tile t holds rows 16t .. 16t+15 and
+ * window w holds elements 256w .. 256w+255.  With T = ceil(rows/16) tiles
+ * and Wn = ceil(k/256) windows per tile, block b = (g T + t) Wn + w is 2048
+ * code bytes at 2048 b and 256 scale bytes at 256 b.  In a block, lane
+ * l = i + 16 q (i < 16, q < 4) owns
+ *   code bytes 16 l and 1024 + 16 l: bytes 128 w + 32 q .. +15 and
+ *     128 w + 32 q + 16 .. +15 of row 16t + i's codes;
+ *   scale bytes 4 l .. 4 l + 3: bytes 16 w + 4 q .. +3 of row 16t + i's scales.
+ * Rows past `rows` and elements past k are zero.
+ *
+ * nvfp4_mma_packed_sizes: bytes of the packed codes and scales (NVFP4_GEMV_OK,
+ * or BAD_SHAPE unless k % 64 == 0, k <= 2^26 and the sizes fit).
+ *
+ * nvfp4_mma_pack_weight: writes that layout from W / sW to W_packed /
+ * sW_packed (device buffers of those sizes; codes 16-byte aligned, scales
+ * 4-byte aligned, no overlap with the inputs or each other).  One kernel on
+ * `stream`; nothing is allocated.
+ *
+ * nvfp4_gemm_smalln_launch_packed / nvfp4_grouped_gemv_launch_packed: the
+ * small-N GEMM and the grouped GEMV above, with the weights in the packed
+ * layout and the vectors (B, X) as before.  Results are bit-identical to the
+ * row-major calls with the same plan.  `tuning` may be NULL; it selects a
+ * matrix-core variant (a VALU row-tile variant is BAD_TUNING), a K split
+ * (small-N only; splits fall on window boundaries) and rows_per_block, which
+ * must be a multiple of 16 (0 = the variant's tiles).  The shape and
+ * alignment rules are the fast kernels' (k % 64 == 0, k <= 2^26, 16-byte
+ * codes, 4-byte scales): there is no generic path for packed weights, so
+ * other shapes are BAD_SHAPE and misaligned pointers ALIGNMENT.  The small-N
+ * call takes its split-K partials from the library's per-(device, stream)
+ * workspace, as nvfp4_gemm_smalln_launch does.
+ */
+int nvfp4_mma_packed_sizes(int64_t groups, int64_t rows, int64_t k, size_t *codes_bytes,
+                           size_t *scales_bytes);
+int nvfp4_mma_pack_weight(const uint8_t *W, const uint8_t *sW, int64_t groups, int64_t rows,
+                          int64_t k, uint8_t *W_packed, uint8_t *sW_packed, void *stream);
+int nvfp4_gemm_smalln_launch_packed(const uint8_t *A_packed, const uint8_t *sfA_packed,
+                                    const uint8_t *B_packed, const uint8_t *sfB,
+                                    const float *alpha, uint16_t *c, int64_t l, int64_t m,
+                                    int64_t n, int64_t k, int32_t out_type,
+                                    const nvfp4_mma_tuning_t *tuning, void *stream);
+int nvfp4_grouped_gemv_launch_packed(const uint8_t *X_packed, const uint8_t *sfX,
+                                     const uint8_t *W_packed, const uint8_t *sfW_packed,
+                                     const int32_t *offsets, const float *gs_x, const float *gs_w,
+                                     uint16_t *c, int64_t tokens, int64_t experts, int64_t n,
+                                     int64_t k, int32_t out_type, const nvfp4_mma_tuning_t *tuning,
+                                     void *stream);
+
 #ifdef __cplusplus
 }
 #endif

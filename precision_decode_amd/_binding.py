@@ -62,6 +62,10 @@ EXPORTED = (
     "nvfp4_gemm_smalln_launch_tuned",
     "nvfp4_grouped_gemv_launch",
     "nvfp4_grouped_gemv_launch_tuned",
+    "nvfp4_mma_packed_sizes",
+    "nvfp4_mma_pack_weight",
+    "nvfp4_gemm_smalln_launch_packed",
+    "nvfp4_grouped_gemv_launch_packed",
 )
 
 
@@ -152,6 +156,15 @@ def load():
     lib.nvfp4_grouped_gemv_launch.argtypes = grouped_args + [_P]
     lib.nvfp4_grouped_gemv_launch_tuned.restype = ctypes.c_int
     lib.nvfp4_grouped_gemv_launch_tuned.argtypes = grouped_args + [ctypes.POINTER(MmaTuning), _P]
+    lib.nvfp4_mma_packed_sizes.restype = ctypes.c_int
+    lib.nvfp4_mma_packed_sizes.argtypes = [_I64, _I64, _I64, ctypes.POINTER(ctypes.c_size_t),
+                                           ctypes.POINTER(ctypes.c_size_t)]
+    lib.nvfp4_mma_pack_weight.restype = ctypes.c_int
+    lib.nvfp4_mma_pack_weight.argtypes = [_P, _P, _I64, _I64, _I64, _P, _P, _P]
+    lib.nvfp4_gemm_smalln_launch_packed.restype = ctypes.c_int
+    lib.nvfp4_gemm_smalln_launch_packed.argtypes = smalln_args + [ctypes.POINTER(MmaTuning), _P]
+    lib.nvfp4_grouped_gemv_launch_packed.restype = ctypes.c_int
+    lib.nvfp4_grouped_gemv_launch_packed.argtypes = grouped_args + [ctypes.POINTER(MmaTuning), _P]
     _lib = lib
     return lib
 
@@ -338,6 +351,39 @@ def nvfp4_grouped_gemv_launch_tuned(X_packed, sfX, W_packed, sfW, offsets, gs_x,
                                                   _ptr(c), tokens, experts, n, k, int(out_type),
                                                   _mma_tuning(tuning), _stream(stream)),
            "nvfp4_grouped_gemv_launch_tuned")
+
+
+def nvfp4_mma_packed_sizes(groups, rows, k):
+    """(codes bytes, scales bytes) of packed weights for groups matrices of rows x k."""
+    cb, sb = ctypes.c_size_t(), ctypes.c_size_t()
+    _check(load().nvfp4_mma_packed_sizes(groups, rows, k, ctypes.byref(cb), ctypes.byref(sb)),
+           "nvfp4_mma_packed_sizes")
+    return int(cb.value), int(sb.value)
+
+
+def nvfp4_mma_pack_weight(W, sW, groups, rows, k, W_packed, sW_packed, stream=None):
+    _check(load().nvfp4_mma_pack_weight(_ptr(W), _ptr(sW), groups, rows, k, _ptr(W_packed),
+                                        _ptr(sW_packed), _stream(stream)), "nvfp4_mma_pack_weight")
+
+
+def nvfp4_gemm_smalln_launch_packed(A_packed, sfA_packed, B_packed, sfB, alpha, c, l, m, n, k,
+                                    out_type=NVFP4_OUT_F16, tuning=None, stream=None):
+    _check(load().nvfp4_gemm_smalln_launch_packed(_ptr(A_packed), _ptr(sfA_packed), _ptr(B_packed),
+                                                  _ptr(sfB), _ptr(alpha), _ptr(c), l, m, n, k,
+                                                  int(out_type), _mma_tuning(tuning),
+                                                  _stream(stream)),
+           "nvfp4_gemm_smalln_launch_packed")
+
+
+def nvfp4_grouped_gemv_launch_packed(X_packed, sfX, W_packed, sfW_packed, offsets, gs_x, gs_w, c,
+                                     tokens, experts, n, k, out_type=NVFP4_OUT_BF16, tuning=None,
+                                     stream=None):
+    _check(load().nvfp4_grouped_gemv_launch_packed(_ptr(X_packed), _ptr(sfX), _ptr(W_packed),
+                                                   _ptr(sfW_packed), _ptr(offsets), _ptr(gs_x),
+                                                   _ptr(gs_w), _ptr(c), tokens, experts, n, k,
+                                                   int(out_type), _mma_tuning(tuning),
+                                                   _stream(stream)),
+           "nvfp4_grouped_gemv_launch_packed")
 
 
 def quantize_activation(x, global_scale, rule=NVFP4_ROUND_HALF_STEP, stream=None):

@@ -58,6 +58,12 @@ constexpr int64_t kComputeUnits = 256;            // CUs of an MI355X (8 XCDs x 
 constexpr int kReduceThreads = 256;
 constexpr int kGenericWaves = 4;
 constexpr int64_t kSliceElems = 2048;   // VALU tiles: K elements of one slice, 1 KiB of a row
+// Packed weights (nvfp4_mma_pack_weight): one window of one 16-row tile is
+// 2 KiB of codes (two 1 KiB halves, 16 bytes per lane) and 256 bytes of
+// scales (4 per lane), in the order the lanes of mma_stream read them.
+constexpr int kPackedWinBytes = 2048;
+constexpr int kPackedWinScaleBytes = 256;
+constexpr int kPackThreads = 256;
 
 struct MmaArgs {
     const uint8_t *W, *sW;      // weights [groups][rows][k/2], scales [groups][rows][k/16]
@@ -149,7 +155,7 @@ __device__ __forceinline__ void decode32(u32x4 q, uint32_t s2, f16x8 (&o)[4]) {
 // vectors, so lane i + 16q ends with rows 4q .. 4q+3, vector i.  Grouped: the
 // operands swap, so lane i + 16q ends with tokens 4q .. 4q+3, row i, and the
 // 16 lanes of a quarter write 16 consecutive outputs of a token.
-template <int R, int U, int W, bool GROUPED>
+template <int R, int U, int W, bool GROUPED, bool PACKED>
 __global__ void __launch_bounds__(W * kWave) mma_stream(const MmaArgs a) {
     __shared__ f32x4 red[(W > 1 ? W - 1 : 1) * R * kWave];
     const int lane = threadIdx.x & (kWave - 1);
@@ -179,10 +185,22 @@ __global__ void __launch_bounds__(W * kWave) mma_stream(const MmaArgs a) {
 
     const int64_t row0 = rb * a.rows_per_block;
     const int64_t nrows = (a.rows - row0 < a.rows_per_block) ? a.rows - row0 : a.rows_per_block;
+    // Packed weights: the group's 16-row tiles one after another, each as its
+    // windows one after another (2 KiB of codes, 256 bytes of scales each);
+    // rows_per_block is a multiple of 16, so the workgroup starts on a tile.
+    const int64_t pwin = (k + kWinElems - 1) / kWinElems;           // windows per tile
+    const int64_t ptiles = (a.rows + kTile - 1) / kTile;            // tiles per group
+    const int64_t tile0 = grp * ptiles + row0 / kTile;
+    const int ntile = static_cast<int>((nrows + kTile - 1) / kTile);
     const __amdgpu_buffer_rsrc_t wdesc =
-        buffer_of(a.W + (grp * a.rows + row0) * (k / 2), static_cast<int>(nrows * (k / 2)));
+        PACKED ? buffer_of(a.W + tile0 * pwin * kPackedWinBytes,
+                           static_cast<int>(ntile * pwin * kPackedWinBytes))
+               : buffer_of(a.W + (grp * a.rows + row0) * (k / 2), static_cast<int>(nrows * (k / 2)));
     const __amdgpu_buffer_rsrc_t swdesc =
-        buffer_of(a.sW + (grp * a.rows + row0) * (k / 16), static_cast<int>(nrows * (k / 16)));
+        PACKED ? buffer_of(a.sW + tile0 * pwin * kPackedWinScaleBytes,
+                           static_cast<int>(ntile * pwin * kPackedWinScaleBytes))
+               : buffer_of(a.sW + (grp * a.rows + row0) * (k / 16),
+                           static_cast<int>(nrows * (k / 16)));
     const float al = group_alpha(a, grp, GROUPED);
 
     for (int64_t vp = v0; vp < v1; vp += kTile) {
@@ -201,13 +219,24 @@ __global__ void __launch_bounds__(W * kWave) mma_stream(const MmaArgs a) {
             const uint32_t so = static_cast<uint32_t>(kk / 16);
 #pragma unroll
             for (int r = 0; r < R; ++r) {
-                const uint32_t row = static_cast<uint32_t>(r * kTile + li);
-                const uint32_t o = in ? row * half + ko : kOutOfRange;
-                const uint32_t os = in ? row * sixteenth + so : kOutOfRange;
+                uint32_t o, os, hstep;
+                if (PACKED) {
+                    // window kk / 256 of tile r: the lane's 16-byte pieces at
+                    // 16 lane and 1024 + 16 lane, its scale word at 4 lane
+                    const uint32_t wi = static_cast<uint32_t>(r * pwin + kk / kWinElems);
+                    o = in ? wi * kPackedWinBytes + 16 * lane : kOutOfRange;
+                    os = in ? wi * kPackedWinScaleBytes + 4 * lane : kOutOfRange;
+                    hstep = kPackedWinBytes / 2;
+                } else {
+                    const uint32_t row = static_cast<uint32_t>(r * kTile + li);
+                    o = in ? row * half + ko : kOutOfRange;
+                    os = in ? row * sixteenth + so : kOutOfRange;
+                    hstep = 16;
+                }
 #pragma unroll
                 for (int h = 0; h < 2; ++h)
                     wq[u][r][h] = __builtin_bit_cast(
-                        u32x4, __builtin_amdgcn_raw_buffer_load_b128(wdesc, o + 16 * h, 0, kNonTemporal));
+                        u32x4, __builtin_amdgcn_raw_buffer_load_b128(wdesc, o + hstep * h, 0, kNonTemporal));
                 ws[u][r] = __builtin_amdgcn_raw_buffer_load_b32(swdesc, os, 0, 0);
             }
             const uint32_t o = in ? static_cast<uint32_t>(li) * half + ko : kOutOfRange;
@@ -480,6 +509,45 @@ __global__ void __launch_bounds__(W * kWave) vec_tile(const MmaArgs a) {
     }
 }
 
+// ---------------------------------------------------------------- weight packing
+// W [groups][rows][k/2] and sW [groups][rows][k/16] -> the packed layout:
+// for tile t (rows 16t .. 16t+15 of a group) and window w (elements 256w ..
+// 256w+255), chunk h (0, 1) of lane l = i + 16q holds bytes 128w + 32q + 16h
+// .. +15 of row 16t + i, at ((t * windows + w) * 2 + h) * 1024 + 16 l; its
+// scale word holds scale bytes 16w + 4q .. +3 of the same row, at
+// (t * windows + w) * 256 + 4 l.  Rows past `rows` and elements past k are
+// zero.  One thread per 16-byte chunk of codes (and per 4-byte scale word).
+__global__ void __launch_bounds__(kPackThreads)
+mma_pack_weight(const uint8_t *__restrict__ W, const uint8_t *__restrict__ sW,
+                uint8_t *__restrict__ Wp, uint8_t *__restrict__ sWp, int64_t groups,
+                int64_t rows, int64_t k) {
+    const int64_t wins = (k + kWinElems - 1) / kWinElems;
+    const int64_t tiles = (rows + kTile - 1) / kTile;
+    const int64_t chunks = groups * tiles * wins * (kPackedWinBytes / 16);
+    const int64_t c = static_cast<int64_t>(blockIdx.x) * kPackThreads + threadIdx.x;
+    if (c >= chunks) return;
+    const int lane = static_cast<int>(c % kWave);
+    const int h = static_cast<int>((c / kWave) % 2);
+    const int64_t tw = c / (2 * kWave);                // (group, tile, window)
+    const int64_t w = tw % wins;
+    const int64_t gt = tw / wins;                      // group * tiles + tile
+    const int64_t g = gt / tiles, t = gt % tiles;
+    const int64_t row = t * kTile + (lane & (kTile - 1));
+    const int q = lane >> 4;
+    const int64_t byte = w * (kWinElems / 2) + 32 * q + 16 * h;   // within the row's k/2 codes
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (row < rows && byte < k / 2)
+        v = *reinterpret_cast<const u32x4 *>(W + (g * rows + row) * (k / 2) + byte);
+    *reinterpret_cast<u32x4 *>(Wp + c * 16) = v;
+    if (h == 0) {
+        const int64_t sbyte = w * (kWinElems / 16) + 4 * q;
+        uint32_t sv = 0u;
+        if (row < rows && sbyte < k / 16)
+            sv = *reinterpret_cast<const uint32_t *>(sW + (g * rows + row) * (k / 16) + sbyte);
+        *reinterpret_cast<uint32_t *>(sWp + tw * kPackedWinScaleBytes + 4 * lane) = sv;
+    }
+}
+
 // ---------------------------------------------------------------- generic kernel
 // Any k % 16 == 0 and any byte alignment.  One wave per (group, weight row);
 // lanes take 16-element blocks; bytes are loaded singly; vectors one by one.
@@ -577,19 +645,19 @@ constexpr int kDefaultGrouped = 3;
 
 typedef void (*MmaKernel)(const MmaArgs);
 
-template <bool G>
+template <bool G, bool P>
 MmaKernel fast_kernel(int v) {
     switch (v) {
-    case 0: return mma_stream<1, 2, 4, G>;
-    case 1: return mma_stream<1, 2, 8, G>;
-    case 2: return mma_stream<2, 2, 4, G>;
-    case 3: return mma_stream<2, 1, 8, G>;
-    case 4: return mma_stream<1, 3, 4, G>;
-    case 5: return mma_stream<2, 2, 8, G>;
-    case 6: return vec_tile<4, 2, 4, G>;
-    case 7: return vec_tile<8, 2, 4, G>;
-    case 8: return vec_tile<4, 4, 4, G>;
-    case 9: return vec_tile<8, 4, 4, G>;
+    case 0: return mma_stream<1, 2, 4, G, P>;
+    case 1: return mma_stream<1, 2, 8, G, P>;
+    case 2: return mma_stream<2, 2, 4, G, P>;
+    case 3: return mma_stream<2, 1, 8, G, P>;
+    case 4: return mma_stream<1, 3, 4, G, P>;
+    case 5: return mma_stream<2, 2, 8, G, P>;
+    case 6: return P ? nullptr : vec_tile<4, 2, 4, G>;
+    case 7: return P ? nullptr : vec_tile<8, 2, 4, G>;
+    case 8: return P ? nullptr : vec_tile<4, 4, 4, G>;
+    case 9: return P ? nullptr : vec_tile<8, 4, 4, G>;
     default: return nullptr;
     }
 }
@@ -625,7 +693,7 @@ int check_dims(int64_t groups, int64_t rows, int64_t nvec, int64_t k, bool allow
 //    units of an MI355X: a workgroup's time is set by its rows, so equal rows
 //    on every unit beat full tiles on some and idle units elsewhere.
 int make_plan(int64_t groups, int64_t rows, int64_t nvec_per_group, int64_t k, bool aligned,
-              bool grouped, const nvfp4_mma_tuning_t *t, Plan *p) {
+              bool grouped, const nvfp4_mma_tuning_t *t, Plan *p, bool packed = false) {
     nvfp4_mma_tuning_t tun = {NVFP4_GEMV_PATH_AUTO, 0, 0, 0};
     if (t) tun = *t;
     if (tun.path < NVFP4_GEMV_PATH_AUTO || tun.path > NVFP4_GEMV_PATH_GENERIC || tun.variant < 0 ||
@@ -637,6 +705,12 @@ int make_plan(int64_t groups, int64_t rows, int64_t nvec_per_group, int64_t k, b
         (tun.variant != 0 || tun.ksplit > 1 || tun.rows_per_block != 0))
         return NVFP4_GEMV_ERR_BAD_TUNING;
     if (grouped && tun.ksplit > 1) return NVFP4_GEMV_ERR_BAD_TUNING;
+    // Packed weights: matrix-core variants only, whole tiles per workgroup,
+    // K splits on window boundaries.
+    if (packed && (!fast_ok || tun.path == NVFP4_GEMV_PATH_GENERIC ||
+                   (tun.variant > 0 && kVariants[tun.variant - 1].form != kMatrixCores) ||
+                   tun.rows_per_block % kTile != 0))
+        return NVFP4_GEMV_ERR_BAD_TUNING;
     const bool fast = tun.path != NVFP4_GEMV_PATH_GENERIC && fast_ok;
     p->path = fast ? NVFP4_GEMV_PATH_FAST : NVFP4_GEMV_PATH_GENERIC;
     if (!fast) {
@@ -653,6 +727,8 @@ int make_plan(int64_t groups, int64_t rows, int64_t nvec_per_group, int64_t k, b
             p->variant = tun.variant - 1;
         } else if (grouped) {
             p->variant = kDefaultGrouped;
+        } else if (packed) {
+            p->variant = kDefaultSmallN;
         } else {
             const int64_t tiles = groups * ceil_div(rows, int64_t(kVariants[kDefaultSmallNFew].R));
             p->variant = (nvec_per_group <= kFewVectors && tiles >= 4 * kComputeUnits)
@@ -683,14 +759,15 @@ int make_plan(int64_t groups, int64_t rows, int64_t nvec_per_group, int64_t k, b
             const int64_t most = k / (int64_t(v.W) * kWinElems);
             while (wg1 * ks < kComputeUnits && ks * 2 <= most) ks *= 2;
         }
-        if (ks > k / kLaneElems) return NVFP4_GEMV_ERR_BAD_TUNING;
-        const int64_t kchunk = ceil_div(ceil_div(k, ks), kLaneElems) * kLaneElems;
+        const int64_t granule = packed ? kWinElems : kLaneElems;
+        if (ks > ceil_div(k, granule)) return NVFP4_GEMV_ERR_BAD_TUNING;
+        const int64_t kchunk = ceil_div(ceil_div(k, ks), granule) * granule;
         p->ksplit = ceil_div(k, kchunk);
         p->kchunk = kchunk;
         int64_t rpb = tile_rows;
         if (tun.rows_per_block > 0) {
             rpb = tun.rows_per_block;
-        } else {
+        } else if (!packed) {
             const int64_t wg = groups * ceil_div(rows, tile_rows) * p->ksplit;
             if (wg < 8 * kComputeUnits) {
                 const int64_t target = ceil_div(wg, kComputeUnits) * kComputeUnits;
@@ -722,14 +799,16 @@ bool aligned_ptrs(const void *w, const void *sw, const void *v, const void *sv) 
     return al(w, 16) && al(v, 16) && al(sw, 4) && al(sv, 4);
 }
 
-int launch(const Plan &p, bool grouped, MmaArgs a, hipStream_t stream) {
+int launch(const Plan &p, bool grouped, MmaArgs a, hipStream_t stream, bool packed = false) {
     a.kchunk = p.kchunk;
     a.row_blocks = p.row_blocks;
     a.rows_per_block = p.rows_per_block;
     const void *fn;
     if (p.path == NVFP4_GEMV_PATH_FAST)
-        fn = reinterpret_cast<const void *>(grouped ? fast_kernel<true>(p.variant)
-                                                    : fast_kernel<false>(p.variant));
+        fn = reinterpret_cast<const void *>(
+            grouped ? (packed ? fast_kernel<true, true>(p.variant) : fast_kernel<true, false>(p.variant))
+                    : (packed ? fast_kernel<false, true>(p.variant)
+                              : fast_kernel<false, false>(p.variant)));
     else
         fn = reinterpret_cast<const void *>(grouped ? mma_generic<true> : mma_generic<false>);
     void *args[] = {&a};
@@ -751,9 +830,32 @@ int launch(const Plan &p, bool grouped, MmaArgs a, hipStream_t stream) {
     return NVFP4_GEMV_OK;
 }
 
+// Bytes of the packed codes and scales of `groups` matrices of rows x k
+// (whole 16-row tiles and 256-element windows); false if they overflow.
+bool packed_sizes(int64_t groups, int64_t rows, int64_t k, int64_t *codes, int64_t *scales) {
+    const int64_t tiles = ceil_div(rows, int64_t(kTile)), wins = ceil_div(k, int64_t(kWinElems));
+    if (!fits_int64_product(groups, tiles) || !fits_int64_product(groups * tiles, wins) ||
+        !fits_int64_product(groups * tiles * wins, kPackedWinBytes))
+        return false;
+    *codes = groups * tiles * wins * kPackedWinBytes;
+    *scales = groups * tiles * wins * kPackedWinScaleBytes;
+    return true;
+}
+
+// Shape and pointer rules of the packed launches: the fast kernel's (k % 64,
+// k <= 2^26, 16-byte codes, 4-byte scales), since packed weights have no
+// generic path.
+int check_packed(int64_t groups, int64_t rows, int64_t k, const void *Wp, const void *sWp,
+                 const void *V, const void *sV, int64_t *codes, int64_t *scales) {
+    if (k % 64 != 0 || k > kMaxFastK || !packed_sizes(groups, rows, k, codes, scales))
+        return NVFP4_GEMV_ERR_BAD_SHAPE;
+    if (!aligned_ptrs(Wp, sWp, V, sV)) return NVFP4_GEMV_ERR_ALIGNMENT;
+    return NVFP4_GEMV_OK;
+}
+
 int validate_smalln(const uint8_t *A, const uint8_t *sfA, const uint8_t *B, const uint8_t *sfB,
                     const float *alpha, uint16_t *c, int64_t l, int64_t m, int64_t n, int64_t k,
-                    int32_t out_type) {
+                    int32_t out_type, bool packed = false) {
     if (!A || !sfA || !B || !sfB || !c) return NVFP4_GEMV_ERR_NULL_POINTER;
     if (out_type != NVFP4_OUT_F16 && out_type != NVFP4_OUT_BF16) return NVFP4_GEMV_ERR_BAD_ARGUMENT;
     int s = check_dims(l, m, n, k, false);
@@ -763,9 +865,13 @@ int validate_smalln(const uint8_t *A, const uint8_t *sfA, const uint8_t *B, cons
         return NVFP4_GEMV_ERR_BAD_SHAPE;
     if (reinterpret_cast<uintptr_t>(c) % 2 != 0 || reinterpret_cast<uintptr_t>(alpha) % 4 != 0)
         return NVFP4_GEMV_ERR_ALIGNMENT;
+    int64_t ab = l * m * (k / 2), sb = l * m * (k / 16);
+    if (packed) {
+        s = check_packed(l, m, k, A, sfA, B, sfB, &ab, &sb);
+        if (s != NVFP4_GEMV_OK) return s;
+    }
     const size_t cn = static_cast<size_t>(l * m * n) * 2;
-    if (overlaps(c, cn, A, static_cast<size_t>(l * m) * (k / 2)) ||
-        overlaps(c, cn, sfA, static_cast<size_t>(l * m) * (k / 16)) ||
+    if (overlaps(c, cn, A, static_cast<size_t>(ab)) || overlaps(c, cn, sfA, static_cast<size_t>(sb)) ||
         overlaps(c, cn, B, static_cast<size_t>(l * n) * (k / 2)) ||
         overlaps(c, cn, sfB, static_cast<size_t>(l * n) * (k / 16)) ||
         overlaps(c, cn, alpha, static_cast<size_t>(l) * 4))
@@ -775,7 +881,8 @@ int validate_smalln(const uint8_t *A, const uint8_t *sfA, const uint8_t *B, cons
 
 int validate_grouped(const uint8_t *X, const uint8_t *sfX, const uint8_t *W, const uint8_t *sfW,
                      const int32_t *offsets, const float *gs_x, const float *gs_w, uint16_t *c,
-                     int64_t tokens, int64_t experts, int64_t n, int64_t k, int32_t out_type) {
+                     int64_t tokens, int64_t experts, int64_t n, int64_t k, int32_t out_type,
+                     bool packed = false) {
     if (!X || !sfX || !W || !sfW || !offsets || !c) return NVFP4_GEMV_ERR_NULL_POINTER;
     if (out_type != NVFP4_OUT_F16 && out_type != NVFP4_OUT_BF16) return NVFP4_GEMV_ERR_BAD_ARGUMENT;
     int s = check_dims(experts, n, tokens, k, true);
@@ -784,11 +891,15 @@ int validate_grouped(const uint8_t *X, const uint8_t *sfX, const uint8_t *W, con
         return NVFP4_GEMV_ERR_BAD_SHAPE;
     auto mis = [](const void *p, uintptr_t a) { return reinterpret_cast<uintptr_t>(p) % a != 0; };
     if (mis(c, 2) || mis(offsets, 4) || mis(gs_x, 4) || mis(gs_w, 4)) return NVFP4_GEMV_ERR_ALIGNMENT;
+    int64_t wb = experts * n * (k / 2), swb = experts * n * (k / 16);
+    if (packed) {
+        s = check_packed(experts, n, k, W, sfW, X, sfX, &wb, &swb);
+        if (s != NVFP4_GEMV_OK) return s;
+    }
     const size_t cn = static_cast<size_t>(tokens * n) * 2;
     if (overlaps(c, cn, X, static_cast<size_t>(tokens) * (k / 2)) ||
         overlaps(c, cn, sfX, static_cast<size_t>(tokens) * (k / 16)) ||
-        overlaps(c, cn, W, static_cast<size_t>(experts * n) * (k / 2)) ||
-        overlaps(c, cn, sfW, static_cast<size_t>(experts * n) * (k / 16)) ||
+        overlaps(c, cn, W, static_cast<size_t>(wb)) || overlaps(c, cn, sfW, static_cast<size_t>(swb)) ||
         overlaps(c, cn, offsets, static_cast<size_t>(experts) * 4) ||
         overlaps(c, cn, gs_x, static_cast<size_t>(experts) * 4) ||
         overlaps(c, cn, gs_w, static_cast<size_t>(experts) * 4))
@@ -896,6 +1007,98 @@ int nvfp4_gemm_smalln_launch(const uint8_t *A_packed, const uint8_t *sfA, const 
     return launch(p, false,
                   smalln_args(A_packed, sfA, B_packed, sfB, alpha, c, l, m, n, k, out_type, part),
                   static_cast<hipStream_t>(stream));
+}
+
+int nvfp4_mma_packed_sizes(int64_t groups, int64_t rows, int64_t k, size_t *codes_bytes,
+                           size_t *scales_bytes) {
+    if (!codes_bytes || !scales_bytes) return NVFP4_GEMV_ERR_NULL_POINTER;
+    int s = check_dims(groups, rows, 1, k, false);
+    if (s != NVFP4_GEMV_OK) return s;
+    int64_t cb, sb;
+    if (k % 64 != 0 || k > kMaxFastK || !packed_sizes(groups, rows, k, &cb, &sb))
+        return NVFP4_GEMV_ERR_BAD_SHAPE;
+    *codes_bytes = static_cast<size_t>(cb);
+    *scales_bytes = static_cast<size_t>(sb);
+    return NVFP4_GEMV_OK;
+}
+
+int nvfp4_mma_pack_weight(const uint8_t *W, const uint8_t *sW, int64_t groups, int64_t rows,
+                          int64_t k, uint8_t *W_packed, uint8_t *sW_packed, void *stream) {
+    if (!W || !sW || !W_packed || !sW_packed) return NVFP4_GEMV_ERR_NULL_POINTER;
+    int s = check_dims(groups, rows, 1, k, false);
+    if (s != NVFP4_GEMV_OK) return s;
+    int64_t cb, sb;
+    s = check_packed(groups, rows, k, W_packed, sW_packed, W, sW, &cb, &sb);
+    if (s != NVFP4_GEMV_OK) return s;
+    const size_t wb = static_cast<size_t>(groups * rows * (k / 2));
+    const size_t swb = static_cast<size_t>(groups * rows * (k / 16));
+    const void *outs[2] = {W_packed, sW_packed};
+    const size_t outn[2] = {static_cast<size_t>(cb), static_cast<size_t>(sb)};
+    for (int i = 0; i < 2; ++i)
+        if (overlaps(outs[i], outn[i], W, wb) || overlaps(outs[i], outn[i], sW, swb))
+            return NVFP4_GEMV_ERR_ALIAS;
+    if (overlaps(W_packed, outn[0], sW_packed, outn[1])) return NVFP4_GEMV_ERR_ALIAS;
+    const int64_t blocks = ceil_div(cb / 16, int64_t(kPackThreads));
+    if (blocks >= (int64_t(1) << 31)) return NVFP4_GEMV_ERR_BAD_SHAPE;
+    void *args[] = {&W, &sW, &W_packed, &sW_packed, &groups, &rows, &k};
+    const hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(mma_pack_weight),
+                                         dim3(static_cast<uint32_t>(blocks)), dim3(kPackThreads),
+                                         args, 0, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? NVFP4_GEMV_OK : NVFP4_GEMV_ERR_LAUNCH;
+}
+
+int nvfp4_gemm_smalln_launch_packed(const uint8_t *A_packed, const uint8_t *sfA_packed,
+                                    const uint8_t *B_packed, const uint8_t *sfB,
+                                    const float *alpha, uint16_t *c, int64_t l, int64_t m,
+                                    int64_t n, int64_t k, int32_t out_type,
+                                    const nvfp4_mma_tuning_t *tuning, void *stream) {
+    int s = validate_smalln(A_packed, sfA_packed, B_packed, sfB, alpha, c, l, m, n, k, out_type,
+                            true);
+    if (s != NVFP4_GEMV_OK) return s;
+    Plan p;
+    s = make_plan(l, m, n, k, true, false, tuning, &p, true);
+    if (s != NVFP4_GEMV_OK) return s;
+    float *part = nullptr;
+    if (p.ws_bytes > 0) {
+        int dev = -1;
+        if (hipGetDevice(&dev) != hipSuccess) return NVFP4_GEMV_ERR_DEVICE;
+        part = static_cast<float *>(nvfp4_stream_workspace(dev, stream, p.ws_bytes));
+        if (!part) return NVFP4_GEMV_ERR_WORKSPACE;
+    }
+    return launch(p, false,
+                  smalln_args(A_packed, sfA_packed, B_packed, sfB, alpha, c, l, m, n, k, out_type,
+                              part),
+                  static_cast<hipStream_t>(stream), true);
+}
+
+int nvfp4_grouped_gemv_launch_packed(const uint8_t *X_packed, const uint8_t *sfX,
+                                     const uint8_t *W_packed, const uint8_t *sfW_packed,
+                                     const int32_t *offsets, const float *gs_x, const float *gs_w,
+                                     uint16_t *c, int64_t tokens, int64_t experts, int64_t n,
+                                     int64_t k, int32_t out_type, const nvfp4_mma_tuning_t *tuning,
+                                     void *stream) {
+    int s = validate_grouped(X_packed, sfX, W_packed, sfW_packed, offsets, gs_x, gs_w, c, tokens,
+                             experts, n, k, out_type, true);
+    if (s != NVFP4_GEMV_OK) return s;
+    Plan p;
+    s = make_plan(experts, n, 0, k, true, true, tuning, &p, true);
+    if (s != NVFP4_GEMV_OK) return s;
+    if (tokens == 0) return NVFP4_GEMV_OK;
+    MmaArgs a = {};
+    a.W = W_packed;
+    a.sW = sfW_packed;
+    a.V = X_packed;
+    a.sV = sfX;
+    a.offsets = offsets;
+    a.gs_v = gs_x;
+    a.gs_w = gs_w;
+    a.c = c;
+    a.groups = experts;
+    a.rows = n;
+    a.nvec = tokens;
+    a.k = k;
+    a.out_bf16 = out_type == NVFP4_OUT_BF16;
+    return launch(p, true, a, static_cast<hipStream_t>(stream), true);
 }
 
 int nvfp4_grouped_gemv_launch_tuned(const uint8_t *X_packed, const uint8_t *sfX,

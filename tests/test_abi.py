@@ -403,3 +403,62 @@ def test_smalln_default_form_by_vector_count(lib):
     for l, m, n, k in ((1, 7168, 3, 16384), (1, 7168, 16, 16384), (1, 256, 2, 16384)):
         t, _ = pd.nvfp4_gemm_smalln_plan(l, m, n, k)
         assert pd.nvfp4_mma_variant_form(t.variant) == pd.NVFP4_MMA_FORM_MATRIX_CORES, (l, m, n, k)
+
+
+# ---------------------------------------------------------------- packed weights
+WP, SWP = 0x80000000, 0x90000000
+
+
+def test_packed_sizes(lib):
+    cb, sb = pd.nvfp4_mma_packed_sizes(1, 7168, 16384)        # 448 tiles x 64 windows
+    assert (cb, sb) == (448 * 64 * 2048, 448 * 64 * 256)
+    assert cb == 7168 * 16384 // 2 and sb == 7168 * 16384 // 16   # whole tiles and windows: no padding
+    cb, sb = pd.nvfp4_mma_packed_sizes(3, 33, 320)             # 3 tiles (33 rows), 2 windows (320)
+    assert (cb, sb) == (3 * 3 * 2 * 2048, 3 * 3 * 2 * 256)
+    for bad in ((1, 16, 48), (1, 16, 96), (1, 16, 2 ** 26 + 64), (0, 16, 64), (1, 0, 64), (1, 16, 0)):
+        with pytest.raises(pd.Nvfp4GemvError):
+            pd.nvfp4_mma_packed_sizes(*bad)
+    assert lib.nvfp4_mma_packed_sizes(1, 16, 64, None, None) == pd.NVFP4_GEMV_ERR_NULL_POINTER
+
+
+def pcall(W=A, sW=SA, groups=2, rows=20, k=128, Wp=WP, sWp=SWP):
+    return pd.load().nvfp4_mma_pack_weight(W, sW, groups, rows, k, Wp, sWp, None)
+
+
+def test_pack_weight_validation(lib):
+    for kw in ("W", "sW", "Wp", "sWp"):
+        assert pcall(**{kw: None}) == pd.NVFP4_GEMV_ERR_NULL_POINTER, kw
+    for groups, rows, k in ((0, 20, 128), (2, 0, 128), (2, 20, 96), (2, 20, 40)):
+        assert pcall(groups=groups, rows=rows, k=k) == pd.NVFP4_GEMV_ERR_BAD_SHAPE
+    assert pcall(W=A + 8) == pd.NVFP4_GEMV_ERR_ALIGNMENT
+    assert pcall(Wp=WP + 8) == pd.NVFP4_GEMV_ERR_ALIGNMENT
+    assert pcall(sW=SA + 2) == pd.NVFP4_GEMV_ERR_ALIGNMENT
+    assert pcall(sWp=SWP + 2) == pd.NVFP4_GEMV_ERR_ALIGNMENT
+    assert pcall(Wp=A + 16) == pd.NVFP4_GEMV_ERR_ALIAS             # output over the input codes
+    assert pcall(sWp=SA) == pd.NVFP4_GEMV_ERR_ALIAS
+    assert pcall(sWp=WP + 1024) == pd.NVFP4_GEMV_ERR_ALIAS          # the two outputs overlap
+
+
+def test_packed_launch_validation(lib):
+    f = pd.load().nvfp4_gemm_smalln_launch_packed
+    g = pd.load().nvfp4_grouped_gemv_launch_packed
+
+    def s(k=128, A_=A, tuning=None, **kw):
+        t = ctypes.byref(_binding.MmaTuning(*tuning)) if tuning else None
+        return f(A_, SA, B_, SB_, AL, C, 1, 64, 4, k, 0, t, None)
+
+    def gr(k=128, tuning=None):
+        t = ctypes.byref(_binding.MmaTuning(*tuning)) if tuning else None
+        return g(X, SX, A, SA, OF, GX, GW, C, 8, 3, 32, k, 1, t, None)
+
+    assert s(k=96) == pd.NVFP4_GEMV_ERR_BAD_SHAPE                  # packed: k % 64 == 0, no generic path
+    assert gr(k=96) == pd.NVFP4_GEMV_ERR_BAD_SHAPE
+    assert s(A_=A + 8) == pd.NVFP4_GEMV_ERR_ALIGNMENT
+    assert f(None, SA, B_, SB_, AL, C, 1, 64, 4, 128, 0, None, None) == pd.NVFP4_GEMV_ERR_NULL_POINTER
+    assert f(C, SA, B_, SB_, AL, C, 1, 64, 4, 128, 0, None, None) == pd.NVFP4_GEMV_ERR_ALIAS
+    valu = [v for v in range(1, pd.nvfp4_mma_num_variants() + 1)
+            if pd.nvfp4_mma_variant_form(v) == pd.NVFP4_MMA_FORM_VALU_TILES]
+    for bad in ((0, valu[0], 0, 0), (2, 0, 0, 0), (0, 1, 0, 8), (0, 3, 0, 24), (0, 1, 0, 48)):
+        assert s(tuning=bad) == pd.NVFP4_GEMV_ERR_BAD_TUNING, bad   # VALU, generic, partial tiles
+        assert gr(tuning=bad) == pd.NVFP4_GEMV_ERR_BAD_TUNING, bad
+    assert gr(tuning=(0, 1, 2, 0)) == pd.NVFP4_GEMV_ERR_BAD_TUNING   # the grouped call never splits K

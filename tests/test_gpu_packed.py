@@ -1,0 +1,180 @@
+"""GPU checks of the packed-weight calls: nvfp4_mma_pack_weight writes the
+layout that include/nvfp4_mma.h defines (byte for byte, against a numpy
+re-layout written from that definition), and the small-N GEMM and grouped GEMV
+on packed weights match the CPU oracle on the row-major weights bit for bit
+(integer-coded inputs), for every matrix-core variant, K splits, ragged rows
+and K not a multiple of the 256-element window."""
+import numpy as np
+import pytest
+import torch
+
+import precision_decode_amd as pd
+import workloads
+from gpu_util import assert_bits_equal, to_device
+from oracle import multi
+
+pytestmark = [pytest.mark.gpu, pytest.mark.filterwarnings("ignore::RuntimeWarning")]
+
+FMT = {pd.NVFP4_OUT_F16: "f16", pd.NVFP4_OUT_BF16: "bf16"}
+FILL = 0xFFFF
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu_ready():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    pd.load()
+
+
+def matrix_core_variants():
+    return [v for v in range(1, pd.nvfp4_mma_num_variants() + 1)
+            if pd.nvfp4_mma_variant_form(v) == pd.NVFP4_MMA_FORM_MATRIX_CORES]
+
+
+def relayout(W, sW, groups, rows, k):
+    """The packed layout of the header, from its definition: block
+    (g, t, w) of 2048 code bytes and 256 scale bytes; lane l = i + 16 q holds
+    code bytes 128 w + 32 q .. +31 of row 16 t + i (two 16-byte halves at 16 l
+    and 1024 + 16 l) and scale bytes 16 w + 4 q .. +3 at 4 l."""
+    tiles, wins = -(-rows // 16), -(-k // 256)
+    Wz = np.zeros((groups, tiles * 16, wins * 128), np.uint8)
+    Sz = np.zeros((groups, tiles * 16, wins * 16), np.uint8)
+    Wz[:, :rows, :k // 2] = W.reshape(groups, rows, k // 2)
+    Sz[:, :rows, :k // 16] = sW.reshape(groups, rows, k // 16)
+    codes = np.zeros((groups, tiles, wins, 2, 64, 16), np.uint8)
+    scales = np.zeros((groups, tiles, wins, 64, 4), np.uint8)
+    for lane in range(64):
+        i, q = lane % 16, lane // 16
+        for w in range(wins):
+            for h in range(2):
+                b = 128 * w + 32 * q + 16 * h
+                codes[:, :, w, h, lane, :] = Wz[:, i::16, b:b + 16]
+            sb = 16 * w + 4 * q
+            scales[:, :, w, lane, :] = Sz[:, i::16, sb:sb + 4]
+    return codes.reshape(-1), scales.reshape(-1)
+
+
+def pack(W, sW, groups, rows, k):
+    cb, sb = pd.nvfp4_mma_packed_sizes(groups, rows, k)
+    Wp = torch.full((cb,), 0xAB, dtype=torch.uint8, device="cuda")   # poisoned: every byte is written
+    sWp = torch.full((sb,), 0xAB, dtype=torch.uint8, device="cuda")
+    pd.nvfp4_mma_pack_weight(W, sW, groups, rows, k, Wp, sWp)
+    torch.cuda.synchronize()
+    return Wp, sWp
+
+
+@pytest.mark.parametrize("groups,rows,k", [(1, 16, 256), (2, 75, 2112), (3, 33, 64), (1, 7168, 16384),
+                                           (5, 20, 576)])
+def test_pack_layout_matches_the_definition(groups, rows, k):
+    ops = workloads.integer_coded(groups, rows, k, seed=groups + rows + k)
+    d = to_device(ops)
+    Wp, sWp = pack(d["A"], d["sfA"], groups, rows, k)
+    want_c, want_s = relayout(ops["A"], ops["sfA"], groups, rows, k)
+    assert Wp.numel() == want_c.size and sWp.numel() == want_s.size
+    assert np.array_equal(Wp.cpu().numpy(), want_c)
+    assert np.array_equal(sWp.cpu().numpy(), want_s)
+
+
+# ---------------------------------------------------------------- small-N GEMM
+def smalln_ops(l, m, n, k, seed=0):
+    a = workloads.integer_coded(l, m, k, seed=seed, alpha="uniform")
+    b = workloads.integer_coded(l, n, k, seed=seed + 1)
+    return {"A": a["A"], "sfA": a["sfA"], "B": b["A"], "sfB": b["sfA"], "alpha": a["alpha"]}
+
+
+def run_smalln_packed(ops, l, m, n, k, out_type=pd.NVFP4_OUT_F16, tuning=None):
+    d = to_device(ops)
+    Ap, sAp = pack(d["A"], d["sfA"], l, m, k)
+    c = torch.full((l, m, n), -1, dtype=torch.int16, device="cuda")
+    pd.nvfp4_gemm_smalln_launch_packed(Ap, sAp, d["B"], d["sfB"], d["alpha"], c, l, m, n, k, out_type,
+                                       tuning)
+    torch.cuda.synchronize()
+    return c.cpu().numpy().view(np.uint16)
+
+
+def oracle_smalln(ops, l, m, n, k, out_type=pd.NVFP4_OUT_F16):
+    return multi.gemm_smalln(ops["A"], ops["sfA"], ops["B"], ops["sfB"], ops["alpha"], l, m, n, k,
+                             FMT[out_type])
+
+
+@pytest.mark.parametrize("ksplit", [0, 1, 3])
+def test_smalln_packed_every_variant(ksplit):
+    l, m, n, k = 2, 75, 11, 2112        # ragged rows, k = 8 windows + 64 elements
+    ops = smalln_ops(l, m, n, k, seed=31 + ksplit)
+    want = oracle_smalln(ops, l, m, n, k, pd.NVFP4_OUT_BF16)
+    for v in matrix_core_variants():
+        tuning = {"variant": v, "ksplit": ksplit}
+        got = run_smalln_packed(ops, l, m, n, k, pd.NVFP4_OUT_BF16, tuning)
+        assert_bits_equal(got, want, f"packed v{v} ks{ksplit}", "bf16")
+
+
+@pytest.mark.parametrize("l,m,n,k", [(1, 7168, 16, 16384), (1, 7168, 4, 16384), (3, 40, 1, 64),
+                                     (2, 130, 17, 1024)])
+def test_smalln_packed_default_plan(l, m, n, k):
+    ops = smalln_ops(l, m, n, k, seed=l + m + n + k)
+    assert_bits_equal(run_smalln_packed(ops, l, m, n, k), oracle_smalln(ops, l, m, n, k),
+                      f"packed {(l, m, n, k)}")
+
+
+@pytest.mark.parametrize("rows_per_block", [16, 32])
+def test_smalln_packed_rows_per_block(rows_per_block):
+    l, m, n, k = 1, 100, 5, 1280
+    ops = smalln_ops(l, m, n, k, seed=41)
+    for v in matrix_core_variants():
+        r, _, _ = pd.nvfp4_mma_variant_info(v)
+        if rows_per_block > 16 * r:
+            continue
+        got = run_smalln_packed(ops, l, m, n, k, tuning={"variant": v, "rows_per_block": rows_per_block})
+        assert_bits_equal(got, oracle_smalln(ops, l, m, n, k), f"packed v{v} rpb {rows_per_block}")
+
+
+# ---------------------------------------------------------------- grouped GEMV
+def grouped_ops(counts, n, k, seed=0):
+    experts, tokens = len(counts), int(sum(counts))
+    w = workloads.integer_coded(experts, n, k, seed=seed)
+    x = workloads.integer_coded(1, max(tokens, 1), k, seed=seed + 1)
+    rng = np.random.default_rng(seed + 2)
+    return {"X": x["A"][0][:max(tokens, 1)], "sfX": x["sfA"][0][:max(tokens, 1)], "W": w["A"],
+            "sfW": w["sfA"], "offsets": np.cumsum(counts).astype(np.int32),
+            "gs_x": rng.uniform(0.5, 2, experts).astype(np.float32),
+            "gs_w": rng.uniform(0.5, 2, experts).astype(np.float32)}
+
+
+def run_grouped_packed(ops, tokens, experts, n, k, out_type=pd.NVFP4_OUT_BF16, tuning=None):
+    d = to_device(ops)
+    Wp, sWp = pack(d["W"], d["sfW"], experts, n, k)
+    c = torch.full((max(tokens, 1), n), FILL - 65536, dtype=torch.int16, device="cuda")
+    pd.nvfp4_grouped_gemv_launch_packed(d["X"], d["sfX"], Wp, sWp, d["offsets"], d["gs_x"], d["gs_w"],
+                                        c, tokens, experts, n, k, out_type, tuning)
+    torch.cuda.synchronize()
+    return c.cpu().numpy().view(np.uint16)[:tokens]
+
+
+def oracle_grouped(ops, tokens, experts, n, k, out_type=pd.NVFP4_OUT_BF16):
+    return multi.grouped_gemv(ops["X"], ops["sfX"], ops["W"], ops["sfW"], ops["offsets"],
+                              ops["gs_x"], ops["gs_w"], tokens, experts, n, k, FMT[out_type],
+                              fill=FILL)
+
+
+@pytest.mark.parametrize("counts,n,k", [
+    ([3, 0, 1, 5], 40, 256),
+    ([0, 0, 37], 17, 2112),
+    ([16, 16], 33, 512),
+    ([2, 1, 0, 0, 4, 9], 96, 1088),
+])
+def test_grouped_packed_every_variant(counts, n, k):
+    ops = grouped_ops(counts, n, k, seed=sum(counts) + n)
+    tokens, experts = int(sum(counts)), len(counts)
+    want = oracle_grouped(ops, tokens, experts, n, k)
+    for v in [0] + matrix_core_variants():
+        got = run_grouped_packed(ops, tokens, experts, n, k, tuning={"variant": v})
+        assert_bits_equal(got, want, f"packed {counts} n={n} k={k} v={v}", "bf16")
+
+
+def test_grouped_packed_moe_decode():
+    cfg = workloads.MOE_CONFIGS["moe_decode"]
+    ops = workloads.moe_operands(cfg)
+    for out_type in (pd.NVFP4_OUT_F16, pd.NVFP4_OUT_BF16):
+        want = oracle_grouped(ops, cfg.tokens, cfg.experts, cfg.n, cfg.k, out_type)
+        got = run_grouped_packed(ops, cfg.tokens, cfg.experts, cfg.n, cfg.k, out_type)
+        assert_bits_equal(got, want, f"packed moe_decode {FMT[out_type]}", FMT[out_type])
