@@ -64,7 +64,8 @@ def parse_args(argv=None):
     p.add_argument("--path", default="gemv",
                    choices=["gemv", "quantize", "gemv_bf16x", "smalln", "grouped"])
     p.add_argument("--config", default="decode",
-                   help="integer-coded workload name from workloads.CONFIGS")
+                   help="GEMV workload from workloads.CONFIGS (decode, batched, shortk, tiny, or "
+                        "gaussian: bf16 draws quantised by the library's device quantiser, untimed)")
     p.add_argument("--act-config", default="tokens",
                    help="activation workload of --path quantize (workloads.ACT_CONFIGS)")
     p.add_argument("--smalln-config", default="decode_n16",
@@ -251,18 +252,43 @@ def cpu_time(fn, runs=3):
 
 
 # ------------------------------------------------------------------------------------ GEMV
+def quantize_gaussian_on_device(torch, np, pd, raw, l, m, k):
+    """NVFP4 operands of a Gaussian workload, quantised by the library's device
+    weight quantiser (before any timing): each batch's A[b] and x[b] is a
+    tensor of its own with its amax global scale, nearest-even codes, and
+    alpha[b] = f32(gA[b] * gx[b])."""
+    rule = pd.NVFP4_ROUND_NEAREST_EVEN
+    out = {}
+    scales = {}
+    for name, rows in (("A", m), ("x", 1)):
+        src = torch.from_numpy(np.ascontiguousarray(raw[name])).to(torch.bfloat16).cuda()
+        codes = torch.empty((l, rows, k // 2), dtype=torch.uint8, device="cuda")
+        sf = torch.empty((l, rows, k // 16), dtype=torch.uint8, device="cuda")
+        g = torch.empty(l, dtype=torch.float32, device="cuda")
+        pd.nvfp4_quantize_weight(src, l, rows, k, rule, codes, sf, g)
+        shape = (l, m) if name == "A" else (l,)
+        out[name] = codes.reshape(*shape, k // 2)
+        out["sf" + name] = sf.reshape(*shape, k // 16)
+        scales[name] = g
+    out["alpha"] = scales["A"] * scales["x"]     # one fp32 rounding, as the workload defines
+    torch.cuda.synchronize()
+    return out
+
+
 def bench_gemv(args, torch, np, pd, workloads):
     cfg = workloads.CONFIGS[args.config]
-    if cfg.kind != "integer":
-        print(f"{cfg.name} is not an integer-coded workload; bench it with an integer config",
-              file=sys.stderr)
-        return None
     l, m, k = cfg.l, cfg.m, cfg.k
     nbytes = cfg.bytes_moved
     print(f"[bench] workload {cfg.name}: l={l} m={m} k={k}, {nbytes} bytes per step", flush=True)
 
-    ops = workloads.for_config(cfg)
-    base = {n: torch.from_numpy(np.ascontiguousarray(v)).cuda() for n, v in ops.items()}
+    if cfg.kind == "integer":
+        raw = None
+        ops = workloads.for_config(cfg)
+        base = {n: torch.from_numpy(np.ascontiguousarray(v)).cuda() for n, v in ops.items()}
+    else:
+        raw = workloads.gaussian_bf16(l, m, k, seed=cfg.seed)
+        base = quantize_gaussian_on_device(torch, np, pd, raw, l, m, k)
+        print("[bench] Gaussian operands quantised on the device (not timed)", flush=True)
     replicas, reps = replicate(torch, base, nbytes, args.replicas)
     c = torch.empty((l, m), dtype=torch.int16, device="cuda")
     stream = torch.cuda.current_stream()
@@ -322,9 +348,20 @@ def bench_gemv(args, torch, np, pd, workloads):
     run_copies(torch, args.copy_mib)
 
     cpu = None
+    quantised = None
     if not args.no_cpu_baseline:
         from oracle import reference as ref
 
+        if raw is not None:
+            # the oracle's own quantisation of the same draws, byte for byte
+            from oracle import quantize as oq
+
+            ops = oq.gaussian_operands(raw, l, m, k)
+            quantised = all(np.array_equal(base[n].cpu().numpy().reshape(ops[n].shape), ops[n])
+                            for n in ("A", "sfA", "x", "sfx")) and \
+                np.array_equal(base["alpha"].cpu().numpy().view(np.uint32), ops["alpha"].view(np.uint32))
+            print(f"[bench] device-quantised operands identical to the oracle's: {quantised}",
+                  flush=True)
         threads = ref.default_threads()
         results = []
         t_med = cpu_time(lambda: results.append(ref.gemv(ops["A"], ops["sfA"], ops["x"], ops["sfx"],
@@ -339,13 +376,16 @@ def bench_gemv(args, torch, np, pd, workloads):
                "seconds": round(t_med, 4),
                "elements_per_s_per_core": round(l * m * k / t_med / threads, 1),
                "parity": parity}
+        if quantised is not None:
+            cpu["quantised_operands_identical"] = quantised
         print(f"[bench] CPU oracle: {t_med:.3f}s per GEMV on {threads} threads", flush=True)
 
     out = {"metric": "achieved HBM GB/s for the NVFP4 block-scaled batched GEMV (us/call and % of "
                      "MI355X peak alongside)"}
     out.update(common_fields(args, gbs, ms_step, "f32"))
-    out["config"] = {"workload": f"{cfg.name}: NVFP4 GEMV l={l} m={m} k={k}, integer-coded, "
-                                 f"alpha=1 ({cfg.note})",
+    inputs = {"one": "integer-coded, alpha=1", "uniform": "integer-coded, alpha U[0.5,2]",
+              "quantizer": "bf16 N(0,1) quantised on the device, alpha = gA*gx"}[cfg.alpha]
+    out["config"] = {"workload": f"{cfg.name}: NVFP4 GEMV l={l} m={m} k={k}, {inputs} ({cfg.note})",
                      "l": l, "m": m, "k": k, "bytes_per_step": nbytes,
                      "replicas": reps, "operands": "HBM (rotated over >= 1 GB of copies)",
                      "plan": {"path": plan.path, "variant": plan.variant, "ksplit": plan.ksplit}}
