@@ -99,11 +99,6 @@ __device__ __forceinline__ void decode_x32(u32x4 xv, uint32_t s2, u32x4 (&out)[4
                    bits(e2m1x2_f16<2>(xv.w) * v1), bits(e2m1x2_f16<3>(xv.w) * v1)};
 }
 
-__device__ __forceinline__ u32x4 load_nt16(const uint8_t *p) {
-    return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
-}
-
-
 // (row block, batch, split) of this workgroup, row block fastest.  The plan
 // keeps the workgroup count below 2^31, so 32-bit division suffices (much
 // shorter than 64-bit division, which every workgroup would run first).
@@ -738,19 +733,32 @@ gemv_splitk_reduce(const float *__restrict__ part, const float *__restrict__ alp
 }
 
 // ---------------------------------------------------------------- read probe
+// Reads n16 16-byte units once, in rounds of 8 loads per thread that are all
+// in flight together: in round r, thread t of the grid loads units
+// r * 8S + t + jS (j < 8, S = the grid's thread count), so every wave
+// instruction reads 1 KiB contiguously.  Each round's loads go through a
+// descriptor over that round's units, so loads past the end read zeros and
+// need no branch or serial tail; round offsets stay below 2^31 bytes.
+constexpr int kProbeLoads = 8;
+
 __global__ void __launch_bounds__(kProbeThreads)
 hbm_read_probe(const uint8_t *__restrict__ buf, int64_t n16, uint32_t *__restrict__ sink) {
     const int64_t stride = static_cast<int64_t>(gridDim.x) * kProbeThreads;
-    int64_t i = static_cast<int64_t>(blockIdx.x) * kProbeThreads + threadIdx.x;
+    const int64_t round = kProbeLoads * stride;
+    const uint32_t t = blockIdx.x * kProbeThreads + threadIdx.x;
     u32x4 acc = {0u, 0u, 0u, 0u};
-    for (; i + 7 * stride < n16; i += 8 * stride) {
-        u32x4 v[8];
+    for (int64_t base = 0; base < n16; base += round) {
+        const int64_t len = (n16 - base < round) ? n16 - base : round;
+        const __amdgpu_buffer_rsrc_t rs = buffer_of(buf + base * 16, static_cast<int>(len * 16));
+        u32x4 v[kProbeLoads];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) v[j] = load_nt16(buf + (i + j * stride) * 16);
+        for (int j = 0; j < kProbeLoads; ++j)
+            v[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                 rs, (t + j * static_cast<uint32_t>(stride)) * 16u, 0,
+                                                 kNonTemporal));
 #pragma unroll
-        for (int j = 0; j < 8; ++j) acc ^= v[j];
+        for (int j = 0; j < kProbeLoads; ++j) acc ^= v[j];
     }
-    for (; i < n16; i += stride) acc ^= load_nt16(buf + i * 16);
     uint32_t w = acc.x ^ acc.y ^ acc.z ^ acc.w;
     for (int o = kWave / 2; o >= 1; o >>= 1) w ^= __shfl_xor(w, o, kWave);
     __shared__ uint32_t per_wave[kProbeThreads / kWave];
@@ -1141,7 +1149,8 @@ int nvfp4_hbm_read_probe(const void *buffer, size_t bytes, uint32_t *sink, void 
     if (reinterpret_cast<uintptr_t>(buffer) % 16 != 0 || reinterpret_cast<uintptr_t>(sink) % 4 != 0)
         return NVFP4_GEMV_ERR_ALIGNMENT;
     const int64_t n16 = static_cast<int64_t>(bytes / 16);
-    int64_t groups = ceil_div(n16, int64_t(kProbeThreads) * 4);
+    // enough groups for one round of 8 loads per thread, up to kProbeMaxGroups
+    int64_t groups = ceil_div(n16, int64_t(kProbeThreads) * kProbeLoads);
     if (groups > kProbeMaxGroups) groups = kProbeMaxGroups;
     const uint8_t *buf = static_cast<const uint8_t *>(buffer);
     void *args[] = {&buf, const_cast<int64_t *>(&n16), &sink};

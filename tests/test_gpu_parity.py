@@ -261,10 +261,13 @@ def test_nan_and_negative_scales_and_overflow():
     assert_bits_equal(run_gpu(to_device(big), 1, 16, 4096), want, "overflow")
 
 
-def test_hbm_read_probe_reads_every_byte_once():
-    n = 64 << 20
+@pytest.mark.parametrize("n", [64 << 20, (64 << 20) + 48, 300 << 20, 16])
+def test_hbm_read_probe_reads_every_byte_once(n):
+    """One round of 8 loads per thread, a ragged round, three rounds with a
+    partial last one (the group count capped), and a single unit."""
     data = torch.randint(0, 2 ** 31 - 1, (n // 4,), dtype=torch.int32, device="cuda")
     sink = torch.zeros(4096, dtype=torch.int32, device="cuda")
+    print(f"probe over {n} bytes", flush=True)
     pd.nvfp4_hbm_read_probe(data, n, sink)
     torch.cuda.synchronize()
     want = np.bitwise_xor.reduce(data.cpu().numpy().view(np.uint32))
