@@ -33,6 +33,12 @@
 //    balanced by splitting K across workgroups (small-N GEMM only), with fp32
 //    partials added in split order by a second kernel.
 //
+// Two other forms sit beside it: weights packed once into the order the
+// lanes read them (mma_pack_weight; every load instruction then reads 1 KiB
+// contiguously instead of 16 rows x 64 bytes), and, for one or two vectors,
+// VALU row tiles that read the row-major weights row-contiguously and take
+// the few dot products themselves (vec_tile).
+//
 // Every accumulator starts at +0.0, so an exactly-zero result is +0.  With
 // integer-coded inputs (E2M1 values times scales 0, 1, 2) every partial sum is
 // a multiple of 1/4 below 2^22, exact in fp32 in any order.
