@@ -143,6 +143,35 @@ def test_smalln_special_values_every_variant():
         assert_within_tolerance(got, want, what=f"special values variant {v}")
 
 
+def gaussian_smalln_ops(l, m, n, k, seed):
+    """Gaussian bf16 draws quantised by the oracle, each batch's A and B a
+    tensor of its own, alpha = gA * gB."""
+    rawA = workloads.gaussian_bf16(l, m, k, seed=seed)["A"]
+    rawB = workloads.gaussian_bf16(l, n, k, seed=seed + 1)["A"]
+    ops = {"A": np.empty((l, m, k // 2), np.uint8), "sfA": np.empty((l, m, k // 16), np.uint8),
+           "B": np.empty((l, n, k // 2), np.uint8), "sfB": np.empty((l, n, k // 16), np.uint8),
+           "alpha": np.empty(l, np.float32)}
+    for b in range(l):
+        ops["A"][b], ops["sfA"][b], ga = oq.quantize_nvfp4(rawA[b])
+        ops["B"][b], ops["sfB"][b], gb = oq.quantize_nvfp4(rawB[b])
+        ops["alpha"][b] = np.float32(ga * gb)
+    return ops
+
+
+@pytest.mark.parametrize("n", [1, 2])
+def test_smalln_valu_tiles_gaussian_within_tolerance(n):
+    """One or two vectors on a weight that fills the GPU: the default plan
+    takes the VALU row tiles."""
+    l, m, k = 1, 4096, 4096
+    assert pd.nvfp4_mma_variant_form(pd.nvfp4_gemm_smalln_plan(l, m, n, k)[0].variant) == \
+        pd.NVFP4_MMA_FORM_VALU_TILES
+    ops = gaussian_smalln_ops(l, m, n, k, seed=60 + n)
+    for out_type in (pd.NVFP4_OUT_F16, pd.NVFP4_OUT_BF16):
+        want = oracle_smalln(ops, l, m, n, k, out_type)
+        got = run_smalln(ops, l, m, n, k, out_type)
+        assert_within_tolerance(got, want, what=f"gaussian VALU tiles n={n}", fmt=FMT[out_type])
+
+
 def test_smalln_gaussian_within_tolerance():
     l, m, n, k = 4, 512, 8, 4096
     rawA = workloads.gaussian_bf16(l, m, k, seed=21)["A"]

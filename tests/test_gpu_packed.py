@@ -10,8 +10,9 @@ import torch
 
 import precision_decode_amd as pd
 import workloads
-from gpu_util import assert_bits_equal, to_device
+from gpu_util import assert_bits_equal, assert_within_tolerance, to_device
 from oracle import multi
+from oracle import quantize as oq
 
 pytestmark = [pytest.mark.gpu, pytest.mark.filterwarnings("ignore::RuntimeWarning")]
 
@@ -178,3 +179,33 @@ def test_grouped_packed_moe_decode():
         want = oracle_grouped(ops, cfg.tokens, cfg.experts, cfg.n, cfg.k, out_type)
         got = run_grouped_packed(ops, cfg.tokens, cfg.experts, cfg.n, cfg.k, out_type)
         assert_bits_equal(got, want, f"packed moe_decode {FMT[out_type]}", FMT[out_type])
+
+
+@pytest.mark.parametrize("out_type", [pd.NVFP4_OUT_F16, pd.NVFP4_OUT_BF16])
+def test_smalln_packed_gaussian_within_tolerance(out_type):
+    """Gaussian bf16 draws quantised by the oracle (each batch's A and B a
+    tensor of its own): the packed call agrees with the oracle within the
+    tolerance, and with the row-major call bit for bit."""
+    l, m, n, k = 2, 300, 16, 4096
+    rawA = workloads.gaussian_bf16(l, m, k, seed=71)["A"]
+    rawB = workloads.gaussian_bf16(l, n, k, seed=72)["A"]
+    ops = {"A": np.empty((l, m, k // 2), np.uint8), "sfA": np.empty((l, m, k // 16), np.uint8),
+           "B": np.empty((l, n, k // 2), np.uint8), "sfB": np.empty((l, n, k // 16), np.uint8),
+           "alpha": np.empty(l, np.float32)}
+    for b in range(l):
+        ops["A"][b], ops["sfA"][b], ga = oq.quantize_nvfp4(rawA[b])
+        ops["B"][b], ops["sfB"][b], gb = oq.quantize_nvfp4(rawB[b])
+        ops["alpha"][b] = np.float32(ga * gb)
+    want = oracle_smalln(ops, l, m, n, k, out_type)
+    # the same matrix-core plan for both layouts: variant, K split and whole-tile row blocks
+    tuning = {"variant": 3, "ksplit": 4, "rows_per_block": 32}
+    got = run_smalln_packed(ops, l, m, n, k, out_type, tuning)
+    assert_within_tolerance(got, want, what="gaussian packed small-N", fmt=FMT[out_type])
+    d = to_device(ops)
+    c = torch.full((l, m, n), -1, dtype=torch.int16, device="cuda")
+    _, ws_bytes = pd.nvfp4_gemm_smalln_plan(l, m, n, k, tuning=tuning)
+    ws = torch.empty(max(ws_bytes, 4), dtype=torch.uint8, device="cuda")
+    pd.nvfp4_gemm_smalln_launch_tuned(d["A"], d["sfA"], d["B"], d["sfB"], d["alpha"], c, l, m, n, k,
+                                      out_type, tuning, ws, ws_bytes)
+    torch.cuda.synchronize()
+    assert np.array_equal(got, c.cpu().numpy().view(np.uint16)), "packed and row-major differ"
