@@ -12,7 +12,7 @@ import torch
 
 import precision_decode_amd as pd
 import workloads
-from gpu_util import assert_bits_equal, assert_within_tolerance, to_device
+from gpu_util import assert_bits_equal, assert_within_tolerance, bits_to_f64, to_device
 from oracle import multi
 from oracle import quantize as oq
 
@@ -348,3 +348,56 @@ def test_grouped_rows_per_block(variant, rows_per_block):
     want = oracle_grouped(ops, 22, 4, n, k)
     got = run_grouped(ops, 22, 4, n, k, tuning={"variant": variant, "rows_per_block": rows_per_block})
     assert_bits_equal(got, want, f"grouped v{variant} rpb {rows_per_block}", "bf16")
+
+
+def grouped_special_ops(counts, n, k, seed):
+    """Arbitrary code bytes with every finite scale code (subnormal, negative,
+    up to 448), a NaN scale code planted in one expert's weight row and in one
+    token; per-expert global scales U[0.5, 2]."""
+    experts, tokens = len(counts), int(sum(counts))
+    finite = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+    w = workloads.random_bytes(experts, n, k, seed=seed, scale_codes=finite)
+    x = workloads.random_bytes(1, tokens, k, seed=seed + 1, scale_codes=finite)
+    rng = np.random.default_rng(seed + 2)
+    ops = {"X": x["A"][0], "sfX": x["sfA"][0], "W": w["A"], "sfW": w["sfA"],
+           "offsets": np.cumsum(counts).astype(np.int32),
+           "gs_x": rng.uniform(0.5, 2, experts).astype(np.float32),
+           "gs_w": rng.uniform(0.5, 2, experts).astype(np.float32)}
+    ops["sfW"][1, 3, 2] = 0x7F                     # expert 1, weight row 3
+    ops["sfX"][tokens - 1, 5] = 0xFF               # the last token
+    return ops
+
+
+def test_grouped_special_values_every_variant():
+    """Terms span many binades, so fp32 sums are not exact: the tolerance
+    applies, and NaN positions (a row of an expert, a token) must agree."""
+    counts, n, k = [3, 4, 0, 5], 24, 512
+    ops = grouped_special_ops(counts, n, k, seed=81)
+    tokens, experts = int(sum(counts)), len(counts)
+    for out_type in (pd.NVFP4_OUT_F16, pd.NVFP4_OUT_BF16):
+        want = oracle_grouped(ops, tokens, experts, n, k, out_type)
+        nan = np.isnan(bits_to_f64(want, FMT[out_type]))
+        assert nan[3:7, 3].all() and nan[tokens - 1].all()
+        for v in range(0, pd.nvfp4_mma_num_variants() + 1):
+            got = run_grouped(ops, tokens, experts, n, k, out_type, tuning={"variant": v})
+            assert_within_tolerance(got, want, what=f"grouped special v{v}", fmt=FMT[out_type])
+
+
+def test_grouped_gaussian_within_tolerance():
+    experts, n, k = 6, 256, 2048
+    counts = [3, 0, 1, 2, 5, 1]
+    tokens = int(sum(counts))
+    rawW = workloads.gaussian_bf16(experts, n, k, seed=91)["A"]
+    rawX = workloads.gaussian_bf16(1, tokens, k, seed=92)["A"][0]
+    W = np.empty((experts, n, k // 2), np.uint8)
+    sW = np.empty((experts, n, k // 16), np.uint8)
+    gw = np.empty(experts, np.float32)
+    for e in range(experts):
+        W[e], sW[e], gw[e] = oq.quantize_nvfp4(rawW[e])
+    X, sX, gx = oq.quantize_nvfp4(rawX)          # the tokens as one tensor: one activation scale
+    ops = {"X": X, "sfX": sX, "W": W, "sfW": sW, "offsets": np.cumsum(counts).astype(np.int32),
+           "gs_x": np.full(experts, gx, np.float32), "gs_w": gw}
+    for out_type in (pd.NVFP4_OUT_F16, pd.NVFP4_OUT_BF16):
+        want = oracle_grouped(ops, tokens, experts, n, k, out_type)
+        got = run_grouped(ops, tokens, experts, n, k, out_type)
+        assert_within_tolerance(got, want, what="gaussian grouped", fmt=FMT[out_type])

@@ -209,3 +209,25 @@ def test_smalln_packed_gaussian_within_tolerance(out_type):
                                       out_type, tuning, ws, ws_bytes)
     torch.cuda.synchronize()
     assert np.array_equal(got, c.cpu().numpy().view(np.uint16)), "packed and row-major differ"
+
+
+def test_grouped_packed_special_values_and_clamped_offsets():
+    """Every finite scale code and planted NaN scales through packed weights
+    (tolerance; NaN positions agree), then offsets past the token count
+    (clamped on the device) and a call with no tokens."""
+    from test_gpu_mma import grouped_special_ops
+    counts, n, k = [3, 4, 0, 5], 24, 512
+    ops = grouped_special_ops(counts, n, k, seed=83)
+    tokens, experts = int(sum(counts)), len(counts)
+    for out_type in (pd.NVFP4_OUT_F16, pd.NVFP4_OUT_BF16):
+        want = oracle_grouped(ops, tokens, experts, n, k, out_type)
+        for v in [0] + matrix_core_variants():
+            got = run_grouped_packed(ops, tokens, experts, n, k, out_type, tuning={"variant": v})
+            assert_within_tolerance(got, want, what=f"packed grouped special v{v}", fmt=FMT[out_type])
+    ops = grouped_ops([3, 2], 16, 128, seed=84)
+    ops["offsets"] = np.array([3, 1000], dtype=np.int32)
+    got = run_grouped_packed(ops, 5, 2, 16, 128)
+    ops["offsets"] = np.array([3, 5], dtype=np.int32)
+    assert_bits_equal(got, oracle_grouped(ops, 5, 2, 16, 128), "packed clamped offsets", "bf16")
+    ops = grouped_ops([0, 0], 16, 64, seed=85)
+    assert run_grouped_packed(ops, 0, 2, 16, 64).size == 0
