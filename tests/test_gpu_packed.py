@@ -231,3 +231,40 @@ def test_grouped_packed_special_values_and_clamped_offsets():
     assert_bits_equal(got, oracle_grouped(ops, 5, 2, 16, 128), "packed clamped offsets", "bf16")
     ops = grouped_ops([0, 0], 16, 64, seed=85)
     assert run_grouped_packed(ops, 0, 2, 16, 64).size == 0
+
+
+def test_smalln_packed_split_determinism_and_two_streams():
+    """Gaussian data with a K split: three packed calls give the same bits;
+    then two streams run packed split-K calls on different operands
+    concurrently, each taking its own library workspace."""
+    l, m, n, k = 1, 200, 16, 8192
+    plan = {"ksplit": 4}
+    rawA = workloads.gaussian_bf16(1, m, k, seed=101)["A"][0]
+    rawB = workloads.gaussian_bf16(1, n, k, seed=102)["A"][0]
+    A, sA, _ = oq.quantize_nvfp4(rawA)
+    B, sB, _ = oq.quantize_nvfp4(rawB)
+    ops = {"A": A[None], "sfA": sA[None], "B": B[None], "sfB": sB[None],
+           "alpha": np.ones(1, np.float32)}
+    first = run_smalln_packed(ops, l, m, n, k, tuning=plan)
+    for _ in range(2):
+        assert np.array_equal(run_smalln_packed(ops, l, m, n, k, tuning=plan), first)
+
+    o1 = smalln_ops(l, 448, n, 16384, seed=103)
+    o2 = smalln_ops(l, 448, n, 16384, seed=104)
+    w1, w2 = oracle_smalln(o1, l, 448, n, 16384), oracle_smalln(o2, l, 448, n, 16384)
+    outs = []
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    packed = []
+    for o in (o1, o2):
+        d = to_device(o)
+        Ap, sAp = pack(d["A"], d["sfA"], l, 448, 16384)
+        packed.append((Ap, sAp, d))
+        outs.append(torch.empty((l, 448, n), dtype=torch.int16, device="cuda"))
+    torch.cuda.synchronize()
+    for _ in range(3):
+        for (Ap, sAp, d), c, s in zip(packed, outs, (s1, s2)):
+            pd.nvfp4_gemm_smalln_launch_packed(Ap, sAp, d["B"], d["sfB"], d["alpha"], c, l, 448, n,
+                                               16384, pd.NVFP4_OUT_F16, plan, stream=s)
+    torch.cuda.synchronize()
+    assert_bits_equal(outs[0].cpu().numpy().view(np.uint16), w1, "stream 1")
+    assert_bits_equal(outs[1].cpu().numpy().view(np.uint16), w2, "stream 2")
