@@ -1,9 +1,10 @@
 """Helpers shared by the GPU tests: move inputs to the device, call the HIP
-library through its C ABI, compare fp16 bit patterns."""
+library through its C ABI, compare fp16 bit patterns, build edge-case inputs."""
 import numpy as np
 import torch
 
 import precision_decode_amd as pd
+import workloads
 
 
 def to_device(ops):
@@ -77,3 +78,21 @@ def assert_within_tolerance(got, want, ulps=2, rel=1e-3, what="", fmt="f16"):
         rel_ok = np.abs(g - w) <= rel * np.abs(w)
     ok = ulp_ok | rel_ok | ~fin
     assert ok.all(), f"{what}: {int((~ok).sum())} outputs outside tolerance"
+
+
+def grouped_special_ops(counts, n, k, seed):
+    """Arbitrary code bytes with every finite scale code (subnormal, negative,
+    up to 448), a NaN scale code planted in one expert's weight row and in one
+    token; per-expert global scales U[0.5, 2]."""
+    experts, tokens = len(counts), int(sum(counts))
+    finite = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+    w = workloads.random_bytes(experts, n, k, seed=seed, scale_codes=finite)
+    x = workloads.random_bytes(1, tokens, k, seed=seed + 1, scale_codes=finite)
+    rng = np.random.default_rng(seed + 2)
+    ops = {"X": x["A"][0], "sfX": x["sfA"][0], "W": w["A"], "sfW": w["sfA"],
+           "offsets": np.cumsum(counts).astype(np.int32),
+           "gs_x": rng.uniform(0.5, 2, experts).astype(np.float32),
+           "gs_w": rng.uniform(0.5, 2, experts).astype(np.float32)}
+    ops["sfW"][1, 3, 2] = 0x7F                     # expert 1, weight row 3
+    ops["sfX"][tokens - 1, 5] = 0xFF               # the last token
+    return ops

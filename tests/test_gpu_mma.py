@@ -12,7 +12,8 @@ import torch
 
 import precision_decode_amd as pd
 import workloads
-from gpu_util import assert_bits_equal, assert_within_tolerance, bits_to_f64, to_device
+from gpu_util import (assert_bits_equal, assert_within_tolerance, bits_to_f64,
+                      grouped_special_ops, to_device)
 from oracle import multi
 from oracle import quantize as oq
 
@@ -348,24 +349,6 @@ def test_grouped_rows_per_block(variant, rows_per_block):
     want = oracle_grouped(ops, 22, 4, n, k)
     got = run_grouped(ops, 22, 4, n, k, tuning={"variant": variant, "rows_per_block": rows_per_block})
     assert_bits_equal(got, want, f"grouped v{variant} rpb {rows_per_block}", "bf16")
-
-
-def grouped_special_ops(counts, n, k, seed):
-    """Arbitrary code bytes with every finite scale code (subnormal, negative,
-    up to 448), a NaN scale code planted in one expert's weight row and in one
-    token; per-expert global scales U[0.5, 2]."""
-    experts, tokens = len(counts), int(sum(counts))
-    finite = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
-    w = workloads.random_bytes(experts, n, k, seed=seed, scale_codes=finite)
-    x = workloads.random_bytes(1, tokens, k, seed=seed + 1, scale_codes=finite)
-    rng = np.random.default_rng(seed + 2)
-    ops = {"X": x["A"][0], "sfX": x["sfA"][0], "W": w["A"], "sfW": w["sfA"],
-           "offsets": np.cumsum(counts).astype(np.int32),
-           "gs_x": rng.uniform(0.5, 2, experts).astype(np.float32),
-           "gs_w": rng.uniform(0.5, 2, experts).astype(np.float32)}
-    ops["sfW"][1, 3, 2] = 0x7F                     # expert 1, weight row 3
-    ops["sfX"][tokens - 1, 5] = 0xFF               # the last token
-    return ops
 
 
 def test_grouped_special_values_every_variant():

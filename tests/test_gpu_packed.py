@@ -10,7 +10,7 @@ import torch
 
 import precision_decode_amd as pd
 import workloads
-from gpu_util import assert_bits_equal, assert_within_tolerance, to_device
+from gpu_util import assert_bits_equal, assert_within_tolerance, grouped_special_ops, to_device
 from oracle import multi
 from oracle import quantize as oq
 
@@ -215,7 +215,6 @@ def test_grouped_packed_special_values_and_clamped_offsets():
     """Every finite scale code and planted NaN scales through packed weights
     (tolerance; NaN positions agree), then offsets past the token count
     (clamped on the device) and a call with no tokens."""
-    from test_gpu_mma import grouped_special_ops
     counts, n, k = [3, 4, 0, 5], 24, 512
     ops = grouped_special_ops(counts, n, k, seed=83)
     tokens, experts = int(sum(counts)), len(counts)
