@@ -432,3 +432,27 @@ def gemv(A_packed, sfA, x_packed, sfx, alpha=None, out=None, stream=None):
         raise ValueError("out must be a contiguous 16-bit device tensor of shape (l, m)")
     nvfp4_gemv_launch(A_packed, sfA, x_packed, sfx, alpha, out, l, m, k, stream)
     return out
+
+
+def pack_weight(W, sW, stream=None):
+    """Tensor-level call: W (groups, rows, k/2) and sW (groups, rows, k/16)
+    uint8 device tensors -> (codes, scales), the packed layout of
+    :func:`nvfp4_mma_pack_weight` as flat uint8 device tensors, for
+    :func:`nvfp4_gemm_smalln_launch_packed` and
+    :func:`nvfp4_grouped_gemv_launch_packed`.  A 2-D W is one group."""
+    import torch
+
+    if W.dim() == 2:
+        W, sW = W.unsqueeze(0), sW.unsqueeze(0)
+    if W.dim() != 3:
+        raise ValueError("W must be (groups, rows, k/2) or (rows, k/2)")
+    groups, rows, half = W.shape
+    k = 2 * half
+    for name, t, shape in (("W", W, (groups, rows, half)), ("sW", sW, (groups, rows, k // 16))):
+        if t.dtype != torch.uint8 or tuple(t.shape) != shape or not t.is_contiguous() or not t.is_cuda:
+            raise ValueError(f"{name} must be a contiguous uint8 device tensor of shape {shape}")
+    cb, sb = nvfp4_mma_packed_sizes(groups, rows, k)
+    codes = torch.empty(cb, dtype=torch.uint8, device=W.device)
+    scales = torch.empty(sb, dtype=torch.uint8, device=W.device)
+    nvfp4_mma_pack_weight(W, sW, groups, rows, k, codes, scales, stream)
+    return codes, scales

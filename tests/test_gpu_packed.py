@@ -267,3 +267,18 @@ def test_smalln_packed_split_determinism_and_two_streams():
     torch.cuda.synchronize()
     assert_bits_equal(outs[0].cpu().numpy().view(np.uint16), w1, "stream 1")
     assert_bits_equal(outs[1].cpu().numpy().view(np.uint16), w2, "stream 2")
+
+
+def test_pack_weight_tensor_helper():
+    """The tensor-level helper gives the same bytes as the C call, for a 3-D
+    and a 2-D weight, and rejects a wrong scale shape."""
+    ops = workloads.integer_coded(2, 40, 512, seed=111)
+    d = to_device(ops)
+    codes, scales = pd.pack_weight(d["A"], d["sfA"])
+    want_c, want_s = relayout(ops["A"], ops["sfA"], 2, 40, 512)
+    assert np.array_equal(codes.cpu().numpy(), want_c) and np.array_equal(scales.cpu().numpy(), want_s)
+    c1, s1 = pd.pack_weight(d["A"][1], d["sfA"][1])
+    w1c, w1s = relayout(ops["A"][1:], ops["sfA"][1:], 1, 40, 512)
+    assert np.array_equal(c1.cpu().numpy(), w1c) and np.array_equal(s1.cpu().numpy(), w1s)
+    with pytest.raises(ValueError):
+        pd.pack_weight(d["A"], d["sfA"][:, :, :8])
