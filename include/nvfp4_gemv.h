@@ -73,11 +73,16 @@ const char *nvfp4_gemv_status_string(int status);
  * The batched GEMV above.  Arguments as described in the header comment.
  *
  * When the launch plan splits K across workgroups (few rows, long K) the fp32
- * partial sums go to a workspace that the library allocates on first need and
- * keeps per (device, stream) until the process ends; such a first call is not
- * capture-safe, later calls of the same or smaller size are.  Callers that
- * must not allocate use nvfp4_gemv_launch_ws.  Concurrent calls on different
- * streams never share a workspace.
+ * partial sums go to a workspace that the library owns, one per (device,
+ * stream), kept until the process ends.  A call that needs more than the
+ * stream's workspace holds grows it with hipMalloc: no synchronisation and no
+ * free (the outgrown buffer stays allocated, since work enqueued before may
+ * still read it).  Such a growing call cannot run while `stream` is being
+ * captured into a graph: it then returns NVFP4_GEMV_ERR_WORKSPACE and enqueues
+ * nothing.  Calls that need no more than the workspace holds allocate nothing
+ * and are capture-safe; nvfp4_workspace_reserve sizes the workspace before a
+ * capture.  Callers that must never allocate use nvfp4_gemv_launch_ws.
+ * Concurrent calls on different streams never share a workspace.
  *
  * Returns NVFP4_GEMV_OK or a negative status.
  */
@@ -106,6 +111,18 @@ int nvfp4_gemv_launch_ws(const uint8_t *A_packed, const uint8_t *sfA,
                          const float *alpha, uint16_t *c,
                          int64_t l, int64_t m, int64_t k,
                          void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Grows the library-owned workspace of (current device, `stream`) to at least
+ * `bytes` bytes, so that later calls on `stream` needing no more than that
+ * allocate nothing (for instance under graph capture).  The workspace serves
+ * nvfp4_gemv_launch, nvfp4_gemm_smalln_launch(_packed), nvfp4_quantize_weight
+ * and nvfp4_gemv_bf16x_launch on that stream; take `bytes` from
+ * nvfp4_gemv_workspace_size or the plan calls.  Not capture-safe itself.
+ * Returns NVFP4_GEMV_OK, NVFP4_GEMV_ERR_DEVICE (no current device) or
+ * NVFP4_GEMV_ERR_WORKSPACE (allocation failed, or `stream` is capturing).
+ */
+int nvfp4_workspace_reserve(size_t bytes, void *stream);
 
 /* ---- launch-plan control (tests and tuning sweeps) ---------------------- */
 

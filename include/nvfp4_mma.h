@@ -85,7 +85,9 @@ typedef struct nvfp4_mma_tuning_t {
 /*
  * The small-N GEMM above.  When the plan splits K across workgroups the fp32
  * partial sums go to the library-owned per-(device, stream) workspace of
- * nvfp4_gemv_launch (allocated on first need, kept until the process ends).
+ * nvfp4_gemv_launch (grown on first need without synchronising, kept until
+ * the process ends; a call that must grow it while `stream` is being captured
+ * returns WORKSPACE: see nvfp4_workspace_reserve).
  * Returns NVFP4_GEMV_OK or a negative status (BAD_ARGUMENT for an unknown
  * out_type).
  */

@@ -81,7 +81,8 @@ int nvfp4_quantize_activation(const uint16_t *x_bf16, const float *global_scale,
  * [groups] (float, 4-byte aligned, device) is an output: the weights' global
  * scales for the GEMV's alpha.  Three kernels are enqueued on `stream`; their
  * scratch (groups * 256 bytes + 4 bytes per row) is the library-owned
- * per-(device, stream) workspace of nvfp4_gemv_launch, allocated on first need.
+ * per-(device, stream) workspace of nvfp4_gemv_launch, grown on first need
+ * without synchronising (see nvfp4_workspace_reserve for graph capture).
  * Shape and alignment rules as for nvfp4_quantize_activation over groups*rows
  * rows.  Returns NVFP4_GEMV_OK, NULL_POINTER, BAD_ARGUMENT, BAD_SHAPE,
  * ALIGNMENT, ALIAS, DEVICE, WORKSPACE or LAUNCH.

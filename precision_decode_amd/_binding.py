@@ -51,6 +51,7 @@ EXPORTED = (
     "nvfp4_gemv_plan",
     "nvfp4_gemv_launch_tuned",
     "nvfp4_hbm_read_probe",
+    "nvfp4_workspace_reserve",
     "nvfp4_quantize_activation",
     "nvfp4_quantize_weight",
     "nvfp4_gemv_bf16x_launch",
@@ -125,6 +126,8 @@ def load():
                                     ctypes.POINTER(Tuning), ctypes.POINTER(ctypes.c_size_t)]
     lib.nvfp4_gemv_launch_tuned.restype = ctypes.c_int
     lib.nvfp4_gemv_launch_tuned.argtypes = gemv_args + [ctypes.POINTER(Tuning), _P, ctypes.c_size_t, _P]
+    lib.nvfp4_workspace_reserve.restype = ctypes.c_int
+    lib.nvfp4_workspace_reserve.argtypes = [ctypes.c_size_t, _P]
     lib.nvfp4_hbm_read_probe.restype = ctypes.c_int
     lib.nvfp4_hbm_read_probe.argtypes = [_P, ctypes.c_size_t, _P, _P]
     lib.nvfp4_quantize_activation.restype = ctypes.c_int
@@ -261,6 +264,10 @@ def nvfp4_gemv_launch_tuned(A_packed, sfA, x_packed, sfx, alpha, c, l, m, k, tun
                                         _ptr(alpha), _ptr(c), l, m, k, _tuning(tuning),
                                         _ptr(workspace), int(workspace_bytes), _stream(stream))
     _check(st, "nvfp4_gemv_launch_tuned")
+
+
+def nvfp4_workspace_reserve(nbytes, stream=None):
+    _check(load().nvfp4_workspace_reserve(int(nbytes), _stream(stream)), "nvfp4_workspace_reserve")
 
 
 def nvfp4_hbm_read_probe(buffer, nbytes, sink, stream=None):

@@ -117,10 +117,11 @@ __device__ __forceinline__ float wave_sum(float v) {
 
 }  // namespace nvfp4dev
 
-// Library-owned split-K workspace, one per (device, stream), grown on demand
-// and kept until the process ends (defined in nvfp4_gemv.hip).  Returns NULL
-// when allocation fails.  Growing synchronises `stream` before freeing the
-// old buffer, since earlier work on it may still read it.
+// Library-owned workspace, one per (device, stream), grown on demand and kept
+// until the process ends (defined in nvfp4_gemv.hip).  Returns NULL when the
+// slot must grow and cannot: allocation failed, or the stream is being
+// captured into a graph.  Never synchronises and never frees a buffer that
+// enqueued work may still read.
 __attribute__((visibility("hidden"))) void *nvfp4_stream_workspace(int dev, void *stream,
                                                                     size_t need);
 

@@ -41,21 +41,17 @@
 #include <map>
 #include <mutex>
 #include <utility>
+#include <vector>
 
 #include "device_common.h"
+#include "gemv_plan.h"
 #include "nvfp4_gemv.h"
 
 namespace {
 
 using namespace nvfp4dev;
+using namespace nvfp4plan;
 
-constexpr int64_t kIterElems = 2048;    // K elements one wave covers per row per iteration
-constexpr int64_t kMaxChunk = 16384;    // K elements staged in LDS per workgroup (32 KiB)
-constexpr int64_t kMinSplitChunk = 2048;
-constexpr int64_t kTargetGroups = 512;  // workgroups wanted before splitting K
-constexpr int64_t kComputeUnits = 256;  // MI355X: 8 XCDs x 32 CUs
-constexpr int kReduceThreads = 256;
-constexpr int kGenericWaves = 4;
 constexpr int kProbeThreads = 256;
 constexpr int kProbeMaxGroups = 4096;
 
@@ -772,33 +768,6 @@ hbm_read_probe(const uint8_t *__restrict__ buf, int64_t n16, uint32_t *__restric
 }
 
 // ---------------------------------------------------------------- host side
-// x staging of a fast variant: fp16 x~ in LDS (gemv_fast), packed codes in LDS
-// (gemv_fastp), no staging (gemv_fastg, x read next to A every iteration), or
-// row tiles (16, 8 or 4 rows) whose waves split K and keep x~ of their slice
-// in registers (gemv_tile).
-enum XForm { kXHalf = 0, kXPacked = 1, kXGlobal = 2, kXTile = 3 };
-
-// The row-tile kernel addresses a tile's rows through one descriptor with
-// 32-bit offsets; it takes K up to this bound.
-constexpr int64_t kTileMaxK = int64_t(1) << 26;
-
-struct Variant {
-    int R, U, W;
-    int xform;
-};
-// Listed as {rows per wave, iterations in flight, waves, x staging}.
-constexpr Variant kVariants[] = {
-    {2, 4, 7, kXHalf},    {1, 8, 4, kXHalf},    {2, 4, 4, kXHalf},    {2, 2, 4, kXHalf},
-    {4, 2, 4, kXHalf},    {2, 4, 8, kXHalf},    {1, 8, 8, kXHalf},    {4, 1, 4, kXHalf},
-    {2, 1, 8, kXHalf},    {1, 4, 4, kXHalf},    {2, 2, 4, kXPacked},  {4, 1, 4, kXPacked},
-    {4, 2, 4, kXPacked},  {2, 4, 8, kXPacked},  {4, 2, 8, kXPacked},  {1, 4, 8, kXPacked},
-    {2, 4, 7, kXGlobal},  {2, 2, 7, kXGlobal},  {4, 2, 7, kXGlobal},  {2, 4, 4, kXGlobal},
-    {1, 8, 7, kXGlobal},  {4, 1, 8, kXGlobal},  {16, 1, 8, kXTile},   {16, 1, 4, kXTile},
-    {16, 1, 2, kXTile},   {16, 1, 1, kXTile},   {8, 1, 1, kXTile},    {8, 1, 2, kXTile},
-    {4, 1, 1, kXTile},    {4, 1, 2, kXTile},
-};
-constexpr int kNumVariants = static_cast<int>(sizeof(kVariants) / sizeof(kVariants[0]));
-
 typedef void (*FastKernel)(const uint8_t *, const uint8_t *, const uint8_t *, const uint8_t *,
                            const float *, uint16_t *, float *, int64_t, int64_t, int64_t,
                            int64_t, int64_t);
@@ -839,158 +808,15 @@ FastKernel fast_kernel(int v) {
     }
 }
 
-int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+static_assert(kNumVariants == 30, "fast_kernel() covers every entry of kVariants");
 
-// Default fast variant (0-based) by the number of 1 KiB K-iterations per row
-// of one workgroup's K-range, from MI355X measurements on the decode, batched,
-// Gaussian and short-K workloads: long rows want more rows in flight per
-// workgroup; with 3 to 5 iterations per row x read next to A beats staging it;
-// rows of one or two iterations are best read as row tiles, whose loads are
-// all in flight at once: rows of one iteration as 4-row tiles of one wave
-// (many small waves, little arithmetic left in each when its last load lands),
-// rows of two as 16-row tiles of two waves.
-int default_variant(int64_t k) {
-    const int64_t nit = ceil_div(k < kMaxChunk ? k : kMaxChunk, kIterElems);
-    if (nit >= 6) return 0;    // {2, 4, 7}
-    if (nit >= 3) return 19;   // {2, 4, 4} x read next to A
-    if (nit == 2) return 24;   // 16-row tile, 2 waves
-    return 28;                 // 4-row tile, 1 wave
-}
-
-struct Plan {
-    int path;          // NVFP4_GEMV_PATH_FAST or _GENERIC
-    int variant;       // 0-based fast-kernel variant
-    int64_t ksplit;
-    int64_t kchunk;
-    int64_t row_blocks;     // row blocks per batch
-    int64_t groups;
-    int threads;
-    size_t lds_bytes;
-    size_t ws_bytes;
-};
-
-int check_shape(int64_t l, int64_t m, int64_t k) {
-    if (l < 1 || m < 1 || k < 16 || k % 16 != 0) return NVFP4_GEMV_ERR_BAD_SHAPE;
-    if (k >= (int64_t(1) << 31) || l > INT64_MAX / m || l * m >= (int64_t(1) << 31))
-        return NVFP4_GEMV_ERR_BAD_SHAPE;
-    if (l * m > INT64_MAX / (k / 2)) return NVFP4_GEMV_ERR_BAD_SHAPE;
-    return NVFP4_GEMV_OK;
-}
-
-// K split: one LDS stage (16384 elements) per workgroup at most for the
-// staged fast kernels; an explicit split must leave every split at least one granule (32
-// elements for the fast kernel, 16 for the generic one) and fit one stage.
-int split_k(int64_t k, int64_t ks_req, int64_t ks_auto, int64_t granule, bool staged,
-            int64_t *ks_out, int64_t *kchunk_out) {
-    int64_t ks = ks_req > 0 ? ks_req : ks_auto;
-    if (ks_req > 0 && ks > k / granule) return NVFP4_GEMV_ERR_BAD_TUNING;
-    int64_t kchunk = ceil_div(ceil_div(k, ks), granule) * granule;
-    if (staged && kchunk > kMaxChunk) {
-        if (ks_req > 0) return NVFP4_GEMV_ERR_BAD_TUNING;
-        kchunk = kMaxChunk;
-    }
-    *ks_out = ceil_div(k, kchunk);
-    *kchunk_out = kchunk;
-    return NVFP4_GEMV_OK;
-}
-
-// Resolves the launch plan; shape must already be valid.
-int make_plan(int64_t l, int64_t m, int64_t k, bool aligned, const nvfp4_gemv_tuning_t *t,
-              Plan *p) {
-    nvfp4_gemv_tuning_t tun = {NVFP4_GEMV_PATH_AUTO, 0, 0, 0};
-    if (t) tun = *t;
-    if (tun.reserved != 0 || tun.path < NVFP4_GEMV_PATH_AUTO || tun.path > NVFP4_GEMV_PATH_GENERIC ||
-        tun.variant < 0 || tun.ksplit < 0)
-        return NVFP4_GEMV_ERR_BAD_TUNING;
-    const bool fast_ok = aligned && (k % 32 == 0);
-    if (tun.path == NVFP4_GEMV_PATH_FAST && !fast_ok) return NVFP4_GEMV_ERR_BAD_TUNING;
-    if (tun.path == NVFP4_GEMV_PATH_GENERIC && tun.variant != 0) return NVFP4_GEMV_ERR_BAD_TUNING;
-    if (tun.variant > kNumVariants) return NVFP4_GEMV_ERR_BAD_TUNING;
-    p->path = (tun.path == NVFP4_GEMV_PATH_GENERIC || !fast_ok) ? NVFP4_GEMV_PATH_GENERIC
-                                                                  : NVFP4_GEMV_PATH_FAST;
-    p->variant = tun.variant > 0 ? tun.variant - 1 : default_variant(k);
-
-    int64_t rows_per_group;
-    if (p->path == NVFP4_GEMV_PATH_FAST) {
-        const Variant &v = kVariants[p->variant];
-        if (v.xform == kXTile && k > kTileMaxK) return NVFP4_GEMV_ERR_BAD_TUNING;
-        rows_per_group = v.xform == kXTile ? v.R : static_cast<int64_t>(v.R) * v.W;
-        p->threads = v.W * kWave;
-    } else {
-        p->variant = 0;
-        rows_per_group = kGenericWaves;
-        p->threads = kGenericWaves * kWave;
-    }
-    p->row_blocks = ceil_div(m, rows_per_group);
-    const int64_t groups1 = l * p->row_blocks;
-    const bool fast = p->path == NVFP4_GEMV_PATH_FAST;
-    const int64_t granule = fast ? 32 : 16;
-
-    const int xform = fast ? kVariants[p->variant].xform : -1;
-    const bool staged = xform == kXHalf || xform == kXPacked;
-    int64_t ks_auto = staged ? ceil_div(k, kMaxChunk) : 1;
-    // A tile's waves already split K: split it across workgroups only while
-    // the tiles leave compute units idle, and only as far as every split
-    // keeps a slice for each wave.
-    const int64_t target = xform == kXTile ? kComputeUnits : kTargetGroups;
-    if (groups1 * ks_auto < target) {
-        const int64_t want = ceil_div(target, groups1);
-        int64_t most = xform == kXTile ? ceil_div(k, kIterElems) / kVariants[p->variant].W
-                                       : k / kMinSplitChunk;
-        if (most < 1) most = 1;
-        const int64_t pick = want < most ? want : most;
-        if (pick > ks_auto) ks_auto = pick;
-    }
-    int64_t ks, kchunk;
-    const int st = split_k(k, tun.ksplit, ks_auto, granule, staged, &ks, &kchunk);
-    if (st != NVFP4_GEMV_OK) return st;
-    p->ksplit = ks;
-    p->kchunk = kchunk;
-    p->groups = groups1 * ks;
-    if (p->groups >= (int64_t(1) << 31)) return NVFP4_GEMV_ERR_BAD_SHAPE;
-    if (staged) {
-        const Variant &v = kVariants[p->variant];
-        const int64_t slots = ceil_div(ceil_div(kchunk, kIterElems), v.U) * v.U;
-        // per slot and lane: 64 bytes of fp16 x~, or 16 bytes of codes + 4 of scales
-        p->lds_bytes = static_cast<size_t>(slots) * kWave * (v.xform == kXPacked ? 20 : 64);
-    } else {
-        p->lds_bytes = 0;
-    }
-    p->ws_bytes = ks > 1 ? static_cast<size_t>(ks) * l * m * sizeof(float) : 0;
-    return NVFP4_GEMV_OK;
-}
-
-bool aligned_for_fast(const void *A, const void *sfA, const void *x, const void *sfx) {
-    auto a = [](const void *p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; };
-    return a(A, 16) && a(x, 16) && a(sfA, 2) && a(sfx, 2);
-}
-
-bool overlaps(const void *p, size_t pn, const void *q, size_t qn) {
-    if (!p || !q || pn == 0 || qn == 0) return false;
-    const uintptr_t a = reinterpret_cast<uintptr_t>(p), b = reinterpret_cast<uintptr_t>(q);
-    return a < b + qn && b < a + pn;
-}
-
-int validate(const uint8_t *A, const uint8_t *sfA, const uint8_t *x, const uint8_t *sfx,
-             const float *alpha, uint16_t *c, int64_t l, int64_t m, int64_t k) {
-    if (!A || !sfA || !x || !sfx || !c) return NVFP4_GEMV_ERR_NULL_POINTER;
-    const int s = check_shape(l, m, k);
-    if (s != NVFP4_GEMV_OK) return s;
-    if (reinterpret_cast<uintptr_t>(c) % 2 != 0 || reinterpret_cast<uintptr_t>(alpha) % 4 != 0)
-        return NVFP4_GEMV_ERR_ALIGNMENT;
-    const size_t cn = static_cast<size_t>(l * m) * 2;
-    if (overlaps(c, cn, A, static_cast<size_t>(l * m) * (k / 2)) ||
-        overlaps(c, cn, sfA, static_cast<size_t>(l * m) * (k / 16)) ||
-        overlaps(c, cn, x, static_cast<size_t>(l) * (k / 2)) ||
-        overlaps(c, cn, sfx, static_cast<size_t>(l) * (k / 16)) ||
-        overlaps(c, cn, alpha, static_cast<size_t>(l) * 4))
-        return NVFP4_GEMV_ERR_ALIAS;
-    return NVFP4_GEMV_OK;
-}
-
-int run(const Plan &p, const uint8_t *A, const uint8_t *sfA, const uint8_t *x,
-        const uint8_t *sfx, const float *alpha, uint16_t *c, int64_t l, int64_t m, int64_t k,
-        void *ws, hipStream_t stream) {
+// Enqueues the plan's kernels: the GEMV (or its partial sums) and, with a K
+// split, the second pass.
+int run(const Plan &p, const GemvArgs &g, void *ws, hipStream_t stream) {
+    const uint8_t *A = g.A, *sfA = g.sfA, *x = g.x, *sfx = g.sfx;
+    const float *alpha = g.alpha;
+    uint16_t *c = g.c;
+    int64_t l = g.l, m = g.m, k = g.k;
     float *part = p.ksplit > 1 ? static_cast<float *>(ws) : nullptr;
     int64_t kchunk = p.kchunk, row_blocks = p.row_blocks;
     void *args[] = {&A, &sfA, &x, &sfx, &alpha, &c, &part, &l, &m, &k, &kchunk, &row_blocks};
@@ -1015,27 +841,72 @@ int run(const Plan &p, const uint8_t *A, const uint8_t *sfA, const uint8_t *x,
     return NVFP4_GEMV_OK;
 }
 
-}  // namespace
-
-// Library-owned split-K workspaces, one per (device, stream).
-namespace {
+// Library-owned split-K workspaces, one per (device, stream).  A slot only
+// grows.  Growing allocates a new buffer and retires the old one without
+// freeing it: kernels enqueued earlier on the stream may still read it, and
+// freeing it safely would need a synchronisation.  Retired buffers are kept
+// until the process ends; each growth at least doubles the slot, so they add
+// at most the slot's final size.  No allocation is made while the stream is
+// being captured into a graph (the call fails instead).
 std::mutex g_ws_mutex;
 std::map<std::pair<int, void *>, std::pair<void *, size_t>> g_ws;
+std::vector<void *> g_ws_retired;
+
+bool stream_capturing(void *stream) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(static_cast<hipStream_t>(stream), &cs) != hipSuccess) {
+        (void)hipGetLastError();
+        return true;   // cannot tell: do not allocate
+    }
+    return cs != hipStreamCaptureStatusNone;
+}
+
+// The library's backend for the launch orchestration of gemv_plan.h.
+struct HipBackend {
+    bool device(int *dev) {
+        if (hipGetDevice(dev) == hipSuccess) return true;
+        (void)hipGetLastError();
+        return false;
+    }
+    void *workspace(int dev, void *stream, size_t need) {
+        return nvfp4_stream_workspace(dev, stream, need);
+    }
+    int run(const Plan &p, const GemvArgs &g, void *ws, void *stream) {
+        return ::run(p, g, ws, static_cast<hipStream_t>(stream));
+    }
+};
+
+GemvArgs gemv_args(const uint8_t *A, const uint8_t *sfA, const uint8_t *x, const uint8_t *sfx,
+                   const float *alpha, uint16_t *c, int64_t l, int64_t m, int64_t k) {
+    GemvArgs g;
+    g.A = A;
+    g.sfA = sfA;
+    g.x = x;
+    g.sfx = sfx;
+    g.alpha = alpha;
+    g.c = c;
+    g.l = l;
+    g.m = m;
+    g.k = k;
+    return g;
+}
+
 }  // namespace
 
 void *nvfp4_stream_workspace(int dev, void *stream, size_t need) {
     std::lock_guard<std::mutex> lock(g_ws_mutex);
     auto &slot = g_ws[std::make_pair(dev, stream)];
     if (slot.second >= need) return slot.first;
-    if (slot.first) {
-        // Earlier work on this stream may still read the old buffer.
-        if (hipStreamSynchronize(static_cast<hipStream_t>(stream)) != hipSuccess) return nullptr;
-        (void)hipFree(slot.first);
-        slot = std::make_pair(nullptr, size_t(0));
-    }
+    if (stream_capturing(stream)) return nullptr;
+    size_t bytes = slot.second > need / 2 ? 2 * slot.second : need;
+    bytes = (bytes + 255) & ~size_t(255);
     void *ptr = nullptr;
-    if (hipMalloc(&ptr, need) != hipSuccess) return nullptr;
-    slot = std::make_pair(ptr, need);
+    if (hipMalloc(&ptr, bytes) != hipSuccess) {
+        (void)hipGetLastError();
+        return nullptr;
+    }
+    if (slot.first) g_ws_retired.push_back(slot.first);
+    slot = std::make_pair(ptr, bytes);
     return ptr;
 }
 
@@ -1102,17 +973,9 @@ int nvfp4_gemv_launch_tuned(const uint8_t *A_packed, const uint8_t *sfA, const u
                             const uint8_t *sfx, const float *alpha, uint16_t *c, int64_t l,
                             int64_t m, int64_t k, const nvfp4_gemv_tuning_t *tuning,
                             void *workspace, size_t workspace_bytes, void *stream) {
-    int s = validate(A_packed, sfA, x_packed, sfx, alpha, c, l, m, k);
-    if (s != NVFP4_GEMV_OK) return s;
-    Plan p;
-    s = make_plan(l, m, k, aligned_for_fast(A_packed, sfA, x_packed, sfx), tuning, &p);
-    if (s != NVFP4_GEMV_OK) return s;
-    if (p.ws_bytes > 0) {
-        if (!workspace || workspace_bytes < p.ws_bytes) return NVFP4_GEMV_ERR_WORKSPACE;
-        if (reinterpret_cast<uintptr_t>(workspace) % 4 != 0) return NVFP4_GEMV_ERR_ALIGNMENT;
-    }
-    return run(p, A_packed, sfA, x_packed, sfx, alpha, c, l, m, k, workspace,
-               static_cast<hipStream_t>(stream));
+    HipBackend be;
+    return launch_caller_workspace(be, gemv_args(A_packed, sfA, x_packed, sfx, alpha, c, l, m, k),
+                                   tuning, workspace, workspace_bytes, stream);
 }
 
 int nvfp4_gemv_launch_ws(const uint8_t *A_packed, const uint8_t *sfA, const uint8_t *x_packed,
@@ -1126,20 +989,19 @@ int nvfp4_gemv_launch_ws(const uint8_t *A_packed, const uint8_t *sfA, const uint
 int nvfp4_gemv_launch(const uint8_t *A_packed, const uint8_t *sfA, const uint8_t *x_packed,
                       const uint8_t *sfx, const float *alpha, uint16_t *c, int64_t l, int64_t m,
                       int64_t k, void *stream) {
-    int s = validate(A_packed, sfA, x_packed, sfx, alpha, c, l, m, k);
-    if (s != NVFP4_GEMV_OK) return s;
-    Plan p;
-    s = make_plan(l, m, k, aligned_for_fast(A_packed, sfA, x_packed, sfx), nullptr, &p);
-    if (s != NVFP4_GEMV_OK) return s;
-    void *ws = nullptr;
-    if (p.ws_bytes > 0) {
-        int dev = -1;
-        if (hipGetDevice(&dev) != hipSuccess) return NVFP4_GEMV_ERR_DEVICE;
-        ws = nvfp4_stream_workspace(dev, stream, p.ws_bytes);
-        if (!ws) return NVFP4_GEMV_ERR_WORKSPACE;
+    HipBackend be;
+    return launch_owned_workspace(be, gemv_args(A_packed, sfA, x_packed, sfx, alpha, c, l, m, k),
+                                  stream);
+}
+
+int nvfp4_workspace_reserve(size_t bytes, void *stream) {
+    if (bytes == 0) return NVFP4_GEMV_OK;
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return NVFP4_GEMV_ERR_DEVICE;
     }
-    return run(p, A_packed, sfA, x_packed, sfx, alpha, c, l, m, k, ws,
-               static_cast<hipStream_t>(stream));
+    return nvfp4_stream_workspace(dev, stream, bytes) ? NVFP4_GEMV_OK : NVFP4_GEMV_ERR_WORKSPACE;
 }
 
 int nvfp4_hbm_read_probe(const void *buffer, size_t bytes, uint32_t *sink, void *stream) {
