@@ -2,21 +2,40 @@
 """Throughput of the NVFP4 block-scaled batched GEMV on one MI355X.
 
 One step = one call of the GEMV (all of its kernels) on one batch of inputs.
-The default workload is the decode-style single large weight: l=1, m=7168,
-k=16384, integer-coded (nibbles uniform over all 16 E2M1 codes, block scales
-from {0, 1, 2}), alpha = 1.  Its 66 MB footprint fits in MI355X's 256 MB
-Infinity Cache, so the timed loop rotates over enough device copies of the
-inputs (>= 1 GB together) that every step reads its operands from HBM; a
-cache-resident ("warm") figure is reported separately and labelled as such.
+With no arguments the GEMV is measured on each of its five workloads in turn
+and one JSON line is printed per workload, the batched workload (l=8,
+m=4096, k=7168, the largest operand that the metric's "batched GEMV" names)
+last:
 
-Prints one JSON line:
+  tiny      l=1,  m=128,  k=256    integer-coded, alpha 1   (launch-bound)
+  decode    l=1,  m=7168, k=16384  integer-coded, alpha 1
+  shortk    l=4,  m=7168, k=2048   integer-coded, alpha 1
+  gaussian  l=16, m=2048, k=4096   bf16 N(0,1) quantised per batch, alpha gA*gx
+  batched   l=8,  m=4096, k=7168   integer-coded, alpha U[0.5, 2]
+
+Every footprint fits in MI355X's 256 MB Infinity Cache, so the timed steps
+rotate over device copies of the inputs (>= 1 GB together) and every step
+reads its operands from HBM; a cache-resident ("warm") figure is reported
+separately and labelled as such.
+
+Timing: W warm-up steps, then a synchronisation, then exactly K steps between
+two HIP events on the launch stream, then a synchronisation.  With --launch
+graph (the default) the K steps are captured once into a HIP graph, replayed
+once untimed, and the timed region is one replay; with --launch stream they
+are launched one by one from Python.  Either way a GPU-side delay kernel runs
+before the start event, so the stream is not idle while the host enqueues
+the first steps.
+
+Each JSON line:
   value        algorithmic bytes per step (A + sfA + x + sfx + c) / time, GB/s
   roofline     the same rate against the 8 TB/s HBM peak, the kernel's HBM
                traffic from rocprofv3 counters when they were taken on this
-               kernel source, and the achievable read rate of a plain
-               streaming-read probe measured in the same run
+               kernel source, and the read rates of two streaming-read probes
+               measured in the same run (a flat 1 GiB read, and a read of the
+               workload's own A and sfA with the GEMV's load pattern)
   cpu_baseline the CPU oracle (plain C, fp64, OpenMP over rows) on the same
-               workload on this host's cores
+               workload on this host's cores, with the parity of the last
+               timed call against it
 
 Other paths (--path), each printing its own JSON line of the same form:
   quantize     the BF16 -> NVFP4 activation quantiser on a bf16 activation
@@ -29,7 +48,12 @@ Other paths (--path), each printing its own JSON line of the same form:
   --packed     with smalln / grouped: the weights are packed once into the
                matrix-core tile layout (not timed) and the packed calls timed
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config decode]
+--trace-cold runs only the warm-up and the timed steps (no cache-resident
+loop, single launches, probes or CPU baseline), for rocprofv3 kernel traces
+whose averages then cover HBM-cold launches only.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config all|decode|...]
+                       [--launch graph|stream] [--trace-cold]
                        [--path gemv|quantize|gemv_bf16x|smalln|grouped] [--packed]
 """
 from __future__ import annotations
@@ -48,12 +72,22 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+METRIC = "achieved HBM GB/s and % of MI355X peak for NVFP4 batched GEMV; \u00b5s/call"
+# GEMV workloads of --config all, in print order: the batched workload's line last
+GEMV_ORDER = ("tiny", "decode", "shortk", "gaussian", "batched")
+# GPU-side delay before a timed region (clock cycles of torch's spin kernel)
+PREROLL_CYCLES = 200_000
+# at most this many input copies (the tiny workload would otherwise need 50000)
+MAX_REPLICAS = 64
 CSRC = os.path.join(ROOT, "precision_decode_amd", "csrc")
 PROFILES = os.path.join(ROOT, "profiles")
 # counter summaries under profiles/ are valid only for the source they were taken on
-KERNEL_SOURCES = {"gemv_fast": "nvfp4_gemv.hip", "quantize_blocks": "nvfp4_quantize.hip",
-                  "mma_stream": "nvfp4_mma.hip", "vec_tile": "nvfp4_mma.hip",
-                  "mma_stream_packed": "nvfp4_mma.hip"}
+# (the GEMV's device code is gemv_kernels.h with its helpers in device_common.h)
+KERNEL_SOURCES = {"gemv_fast": ("gemv_kernels.h", "device_common.h"),
+                  "quantize_blocks": ("nvfp4_quantize.hip", "device_common.h"),
+                  "mma_stream": ("nvfp4_mma.hip", "device_common.h"),
+                  "vec_tile": ("nvfp4_mma.hip", "device_common.h"),
+                  "mma_stream_packed": ("nvfp4_mma.hip", "device_common.h")}
 
 
 def parse_args(argv=None):
@@ -63,9 +97,16 @@ def parse_args(argv=None):
     p.add_argument("--warmup", type=int, default=100)
     p.add_argument("--path", default="gemv",
                    choices=["gemv", "quantize", "gemv_bf16x", "smalln", "grouped"])
-    p.add_argument("--config", default="decode",
+    p.add_argument("--config", default="all",
                    help="GEMV workload from workloads.CONFIGS (decode, batched, shortk, tiny, or "
-                        "gaussian: bf16 draws quantised by the library's device quantiser, untimed)")
+                        "gaussian: bf16 draws quantised by the library's device quantiser, untimed), "
+                        "or all: each in turn, one JSON line each, batched last")
+    p.add_argument("--launch", default="graph", choices=["graph", "stream"],
+                   help="GEMV: time the K steps as one replay of a HIP graph that holds them, or "
+                        "launched one by one on the stream")
+    p.add_argument("--trace-cold", action="store_true",
+                   help="GEMV: only the warm-up and the timed steps (no cache-resident loop, "
+                        "single launches, probes or CPU baseline), for kernel traces")
     p.add_argument("--act-config", default="tokens",
                    help="activation workload of --path quantize (workloads.ACT_CONFIGS)")
     p.add_argument("--smalln-config", default="decode_n16",
@@ -98,8 +139,11 @@ def parse_args(argv=None):
 
 
 def kernel_source_hash(kernel: str = "gemv_fast") -> str:
-    with open(os.path.join(CSRC, KERNEL_SOURCES[kernel]), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def recorded_traffic(config: str, kernel: str = "gemv_fast"):
@@ -143,10 +187,21 @@ def single_launch_percentiles(torch, stream, step, n):
 
 
 class Timer:
-    """HIP events on the launch stream around n back-to-back calls."""
+    """HIP events on the launch stream around n back-to-back calls.  A GPU-side
+    delay kernel runs first, so the stream is busy (not idle at the start
+    event) while the host enqueues the first calls."""
 
     def __init__(self, torch, stream):
         self.torch, self.stream = torch, stream
+        self.enqueue_s = 0.0
+
+    def preroll(self):
+        sleep = getattr(self.torch.cuda, "_sleep", None)
+        if sleep is not None:
+            try:
+                sleep(PREROLL_CYCLES)
+            except RuntimeError:
+                self.torch.cuda._sleep = None     # not available on this build: no delay
 
     def __call__(self, n, fn):
         torch = self.torch
@@ -154,6 +209,7 @@ class Timer:
         end = torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
+        self.preroll()
         start.record(self.stream)
         for i in range(n):
             fn(i)
@@ -163,8 +219,26 @@ class Timer:
         return start.elapsed_time(end), time.perf_counter() - t0
 
 
+def capture_steps(torch, n, step, state):
+    """A HIP graph holding steps 0 .. n-1, captured on a side stream (nothing
+    runs).  `state["stream"]` is the stream the step function launches on."""
+    g = torch.cuda.CUDAGraph()
+    cs = torch.cuda.Stream()
+    main = torch.cuda.current_stream()
+    cs.wait_stream(main)
+    try:
+        with torch.cuda.graph(g, stream=cs):
+            state["stream"] = cs.cuda_stream
+            for i in range(n):
+                step(i)
+    finally:
+        state["stream"] = main.cuda_stream
+    main.wait_stream(cs)
+    return g
+
+
 def replicate(torch, base, nbytes, reps_arg):
-    reps = reps_arg or max(1, -(-1_000_000_000 // nbytes))
+    reps = reps_arg or min(MAX_REPLICAS, max(1, -(-1_000_000_000 // nbytes)))
     return [base] + [{n: t.clone() for n, t in base.items()} for _ in range(reps - 1)], reps
 
 
@@ -275,8 +349,47 @@ def quantize_gaussian_on_device(torch, np, pd, raw, l, m, k):
     return out
 
 
-def bench_gemv(args, torch, np, pd, workloads):
-    cfg = workloads.CONFIGS[args.config]
+def flat_probe_gbs(torch, pd, timer, sptr, shared):
+    """The library's flat streaming-read probe over 1 GiB (measured once per run)."""
+    if "flat_probe_gbs" not in shared:
+        pbytes = 1 << 30
+        pbuf = torch.empty(pbytes, dtype=torch.uint8, device="cuda")
+        pbuf.fill_(1)
+        sink = torch.empty(4096, dtype=torch.int32, device="cuda")
+        for _ in range(3):
+            pd.nvfp4_hbm_read_probe(pbuf, pbytes, sink, sptr)
+        pn = 20
+        pms, _ = timer(pn, lambda i: pd.nvfp4_hbm_read_probe(pbuf, pbytes, sink, sptr))
+        shared["flat_probe_gbs"] = pbytes / (pms / pn * 1e-3) / 1e9
+        del pbuf
+        print(f"[bench] streaming-read probe (1 GiB): {shared['flat_probe_gbs']:.1f} GB/s", flush=True)
+    return shared["flat_probe_gbs"]
+
+
+def row_probe_gbs(torch, pd, timer, sptr, replicas, l, m, k):
+    """The row-pattern read probe over every copy's A and sfA in turn: the read
+    ceiling of the GEMV's load pattern for this weight, operands in HBM."""
+    if k % 32 != 0:
+        return None
+    reps = len(replicas)
+    rows = l * m
+    sink = torch.empty(-(-rows // 14), dtype=torch.int32, device="cuda")
+    nbytes = rows * (k // 2 + k // 16)
+    for i in range(min(reps, 4)):
+        pd.nvfp4_hbm_read_probe_rows(replicas[i]["A"], replicas[i]["sfA"], rows, k, sink, sptr)
+    pn = max(8, 4 * reps)
+    pms, _ = timer(pn, lambda i: pd.nvfp4_hbm_read_probe_rows(replicas[i % reps]["A"],
+                                                              replicas[i % reps]["sfA"], rows, k,
+                                                              sink, sptr))
+    gbs = nbytes / (pms / pn * 1e-3) / 1e9
+    print(f"[bench] row-pattern read probe over A and sfA ({nbytes / 1e6:.1f} MB, rotated): "
+          f"{gbs:.1f} GB/s ({pms / pn * 1e3:.2f} us per read)", flush=True)
+    return gbs
+
+
+def bench_gemv(args, torch, np, pd, workloads, name=None, shared=None):
+    shared = {} if shared is None else shared
+    cfg = workloads.CONFIGS[name or args.config]
     l, m, k = cfg.l, cfg.m, cfg.k
     nbytes = cfg.bytes_moved
     print(f"[bench] workload {cfg.name}: l={l} m={m} k={k}, {nbytes} bytes per step", flush=True)
@@ -292,64 +405,77 @@ def bench_gemv(args, torch, np, pd, workloads):
     replicas, reps = replicate(torch, base, nbytes, args.replicas)
     c = torch.empty((l, m), dtype=torch.int16, device="cuda")
     stream = torch.cuda.current_stream()
-    sptr = stream.cuda_stream
+    state = {"stream": stream.cuda_stream}
     timer = Timer(torch, stream)
 
     tuned = args.variant or args.ksplit
     tuning = {"variant": args.variant, "ksplit": args.ksplit}
     plan, ws_bytes = pd.nvfp4_gemv_plan(l, m, k, aligned=True, tuning=tuning if tuned else None)
     ws = torch.empty(max(ws_bytes, 4), dtype=torch.uint8, device="cuda")
+    if not tuned and ws_bytes:
+        pd.nvfp4_workspace_reserve(ws_bytes, stream)   # before any capture
 
     def step(i):
         r = replicas[i % reps]
         if tuned:
             pd.nvfp4_gemv_launch_tuned(r["A"], r["sfA"], r["x"], r["sfx"], r["alpha"], c, l, m, k,
-                                       tuning, ws, ws_bytes, sptr)
+                                       tuning, ws, ws_bytes, state["stream"])
         else:
-            pd.nvfp4_gemv_launch(r["A"], r["sfA"], r["x"], r["sfx"], r["alpha"], c, l, m, k, sptr)
+            pd.nvfp4_gemv_launch(r["A"], r["sfA"], r["x"], r["sfx"], r["alpha"], c, l, m, k,
+                                 state["stream"])
 
+    footprint = reps * nbytes
+    operands = ("HBM (rotated over >= 1 GB of copies)" if footprint >= 1_000_000_000 else
+                f"rotated over {reps} copies ({footprint / 1e6:.1f} MB, cache-resident: "
+                f"launch-bound workload)")
     print(f"[bench] plan path={plan.path} variant={plan.variant} ksplit={plan.ksplit}; "
-          f"{reps} replicas ({reps * nbytes / 1e9:.2f} GB)", flush=True)
-    ms_step, gbs = timed_steps(args, timer, step, nbytes, "gemv")
+          f"{reps} replicas ({footprint / 1e9:.3f} GB)", flush=True)
 
-    nw = min(args.steps, 500)
-    warm_ms, _ = timer(nw, lambda i: step(0))
-    warm_gbs = nbytes / (warm_ms / nw * 1e-3) / 1e9
-    print(f"[bench] cache-resident (same buffers every step): {warm_gbs:.1f} GB/s", flush=True)
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    # the K steps launched one by one from the host
+    ms_total, wall = timer(args.steps, step)
+    stream_us = ms_total / args.steps * 1e3
+    enqueue_us = timer.enqueue_s / args.steps * 1e6
+    print(f"[bench] gemv, stream launches: {args.steps} steps: {stream_us:.2f} us/step "
+          f"({nbytes / stream_us / 1e3:.1f} GB/s), host enqueue {enqueue_us:.2f} us/step", flush=True)
+    graph_us = None
+    if args.launch == "graph":
+        g = capture_steps(torch, args.steps, step, state)
+        g.replay()                                   # untimed: uploads the graph
+        torch.cuda.synchronize()
+        ms_total, wall = timer(1, lambda i: g.replay())
+        graph_us = ms_total / args.steps * 1e3
+        print(f"[bench] gemv, one graph replay of {args.steps} steps: {graph_us:.2f} us/step "
+              f"({nbytes / graph_us / 1e3:.1f} GB/s)", flush=True)
+    us_step = graph_us if graph_us is not None else stream_us
+    ms_step = us_step * 1e-3
+    gbs = nbytes / (ms_step * 1e-3) / 1e9
+    print(f"[bench] gemv {cfg.name}: {us_step:.2f} us/step, {gbs:.1f} GB/s "
+          f"({100 * gbs / HBM_PEAK_GBS:.1f}% of peak)", flush=True)
+    # the last timed call's output, before anything else writes c
+    got = c.cpu().numpy().view(np.uint16).copy()
 
-    single = single_launch_percentiles(torch, stream, step, args.single_launches)
-    if single:
-        print(f"[bench] single launches after a 512 MiB scratch write: p10 {single['p10']} us, "
-              f"p50 {single['p50']} us, p90 {single['p90']} us", flush=True)
+    warm_gbs = single = probe_gbs = probe_rows = None
+    if not args.trace_cold:
+        nw = min(args.steps, 500)
+        warm_ms, _ = timer(nw, lambda i: step(0))
+        warm_gbs = nbytes / (warm_ms / nw * 1e-3) / 1e9
+        print(f"[bench] cache-resident (same buffers every step): {warm_gbs:.1f} GB/s", flush=True)
 
-    probe_gbs = probe_ws_gbs = None
-    if not args.no_probe:
-        pbytes = 1 << 30
-        pbuf = torch.empty(pbytes, dtype=torch.uint8, device="cuda")
-        pbuf.fill_(1)
-        sink = torch.empty(4096, dtype=torch.int32, device="cuda")
-        for _ in range(3):
-            pd.nvfp4_hbm_read_probe(pbuf, pbytes, sink, sptr)
-        pn = 20
-        pms, _ = timer(pn, lambda i: pd.nvfp4_hbm_read_probe(pbuf, pbytes, sink, sptr))
-        probe_gbs = pbytes / (pms / pn * 1e-3) / 1e9
-        del pbuf
-        print(f"[bench] streaming-read probe (1 GiB): {probe_gbs:.1f} GB/s", flush=True)
-        # the same probe over each copy's A in turn: the achievable read rate
-        # for a read of this workload's size, operands in HBM
-        abytes = replicas[0]["A"].numel()
-        pn = 4 * reps
-        pms, _ = timer(pn, lambda i: pd.nvfp4_hbm_read_probe(replicas[i % reps]["A"], abytes, sink,
-                                                             sptr))
-        probe_ws_gbs = abytes / (pms / pn * 1e-3) / 1e9
-        print(f"[bench] streaming-read probe over A ({abytes / 1e6:.1f} MB, rotated): "
-              f"{probe_ws_gbs:.1f} GB/s", flush=True)
-
+        single = single_launch_percentiles(torch, stream, step, args.single_launches)
+        if single:
+            print(f"[bench] single launches after a 512 MiB scratch write: p10 {single['p10']} us, "
+                  f"p50 {single['p50']} us, p90 {single['p90']} us", flush=True)
+        if not args.no_probe:
+            probe_gbs = flat_probe_gbs(torch, pd, timer, state["stream"], shared)
+            probe_rows = row_probe_gbs(torch, pd, timer, state["stream"], replicas, l, m, k)
     run_copies(torch, args.copy_mib)
 
     cpu = None
     quantised = None
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not args.trace_cold:
         from oracle import reference as ref
 
         if raw is not None:
@@ -366,8 +492,7 @@ def bench_gemv(args, torch, np, pd, workloads):
         results = []
         t_med = cpu_time(lambda: results.append(ref.gemv(ops["A"], ops["sfA"], ops["x"], ops["sfx"],
                                                          ops["alpha"], l, m, k, nthreads=threads)))
-        torch.cuda.synchronize()
-        parity = parity_summary(np, c.cpu().numpy().view(np.uint16), results[-1])
+        parity = parity_summary(np, got, results[-1])
         print(f"[bench] parity of the last timed call with the oracle: {parity}", flush=True)
         cpu = {"value": round(nbytes / t_med / 1e9, 4), "unit": "GB/s", "cores": threads,
                "kind": "oracle",
@@ -380,20 +505,37 @@ def bench_gemv(args, torch, np, pd, workloads):
             cpu["quantised_operands_identical"] = quantised
         print(f"[bench] CPU oracle: {t_med:.3f}s per GEMV on {threads} threads", flush=True)
 
-    out = {"metric": "achieved HBM GB/s for the NVFP4 block-scaled batched GEMV (us/call and % of "
-                     "MI355X peak alongside)"}
+    out = {"metric": METRIC}
     out.update(common_fields(args, gbs, ms_step, "f32"))
     inputs = {"one": "integer-coded, alpha=1", "uniform": "integer-coded, alpha U[0.5,2]",
               "quantizer": "bf16 N(0,1) quantised on the device, alpha = gA*gx"}[cfg.alpha]
     out["config"] = {"workload": f"{cfg.name}: NVFP4 GEMV l={l} m={m} k={k}, {inputs} ({cfg.note})",
                      "l": l, "m": m, "k": k, "bytes_per_step": nbytes,
-                     "replicas": reps, "operands": "HBM (rotated over >= 1 GB of copies)",
+                     "replicas": reps, "operands": operands,
+                     "launch": ("one HIP graph replay of the K steps" if graph_us is not None
+                                else "K stream launches"),
                      "plan": {"path": plan.path, "variant": plan.variant, "ksplit": plan.ksplit}}
-    out["roofline"] = roofline(gbs, recorded_traffic(cfg.name), probe_read_gbs=probe_gbs,
-                               probe_read_same_size_gbs=probe_ws_gbs, cache_resident_gbs=warm_gbs)
+    out["timing_us"] = {"graph_replay": None if graph_us is None else round(graph_us, 3),
+                        "stream_launches": round(stream_us, 3),
+                        "host_enqueue_per_launch": round(enqueue_us, 3)}
+    out["roofline"] = roofline(gbs, recorded_traffic(cfg.name), kernel=plan_kernel_name(pd, plan),
+                               probe_read_gbs=probe_gbs, probe_rows_same_size_gbs=probe_rows,
+                               cache_resident_gbs=warm_gbs)
     out["single_launch_us"] = single
     out["cpu_baseline"] = with_speedup(cpu, gbs)
+    if cpu is not None:
+        out["parity"] = cpu["parity"]
     return out
+
+
+def plan_kernel_name(pd, plan):
+    """The GEMV kernel a plan launches, as the profiles name it."""
+    if plan.path != pd.NVFP4_GEMV_PATH_FAST:
+        return "gemv_generic"
+    r, u, w, xs = pd.nvfp4_gemv_variant_info(plan.variant)
+    if xs == 3:
+        return f"gemv_tile<{w}, {r}>"
+    return f"{('gemv_fast', 'gemv_fastp', 'gemv_fastg')[xs]}<{r}, {u}, {w}>"
 
 
 # ------------------------------------------------------------------------------ quantiser
@@ -450,7 +592,7 @@ def bench_quantize(args, torch, np, pd, workloads):
 
 # ------------------------------------------------------------- GEMV fed by a bf16 activation
 def bench_bf16x(args, torch, np, pd, workloads):
-    cfg = workloads.CONFIGS[args.config]
+    cfg = workloads.CONFIGS["decode" if args.config == "all" else args.config]
     if cfg.kind != "integer":
         print(f"{cfg.name} is not an integer-coded workload", file=sys.stderr)
         return None
@@ -681,7 +823,16 @@ def main(argv=None) -> int:
         return 1
     torch.cuda.set_device(0)
 
-    fn = {"gemv": bench_gemv, "quantize": bench_quantize, "gemv_bf16x": bench_bf16x,
+    if args.path == "gemv":
+        names = GEMV_ORDER if args.config == "all" else (args.config,)
+        shared = {}
+        for name in names:
+            out = bench_gemv(args, torch, np, pd, workloads, name, shared)
+            print(json.dumps(out), flush=True)
+            torch.cuda.synchronize()
+            torch.cuda.empty_cache()
+        return 0
+    fn = {"quantize": bench_quantize, "gemv_bf16x": bench_bf16x,
           "smalln": bench_smalln, "grouped": bench_grouped}[args.path]
     out = fn(args, torch, np, pd, workloads)
     if out is None:

@@ -187,6 +187,19 @@ int nvfp4_gemv_launch_tuned(const uint8_t *A_packed, const uint8_t *sfA,
  */
 int nvfp4_hbm_read_probe(const void *buffer, size_t bytes, uint32_t *sink, void *stream);
 
+/*
+ * Streams `rows` rows of packed codes (A, k/2 bytes per row, 16-byte aligned)
+ * and their scales (sfA, k/16 bytes per row, 2-byte aligned) once, with the
+ * load pattern of the GEMV's kernel for long rows (workgroups of 7 waves over
+ * 14 rows, 2 rows per wave, 4 iterations of 1 KiB per row in flight), and does
+ * no arithmetic.  Its run time is the read ceiling of that pattern for a
+ * weight of this shape.  Workgroup g stores the XOR of all words it read in
+ * sink[g]: `sink` (device) holds ceil(rows / 14) uint32.  Shape rules:
+ * rows >= 1, k >= 32, k % 32 == 0, k < 2^31.  Returns a status.
+ */
+int nvfp4_hbm_read_probe_rows(const uint8_t *A, const uint8_t *sfA, int64_t rows, int64_t k,
+                              uint32_t *sink, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

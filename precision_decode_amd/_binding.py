@@ -51,6 +51,7 @@ EXPORTED = (
     "nvfp4_gemv_plan",
     "nvfp4_gemv_launch_tuned",
     "nvfp4_hbm_read_probe",
+    "nvfp4_hbm_read_probe_rows",
     "nvfp4_workspace_reserve",
     "nvfp4_quantize_activation",
     "nvfp4_quantize_weight",
@@ -128,6 +129,8 @@ def load():
     lib.nvfp4_gemv_launch_tuned.argtypes = gemv_args + [ctypes.POINTER(Tuning), _P, ctypes.c_size_t, _P]
     lib.nvfp4_workspace_reserve.restype = ctypes.c_int
     lib.nvfp4_workspace_reserve.argtypes = [ctypes.c_size_t, _P]
+    lib.nvfp4_hbm_read_probe_rows.restype = ctypes.c_int
+    lib.nvfp4_hbm_read_probe_rows.argtypes = [_P, _P, _I64, _I64, _P, _P]
     lib.nvfp4_hbm_read_probe.restype = ctypes.c_int
     lib.nvfp4_hbm_read_probe.argtypes = [_P, ctypes.c_size_t, _P, _P]
     lib.nvfp4_quantize_activation.restype = ctypes.c_int
@@ -273,6 +276,11 @@ def nvfp4_workspace_reserve(nbytes, stream=None):
 def nvfp4_hbm_read_probe(buffer, nbytes, sink, stream=None):
     _check(load().nvfp4_hbm_read_probe(_ptr(buffer), int(nbytes), _ptr(sink), _stream(stream)),
            "nvfp4_hbm_read_probe")
+
+
+def nvfp4_hbm_read_probe_rows(A, sfA, rows, k, sink, stream=None):
+    _check(load().nvfp4_hbm_read_probe_rows(_ptr(A), _ptr(sfA), rows, k, _ptr(sink),
+                                            _stream(stream)), "nvfp4_hbm_read_probe_rows")
 
 
 def nvfp4_quantize_activation(x_bf16, global_scale, scale_per_row, x_packed, sf, rows, d, rule,

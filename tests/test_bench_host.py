@@ -7,10 +7,52 @@ import pytest
 import bench
 
 
-def test_defaults_time_the_decode_gemv():
+def test_defaults_time_every_gemv_workload_batched_last():
     a = bench.parse_args([])
-    assert a.gpus == 1 and a.path == "gemv" and a.config == "decode"
-    assert a.steps > 0 and a.warmup > 0 and a.single_launches > 0
+    assert a.gpus == 1 and a.path == "gemv" and a.config == "all" and a.launch == "graph"
+    assert a.steps > 0 and a.warmup > 0 and a.single_launches > 0 and not a.trace_cold
+    import workloads
+    assert set(bench.GEMV_ORDER) == set(workloads.CONFIGS)
+    assert bench.GEMV_ORDER[-1] == "batched"          # the line a parser of the last line reads
+
+
+def test_metric_is_the_baseline_metric():
+    import json
+    with open(os.path.join(os.path.dirname(bench.__file__), "BASELINE.json")) as f:
+        assert json.load(f)["metric"] == bench.METRIC
+
+
+def test_plan_kernel_names_match_the_profiles():
+    class FakePd:
+        NVFP4_GEMV_PATH_FAST = 1
+        info = {1: (2, 4, 7, 0), 11: (2, 2, 4, 1), 20: (2, 4, 4, 2), 29: (4, 1, 1, 3),
+                25: (16, 1, 2, 3)}
+
+        def nvfp4_gemv_variant_info(self, v):
+            return self.info[v]
+
+    class P:
+        def __init__(self, v, path=1):
+            self.variant, self.path = v, path
+
+    pd = FakePd()
+    assert bench.plan_kernel_name(pd, P(1)) == "gemv_fast<2, 4, 7>"
+    assert bench.plan_kernel_name(pd, P(11)) == "gemv_fastp<2, 2, 4>"
+    assert bench.plan_kernel_name(pd, P(20)) == "gemv_fastg<2, 4, 4>"
+    assert bench.plan_kernel_name(pd, P(29)) == "gemv_tile<1, 4>"
+    assert bench.plan_kernel_name(pd, P(25)) == "gemv_tile<2, 16>"
+    assert bench.plan_kernel_name(pd, P(0, path=2)) == "gemv_generic"
+
+
+def test_replicas_are_capped():
+    class FakeT:
+        def clone(self):
+            return self
+
+    reps_list, reps = bench.replicate(None, {"A": FakeT()}, 18832, 0)
+    assert reps == bench.MAX_REPLICAS and len(reps_list) == reps
+    _, reps = bench.replicate(None, {"A": FakeT()}, 66_083_840, 0)
+    assert reps == 16 and reps * 66_083_840 >= 1_000_000_000
 
 
 def test_more_than_one_gpu_exits_with_a_message(capsys):
@@ -34,6 +76,7 @@ def test_recorded_traffic_needs_the_current_source(tmp_path, monkeypatch):
     monkeypatch.setattr(bench, "PROFILES", str(tmp_path))
     assert bench.recorded_traffic("decode") is None                     # no file
     h = bench.kernel_source_hash("gemv_fast")
+    assert len(h) == 16 and h != bench.kernel_source_hash("mma_stream")
     f = tmp_path / "gemv_fast_decode_hbm_counters.txt"
     f.write_text(f"kernel_source_sha256_16: {h}\nhbm_bytes_per_launch: 66291018\n")
     assert bench.recorded_traffic("decode") == 66291018.0

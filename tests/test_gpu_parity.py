@@ -273,3 +273,24 @@ def test_hbm_read_probe_reads_every_byte_once(n):
     want = np.bitwise_xor.reduce(data.cpu().numpy().view(np.uint32))
     got = np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32))
     assert got == want
+
+
+@pytest.mark.parametrize("rows,k", [(7168, 16384), (29, 2048), (15, 7168), (1, 32), (100, 4128)])
+def test_hbm_read_probe_rows_reads_every_byte_once(rows, k):
+    """Whole and ragged workgroups (14 rows each), rows shorter than one
+    iteration, K not a multiple of the 4 KiB in flight."""
+    print(f"row probe over {rows} x {k}", flush=True)
+    g = torch.Generator().manual_seed(rows * 7 + k)
+    a = torch.randint(0, 256, (rows * k // 2,), dtype=torch.uint8, generator=g)
+    s = torch.randint(0, 256, (rows * k // 16,), dtype=torch.uint8, generator=g)
+    groups = -(-rows // 14)
+    sink = torch.zeros(groups, dtype=torch.int32, device="cuda")
+    pd.nvfp4_hbm_read_probe_rows(a.cuda(), s.cuda(), rows, k, sink)
+    torch.cuda.synchronize()
+
+    # the probe XORs 16-byte code chunks and 2-byte scale pairs: fold both to 32 bits
+    want = np.bitwise_xor.reduce(a.numpy().view(np.uint32))
+    sv = s.numpy().view(np.uint16).astype(np.uint32)
+    want ^= np.bitwise_xor.reduce(sv) if sv.size else np.uint32(0)
+    got = np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32))
+    assert got == want
