@@ -124,6 +124,30 @@ int nvfp4_gemv_launch_ws(const uint8_t *A_packed, const uint8_t *sfA,
  */
 int nvfp4_workspace_reserve(size_t bytes, void *stream);
 
+/*
+ * For callers that cannot allocate device memory (code under graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): nvfp4_gemv_launch
+ * with the same arguments, results and kernels, except that the split-K
+ * partial sums go to a fixed array of NVFP4_GEMV_NOALLOC_SCRATCH_BYTES bytes
+ * that the library holds in each GPU's memory from when it is loaded until the
+ * process ends.  The call never allocates or frees memory.  A shape whose
+ * partial sums need more than the array holds (nvfp4_gemv_workspace_size
+ * above NVFP4_GEMV_NOALLOC_SCRATCH_BYTES, which takes hundreds of thousands of
+ * rows with K split) returns NVFP4_GEMV_ERR_WORKSPACE and enqueues nothing.
+ *
+ * Every call on one GPU shares that GPU's array: calls that may overlap in
+ * time on one GPU (on different streams, or from different threads without
+ * ordering) race on it and give undefined results; calls ordered on one
+ * stream are safe.  Nothing in the array needs clearing between calls: each
+ * call writes every partial sum before reading it.
+ */
+#define NVFP4_GEMV_NOALLOC_SCRATCH_BYTES ((size_t)4 << 20)
+
+int nvfp4_gemv_launch_noalloc(const uint8_t *A_packed, const uint8_t *sfA,
+                              const uint8_t *x_packed, const uint8_t *sfx,
+                              const float *alpha, uint16_t *c,
+                              int64_t l, int64_t m, int64_t k, void *stream);
+
 /* ---- launch-plan control (tests and tuning sweeps) ---------------------- */
 
 /* Kernel choice. */

@@ -40,6 +40,8 @@ NVFP4_GEMV_PATH_AUTO = 0
 NVFP4_GEMV_PATH_FAST = 1
 NVFP4_GEMV_PATH_GENERIC = 2
 
+NVFP4_GEMV_NOALLOC_SCRATCH_BYTES = 4 << 20
+
 # Every symbol the header declares.
 EXPORTED = (
     "nvfp4_gemv_status_string",
@@ -53,6 +55,7 @@ EXPORTED = (
     "nvfp4_hbm_read_probe",
     "nvfp4_hbm_read_probe_rows",
     "nvfp4_workspace_reserve",
+    "nvfp4_gemv_launch_noalloc",
     "nvfp4_quantize_activation",
     "nvfp4_quantize_weight",
     "nvfp4_gemv_bf16x_launch",
@@ -127,6 +130,8 @@ def load():
                                     ctypes.POINTER(Tuning), ctypes.POINTER(ctypes.c_size_t)]
     lib.nvfp4_gemv_launch_tuned.restype = ctypes.c_int
     lib.nvfp4_gemv_launch_tuned.argtypes = gemv_args + [ctypes.POINTER(Tuning), _P, ctypes.c_size_t, _P]
+    lib.nvfp4_gemv_launch_noalloc.restype = ctypes.c_int
+    lib.nvfp4_gemv_launch_noalloc.argtypes = gemv_args + [_P]
     lib.nvfp4_workspace_reserve.restype = ctypes.c_int
     lib.nvfp4_workspace_reserve.argtypes = [ctypes.c_size_t, _P]
     lib.nvfp4_hbm_read_probe_rows.restype = ctypes.c_int
@@ -267,6 +272,12 @@ def nvfp4_gemv_launch_tuned(A_packed, sfA, x_packed, sfx, alpha, c, l, m, k, tun
                                         _ptr(alpha), _ptr(c), l, m, k, _tuning(tuning),
                                         _ptr(workspace), int(workspace_bytes), _stream(stream))
     _check(st, "nvfp4_gemv_launch_tuned")
+
+
+def nvfp4_gemv_launch_noalloc(A_packed, sfA, x_packed, sfx, alpha, c, l, m, k, stream=None):
+    st = load().nvfp4_gemv_launch_noalloc(_ptr(A_packed), _ptr(sfA), _ptr(x_packed), _ptr(sfx),
+                                          _ptr(alpha), _ptr(c), l, m, k, _stream(stream))
+    _check(st, "nvfp4_gemv_launch_noalloc")
 
 
 def nvfp4_workspace_reserve(nbytes, stream=None):

@@ -5,8 +5,8 @@
 // Plain C++17 with no HIP types, so that the same code is compiled into the
 // library (nvfp4_gemv.hip) and into host-only checks built with g++ and the
 // address and undefined-behaviour sanitizers.  The launch orchestration takes
-// a "backend" with three calls (current device, library-owned workspace,
-// launch of a plan): the library's backend
+// a "backend" with four calls (current device, library-owned workspace,
+// fixed-size scratch of a device, launch of a plan): the library's backend
 // calls HIP, a test backend can fail each of them on purpose.
 //
 // The operation the plans serve is the NVFP4 batched GEMV of "nvFP4 Batch
@@ -36,6 +36,9 @@ constexpr int kGenericWaves = 4;
 // The row-tile kernel addresses a tile's rows through one descriptor with
 // 32-bit offsets; it takes K up to this bound.
 constexpr int64_t kTileMaxK = int64_t(1) << 26;
+// Largest split-K workspace the no-allocation entry point can use: the size
+// of its fixed device array.
+constexpr size_t kNoAllocScratchBytes = NVFP4_GEMV_NOALLOC_SCRATCH_BYTES;
 
 // x staging of a fast variant: fp16 x~ in LDS (gemv_fast), packed codes in LDS
 // (gemv_fastp), no staging (gemv_fastg, x read next to A every iteration), or
@@ -225,6 +228,8 @@ inline int validate(const GemvArgs &a) {
 //   bool  device(int *dev)                          current device, false if none
 //   void *workspace(int dev, void *stream, size_t)  library-owned per-stream
 //                                                   workspace, NULL on failure
+//   void *scratch(int dev)                          the device's fixed scratch
+//                                                   array, NULL on failure
 //   int   run(const Plan &, const GemvArgs &, void *ws, void *stream)
 //                                                   enqueues the plan's kernels;
 //                                                   NVFP4_GEMV_OK or _ERR_LAUNCH
@@ -264,6 +269,27 @@ int launch_caller_workspace(Backend &be, const GemvArgs &a, const nvfp4_gemv_tun
             return NVFP4_GEMV_ERR_ALIAS;
     }
     return be.run(p, a, p.ws_bytes > 0 ? workspace : nullptr, stream);
+}
+
+// nvfp4_gemv_launch_noalloc: default plan, split-K partials in the current
+// device's fixed scratch array; a plan needing more than the array holds is
+// refused before anything else is asked of the backend.
+template <class Backend>
+int launch_fixed_scratch(Backend &be, const GemvArgs &a, void *stream) {
+    int s = validate(a);
+    if (s != NVFP4_GEMV_OK) return s;
+    Plan p;
+    s = make_plan(a.l, a.m, a.k, aligned_for_fast(a.A, a.sfA, a.x, a.sfx), nullptr, &p);
+    if (s != NVFP4_GEMV_OK) return s;
+    void *ws = nullptr;
+    if (p.ws_bytes > 0) {
+        if (p.ws_bytes > kNoAllocScratchBytes) return NVFP4_GEMV_ERR_WORKSPACE;
+        int dev = -1;
+        if (!be.device(&dev)) return NVFP4_GEMV_ERR_DEVICE;
+        ws = be.scratch(dev);
+        if (!ws) return NVFP4_GEMV_ERR_WORKSPACE;
+    }
+    return be.run(p, a, ws, stream);
 }
 
 }  // namespace nvfp4plan

@@ -7,7 +7,7 @@
 // Batched GEMV 概念阐述").  The kernels and their design are in
 // gemv_kernels.h; the validation and launch plan, shared with the host-only
 // checks, in gemv_plan.h.  This file maps plans to kernel launches, owns the
-// per-stream split-K workspaces, and defines the
+// per-stream split-K workspaces and the fixed scratch array, and defines the
 // C entry points of include/nvfp4_gemv.h.
 #include <hip/hip_runtime.h>
 
@@ -123,6 +123,14 @@ bool stream_capturing(void *stream) {
     return cs != hipStreamCaptureStatusNone;
 }
 
+// Device addresses of the fixed scratch array, one per device, taken once
+// with that device current (each GPU holds its own copy of the array).
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+void *scratch_address(int dev);
+
 // The library's backend for the launch orchestration of gemv_plan.h.
 struct HipBackend {
     bool device(int *dev) {
@@ -133,6 +141,7 @@ struct HipBackend {
     void *workspace(int dev, void *stream, size_t need) {
         return nvfp4_stream_workspace(dev, stream, need);
     }
+    void *scratch(int dev) { return scratch_address(dev); }
     int run(const Plan &p, const GemvArgs &g, void *ws, void *stream) {
         return ::run(p, g, ws, static_cast<hipStream_t>(stream));
     }
@@ -153,6 +162,27 @@ GemvArgs gemv_args(const uint8_t *A, const uint8_t *sfA, const uint8_t *x, const
     return g;
 }
 
+}  // namespace
+
+// Split-K partial sums of nvfp4_gemv_launch_noalloc.  Host code never passes
+// this name to a kernel or a copy: on the host it is only a stand-in for the
+// symbol, and the device address comes from hipGetSymbolAddress.
+static __device__ __align__(256) float scratch[kNoAllocScratchBytes / sizeof(float)];
+
+namespace {
+void *scratch_address(int dev) {
+    if (dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_ptr[dev]) {
+        void *ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) {
+            (void)hipGetLastError();
+            return nullptr;
+        }
+        g_scratch_ptr[dev] = ptr;
+    }
+    return g_scratch_ptr[dev];
+}
 }  // namespace
 
 void *nvfp4_stream_workspace(int dev, void *stream, size_t need) {
@@ -254,6 +284,14 @@ int nvfp4_gemv_launch(const uint8_t *A_packed, const uint8_t *sfA, const uint8_t
     HipBackend be;
     return launch_owned_workspace(be, gemv_args(A_packed, sfA, x_packed, sfx, alpha, c, l, m, k),
                                   stream);
+}
+
+int nvfp4_gemv_launch_noalloc(const uint8_t *A_packed, const uint8_t *sfA,
+                              const uint8_t *x_packed, const uint8_t *sfx, const float *alpha,
+                              uint16_t *c, int64_t l, int64_t m, int64_t k, void *stream) {
+    HipBackend be;
+    return launch_fixed_scratch(be, gemv_args(A_packed, sfA, x_packed, sfx, alpha, c, l, m, k),
+                                stream);
 }
 
 int nvfp4_workspace_reserve(size_t bytes, void *stream) {

@@ -31,8 +31,9 @@ int g_failures = 0;
 struct MockBackend {
     bool has_device = true;
     bool workspace_ok = true;
+    bool scratch_ok = true;
     bool launch_ok = true;
-    int device_calls = 0, workspace_calls = 0, run_calls = 0;
+    int device_calls = 0, workspace_calls = 0, scratch_calls = 0, run_calls = 0;
     size_t last_need = 0;
     void *last_ws = nullptr;
     Plan last_plan{};
@@ -48,6 +49,10 @@ struct MockBackend {
         last_need = need;
         if (!workspace_ok || need > ws_memory.size()) return nullptr;
         return ws_memory.data();
+    }
+    void *scratch(int) {
+        ++scratch_calls;
+        return scratch_ok ? ws_memory.data() : nullptr;
     }
     int run(const Plan &p, const GemvArgs &, void *ws, void *) {
         ++run_calls;
@@ -247,6 +252,55 @@ void workspace_and_launch_failures() {
     }
 }
 
+void fixed_scratch_entry() {
+    const GemvArgs split = args(1, 896, 16384);
+    {
+        MockBackend be;   // fits: the scratch array is used, nothing else
+        CHECK(launch_fixed_scratch(be, split, nullptr) == NVFP4_GEMV_OK);
+        CHECK(be.scratch_calls == 1 && be.workspace_calls == 0 && be.run_calls == 1);
+        CHECK(be.last_ws == be.ws_memory.data() && be.last_plan.ksplit > 1);
+    }
+    {
+        MockBackend be;   // no split: no scratch, no device query
+        CHECK(launch_fixed_scratch(be, args(1, 7168, 16384), nullptr) == NVFP4_GEMV_OK);
+        CHECK(be.scratch_calls == 0 && be.device_calls == 0 && be.last_ws == nullptr);
+    }
+    {
+        // partial sums larger than the array: refused before the backend is asked
+        MockBackend be;
+        const GemvArgs big = args(1, 524352, 32768);
+        Plan p;
+        CHECK(make_plan(1, 524352, 32768, true, nullptr, &p) == NVFP4_GEMV_OK);
+        CHECK(p.ws_bytes > kNoAllocScratchBytes);
+        CHECK(launch_fixed_scratch(be, big, nullptr) == NVFP4_GEMV_ERR_WORKSPACE);
+        CHECK(be.device_calls == 0 && be.scratch_calls == 0 && be.run_calls == 0);
+        // the largest such shape that fits is accepted
+        const GemvArgs fits = args(1, 524288, 32768);
+        CHECK(make_plan(1, 524288, 32768, true, nullptr, &p) == NVFP4_GEMV_OK);
+        CHECK(p.ws_bytes == kNoAllocScratchBytes);
+        CHECK(launch_fixed_scratch(be, fits, nullptr) == NVFP4_GEMV_OK);
+    }
+    {
+        MockBackend be;
+        be.scratch_ok = false;
+        CHECK(launch_fixed_scratch(be, split, nullptr) == NVFP4_GEMV_ERR_WORKSPACE);
+        be.scratch_ok = true;
+        be.has_device = false;
+        CHECK(launch_fixed_scratch(be, split, nullptr) == NVFP4_GEMV_ERR_DEVICE);
+        be.has_device = true;
+        be.launch_ok = false;
+        CHECK(launch_fixed_scratch(be, split, nullptr) == NVFP4_GEMV_ERR_LAUNCH);
+        CHECK(be.workspace_calls == 0);
+    }
+    {
+        MockBackend be;
+        GemvArgs a = split;
+        a.sfx = nullptr;
+        CHECK(launch_fixed_scratch(be, a, nullptr) == NVFP4_GEMV_ERR_NULL_POINTER);
+        CHECK(be.device_calls == 0 && be.scratch_calls == 0 && be.run_calls == 0);
+    }
+}
+
 void overlap_near_the_top_of_the_address_space() {
     const void *top = reinterpret_cast<const void *>(UINTPTR_MAX - 15);
     const void *below = reinterpret_cast<const void *>(UINTPTR_MAX - 31);
@@ -264,6 +318,7 @@ int main() {
     the_headline_workloads_plan_as_measured();
     validation_comes_before_any_backend_call();
     workspace_and_launch_failures();
+    fixed_scratch_entry();
     overlap_near_the_top_of_the_address_space();
     if (g_failures) {
         std::printf("plan_check: %d failed checks\n", g_failures);

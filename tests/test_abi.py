@@ -496,3 +496,24 @@ def test_split_k_launch_without_a_device(lib):
     need = lib.nvfp4_gemv_workspace_size(1, 896, 16384)
     assert need > 0
     assert call(l=1, m=896, k=16384) == pd.NVFP4_GEMV_ERR_DEVICE
+
+
+@fake_pointers
+def test_noalloc_validation_and_size_limit(lib):
+    f = lib.nvfp4_gemv_launch_noalloc
+    assert f(None, SA, X, SX, AL, C, 1, 8, 64, None) == pd.NVFP4_GEMV_ERR_NULL_POINTER
+    assert f(A, SA, X, SX, AL, C, 1, 8, 40, None) == pd.NVFP4_GEMV_ERR_BAD_SHAPE
+    assert f(A, SA, X, SX, AL, A + 2, 1, 8, 64, None) == pd.NVFP4_GEMV_ERR_ALIAS
+    # partial sums above the fixed array: refused before any device query
+    l, m, k = 1, 524352, 32768
+    assert pd.nvfp4_gemv_workspace_size(l, m, k) > pd.NVFP4_GEMV_NOALLOC_SCRATCH_BYTES
+    big = (1 << 44, 2 << 44, 3 << 44, 4 << 44, 5 << 44, 6 << 44)
+    assert f(*big, l, m, k, None) == pd.NVFP4_GEMV_ERR_WORKSPACE
+    # a split that fits reaches the device query (none here)
+    assert f(A, SA, X, SX, AL, C, 1, 896, 16384, None) == pd.NVFP4_GEMV_ERR_DEVICE
+
+
+def test_noalloc_limit_matches_header():
+    text = open(os.path.join(ROOT, "include", "nvfp4_gemv.h")).read()
+    assert "#define NVFP4_GEMV_NOALLOC_SCRATCH_BYTES ((size_t)4 << 20)" in text
+    assert pd.NVFP4_GEMV_NOALLOC_SCRATCH_BYTES == 4 << 20
