@@ -19,12 +19,13 @@ reads its operands from HBM; a cache-resident ("warm") figure is reported
 separately and labelled as such.
 
 Timing: W warm-up steps, then a synchronisation, then exactly K steps between
-two HIP events on the launch stream, then a synchronisation.  With --launch
-graph (the default) the K steps are captured once into a HIP graph, replayed
-once untimed, and the timed region is one replay; with --launch stream they
-are launched one by one from Python.  Either way a GPU-side delay kernel runs
-before the start event, so the stream is not idle while the host enqueues
-the first steps.
+two HIP events on the launch stream, then a synchronisation.  A GPU-side
+delay kernel (about 0.8 ms) runs before the start event, so the stream is not
+idle while the host enqueues the first steps and the clocks have left their
+idle state.  With --launch stream (the default) the K steps are launched one
+by one from Python; the same K steps are also captured once into a HIP graph,
+replayed once untimed and timed as one replay, and both figures are
+reported (--launch graph makes the replay the headline figure).
 
 Each JSON line:
   value        algorithmic bytes per step (A + sfA + x + sfx + c) / time, GB/s
@@ -76,7 +77,7 @@ METRIC = "achieved HBM GB/s and % of MI355X peak for NVFP4 batched GEMV; \u00b5s
 # GEMV workloads of --config all, in print order: the batched workload's line last
 GEMV_ORDER = ("tiny", "decode", "shortk", "gaussian", "batched")
 # GPU-side delay before a timed region (clock cycles of torch's spin kernel)
-PREROLL_CYCLES = 200_000
+PREROLL_CYCLES = 2_000_000
 # at most this many input copies (the tiny workload would otherwise need 50000)
 MAX_REPLICAS = 64
 CSRC = os.path.join(ROOT, "precision_decode_amd", "csrc")
@@ -101,7 +102,7 @@ def parse_args(argv=None):
                    help="GEMV workload from workloads.CONFIGS (decode, batched, shortk, tiny, or "
                         "gaussian: bf16 draws quantised by the library's device quantiser, untimed), "
                         "or all: each in turn, one JSON line each, batched last")
-    p.add_argument("--launch", default="graph", choices=["graph", "stream"],
+    p.add_argument("--launch", default="stream", choices=["graph", "stream"],
                    help="GEMV: time the K steps as one replay of a HIP graph that holds them, or "
                         "launched one by one on the stream")
     p.add_argument("--trace-cold", action="store_true",
@@ -441,7 +442,7 @@ def bench_gemv(args, torch, np, pd, workloads, name=None, shared=None):
     print(f"[bench] gemv, stream launches: {args.steps} steps: {stream_us:.2f} us/step "
           f"({nbytes / stream_us / 1e3:.1f} GB/s), host enqueue {enqueue_us:.2f} us/step", flush=True)
     graph_us = None
-    if args.launch == "graph":
+    if not args.trace_cold or args.launch == "graph":
         g = capture_steps(torch, args.steps, step, state)
         g.replay()                                   # untimed: uploads the graph
         torch.cuda.synchronize()
@@ -449,7 +450,7 @@ def bench_gemv(args, torch, np, pd, workloads, name=None, shared=None):
         graph_us = ms_total / args.steps * 1e3
         print(f"[bench] gemv, one graph replay of {args.steps} steps: {graph_us:.2f} us/step "
               f"({nbytes / graph_us / 1e3:.1f} GB/s)", flush=True)
-    us_step = graph_us if graph_us is not None else stream_us
+    us_step = graph_us if args.launch == "graph" else stream_us
     ms_step = us_step * 1e-3
     gbs = nbytes / (ms_step * 1e-3) / 1e9
     print(f"[bench] gemv {cfg.name}: {us_step:.2f} us/step, {gbs:.1f} GB/s "
@@ -512,7 +513,7 @@ def bench_gemv(args, torch, np, pd, workloads, name=None, shared=None):
     out["config"] = {"workload": f"{cfg.name}: NVFP4 GEMV l={l} m={m} k={k}, {inputs} ({cfg.note})",
                      "l": l, "m": m, "k": k, "bytes_per_step": nbytes,
                      "replicas": reps, "operands": operands,
-                     "launch": ("one HIP graph replay of the K steps" if graph_us is not None
+                     "launch": ("one HIP graph replay of the K steps" if args.launch == "graph"
                                 else "K stream launches"),
                      "plan": {"path": plan.path, "variant": plan.variant, "ksplit": plan.ksplit}}
     out["timing_us"] = {"graph_replay": None if graph_us is None else round(graph_us, 3),

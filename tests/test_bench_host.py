@@ -9,7 +9,7 @@ import bench
 
 def test_defaults_time_every_gemv_workload_batched_last():
     a = bench.parse_args([])
-    assert a.gpus == 1 and a.path == "gemv" and a.config == "all" and a.launch == "graph"
+    assert a.gpus == 1 and a.path == "gemv" and a.config == "all" and a.launch == "stream"
     assert a.steps > 0 and a.warmup > 0 and a.single_launches > 0 and not a.trace_cold
     import workloads
     assert set(bench.GEMV_ORDER) == set(workloads.CONFIGS)
