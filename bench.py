@@ -84,7 +84,7 @@ CSRC = os.path.join(ROOT, "precision_decode_amd", "csrc")
 PROFILES = os.path.join(ROOT, "profiles")
 # counter summaries under profiles/ are valid only for the source they were taken on
 # (the GEMV's device code is gemv_kernels.h with its helpers in device_common.h)
-KERNEL_SOURCES = {"gemv_fast": ("gemv_kernels.h", "device_common.h"),
+KERNEL_SOURCES = {"gemv": ("gemv_kernels.h", "device_common.h"),
                   "quantize_blocks": ("nvfp4_quantize.hip", "device_common.h"),
                   "mma_stream": ("nvfp4_mma.hip", "device_common.h"),
                   "vec_tile": ("nvfp4_mma.hip", "device_common.h"),
@@ -139,7 +139,7 @@ def parse_args(argv=None):
     return p.parse_args(argv)
 
 
-def kernel_source_hash(kernel: str = "gemv_fast") -> str:
+def kernel_source_hash(kernel: str = "gemv") -> str:
     h = hashlib.sha256()
     for name in KERNEL_SOURCES[kernel]:
         with open(os.path.join(CSRC, name), "rb") as f:
@@ -147,7 +147,7 @@ def kernel_source_hash(kernel: str = "gemv_fast") -> str:
     return h.hexdigest()[:16]
 
 
-def recorded_traffic(config: str, kernel: str = "gemv_fast"):
+def recorded_traffic(config: str, kernel: str = "gemv"):
     """HBM bytes per launch from a committed counter summary, if it was taken
     on the current kernel source; otherwise None."""
     path = os.path.join(PROFILES, f"{kernel}_{config}_hbm_counters.txt")

@@ -75,9 +75,9 @@ def test_roofline_fields():
 def test_recorded_traffic_needs_the_current_source(tmp_path, monkeypatch):
     monkeypatch.setattr(bench, "PROFILES", str(tmp_path))
     assert bench.recorded_traffic("decode") is None                     # no file
-    h = bench.kernel_source_hash("gemv_fast")
+    h = bench.kernel_source_hash("gemv")
     assert len(h) == 16 and h != bench.kernel_source_hash("mma_stream")
-    f = tmp_path / "gemv_fast_decode_hbm_counters.txt"
+    f = tmp_path / "gemv_decode_hbm_counters.txt"
     f.write_text(f"kernel_source_sha256_16: {h}\nhbm_bytes_per_launch: 66291018\n")
     assert bench.recorded_traffic("decode") == 66291018.0
     f.write_text("kernel_source_sha256_16: 0000000000000000\nhbm_bytes_per_launch: 1\n")
