@@ -270,7 +270,8 @@ def run_copies(torch, mib):
 def roofline(gbs, traffic, **extra):
     r = {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
          "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic}
-    r.update({k: (round(v, 2) if isinstance(v, float) else v) for k, v in extra.items()})
+    r.update({k: (round(v, 4 if k.startswith("frac") else 2) if isinstance(v, float) else v)
+              for k, v in extra.items()})
     return r
 
 
@@ -388,6 +389,25 @@ def row_probe_gbs(torch, pd, timer, sptr, replicas, l, m, k):
     return gbs
 
 
+def flat_probe_same_size_gbs(torch, pd, timer, sptr, nbytes):
+    """The flat streaming-read probe over contiguous copies of `nbytes` (the
+    workload's A and sfA together), rotated over >= 1 GB: the read rate of a
+    plain sequential read of this size, operands in HBM."""
+    nb = -(-nbytes // 16) * 16
+    reps = max(2, -(-1_000_000_000 // nb))
+    bufs = [torch.ones(nb, dtype=torch.uint8, device="cuda") for _ in range(reps)]
+    sink = torch.empty(4096, dtype=torch.int32, device="cuda")
+    for i in range(reps):
+        pd.nvfp4_hbm_read_probe(bufs[i], nb, sink, sptr)
+    pn = max(8, 4 * reps)
+    pms, _ = timer(pn, lambda i: pd.nvfp4_hbm_read_probe(bufs[i % reps], nb, sink, sptr))
+    gbs = nb / (pms / pn * 1e-3) / 1e9
+    del bufs
+    print(f"[bench] flat read probe over {nb / 1e6:.1f} MB copies (rotated): {gbs:.1f} GB/s "
+          f"({pms / pn * 1e3:.2f} us per read)", flush=True)
+    return gbs
+
+
 def bench_gemv(args, torch, np, pd, workloads, name=None, shared=None):
     shared = {} if shared is None else shared
     cfg = workloads.CONFIGS[name or args.config]
@@ -458,7 +478,7 @@ def bench_gemv(args, torch, np, pd, workloads, name=None, shared=None):
     # the last timed call's output, before anything else writes c
     got = c.cpu().numpy().view(np.uint16).copy()
 
-    warm_gbs = single = probe_gbs = probe_rows = None
+    warm_gbs = single = probe_gbs = probe_rows = probe_flat = None
     if not args.trace_cold:
         nw = min(args.steps, 500)
         warm_ms, _ = timer(nw, lambda i: step(0))
@@ -472,6 +492,8 @@ def bench_gemv(args, torch, np, pd, workloads, name=None, shared=None):
         if not args.no_probe:
             probe_gbs = flat_probe_gbs(torch, pd, timer, state["stream"], shared)
             probe_rows = row_probe_gbs(torch, pd, timer, state["stream"], replicas, l, m, k)
+            probe_flat = flat_probe_same_size_gbs(torch, pd, timer, state["stream"],
+                                                  l * m * (k // 2 + k // 16))
     run_copies(torch, args.copy_mib)
 
     cpu = None
@@ -519,8 +541,12 @@ def bench_gemv(args, torch, np, pd, workloads, name=None, shared=None):
     out["timing_us"] = {"graph_replay": None if graph_us is None else round(graph_us, 3),
                         "stream_launches": round(stream_us, 3),
                         "host_enqueue_per_launch": round(enqueue_us, 3)}
+    # the GEMV's rate against the best read probe of its own size, in the same run
+    best = max([g for g in (probe_rows, probe_flat) if g] or [0.0]) or None
     out["roofline"] = roofline(gbs, recorded_traffic(cfg.name), kernel=plan_kernel_name(pd, plan),
                                probe_read_gbs=probe_gbs, probe_rows_same_size_gbs=probe_rows,
+                               probe_flat_same_size_gbs=probe_flat,
+                               frac_of_best_same_size_probe=(gbs / best) if best else None,
                                cache_resident_gbs=warm_gbs)
     out["single_launch_us"] = single
     out["cpu_baseline"] = with_speedup(cpu, gbs)
