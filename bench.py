@@ -220,11 +220,12 @@ class Timer:
         return start.elapsed_time(end), time.perf_counter() - t0
 
 
-def capture_steps(torch, n, step, state):
-    """A HIP graph holding steps 0 .. n-1, captured on a side stream (nothing
-    runs).  `state["stream"]` is the stream the step function launches on."""
+def capture_steps(torch, n, step, state, cs=None):
+    """A HIP graph holding steps 0 .. n-1, captured on the side stream `cs`
+    (a new one when None; nothing runs).  `state["stream"]` is the stream the
+    step function launches on."""
     g = torch.cuda.CUDAGraph()
-    cs = torch.cuda.Stream()
+    cs = torch.cuda.Stream() if cs is None else cs
     main = torch.cuda.current_stream()
     cs.wait_stream(main)
     try:
@@ -433,8 +434,11 @@ def bench_gemv(args, torch, np, pd, workloads, name=None, shared=None):
     tuning = {"variant": args.variant, "ksplit": args.ksplit}
     plan, ws_bytes = pd.nvfp4_gemv_plan(l, m, k, aligned=True, tuning=tuning if tuned else None)
     ws = torch.empty(max(ws_bytes, 4), dtype=torch.uint8, device="cuda")
+    capture_stream = torch.cuda.Stream()
     if not tuned and ws_bytes:
-        pd.nvfp4_workspace_reserve(ws_bytes, stream)   # before any capture
+        # the library's split-K workspace, sized before any capture on both streams
+        pd.nvfp4_workspace_reserve(ws_bytes, stream)
+        pd.nvfp4_workspace_reserve(ws_bytes, capture_stream)
 
     def step(i):
         r = replicas[i % reps]
@@ -463,7 +467,7 @@ def bench_gemv(args, torch, np, pd, workloads, name=None, shared=None):
           f"({nbytes / stream_us / 1e3:.1f} GB/s), host enqueue {enqueue_us:.2f} us/step", flush=True)
     graph_us = None
     if not args.trace_cold or args.launch == "graph":
-        g = capture_steps(torch, args.steps, step, state)
+        g = capture_steps(torch, args.steps, step, state, capture_stream)
         g.replay()                                   # untimed: uploads the graph
         torch.cuda.synchronize()
         ms_total, wall = timer(1, lambda i: g.replay())
