@@ -531,7 +531,8 @@ gemv_fastg(const uint8_t *__restrict__ A, const uint8_t *__restrict__ sfA,
 // rows its half or row is responsible for and adds its partner's values),
 // then the TR/4 values left are summed inside each 16-lane row by DPP.  The
 // waves' row sums meet in LDS and wave 0 adds them in wave order, so the
-// result does not depend on timing.
+// result does not depend on timing; a one-wave tile writes its rows from the
+// lanes that hold them.
 constexpr int kTileMaxWaves = 8;
 
 template <int W, int TR>
@@ -631,13 +632,26 @@ gemv_tile(const uint8_t *__restrict__ A, const uint8_t *__restrict__ sfA,
     // Lane j < TR/4 of 16-lane row q (q = lane / 16) holds tile row
     // j + (TR/4) (q & 1) + (TR/2) (q >> 1).
     const int j = lane & 15, q = lane >> 4;
-    if (j < Q) {
-        float v = h4[0];
+    const int trow = j + Q * (q & 1) + H * (q >> 1);
+    float tv = h4[0];
 #pragma unroll
-        for (int r = 1; r < Q; ++r)
-            if (j == r) v = h4[r];
-        red[wave * TR + j + Q * (q & 1) + H * (q >> 1)] = v;
+    for (int r = 1; r < Q; ++r)
+        if (j == r) tv = h4[r];
+    if constexpr (W == 1) {
+        // one wave: those lanes write their rows themselves (no LDS round trip
+        // before the kernel's last stores)
+        if (j < Q && trow < nrows) {
+            const int64_t row = row0 + trow;
+            if (part != nullptr) {
+                part[(split * l + b) * m + row] = tv;
+            } else {
+                const float al = alpha ? alpha[b] : 1.0f;
+                c[b * m + row] = f16_of_product(al, tv);
+            }
+        }
+        return;
     }
+    if (j < Q) red[wave * TR + trow] = tv;
     __syncthreads();
     if (wave == 0 && lane < nrows) {
         float v = red[lane];
