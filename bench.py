@@ -87,6 +87,8 @@ PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = {"gemv": ("gemv_kernels.h", "device_common.h"),
                   "quantize_blocks": ("nvfp4_quantize.hip", "device_common.h"),
                   "mma_stream": ("nvfp4_mma.hip", "device_common.h"),
+                  "mma_lds": ("nvfp4_mma.hip", "device_common.h"),
+                  "mma_generic": ("nvfp4_mma.hip", "device_common.h"),
                   "vec_tile": ("nvfp4_mma.hip", "device_common.h"),
                   "mma_stream_packed": ("nvfp4_mma.hip", "device_common.h")}
 
@@ -131,7 +133,7 @@ def parse_args(argv=None):
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-probe", action="store_true")
     p.add_argument("--single-launches", type=int, default=50,
-                   help="GEMV: single launches, each after a 512 MiB scratch write, for per-launch "
+                   help="GEMV: single launches, each after a 512 MiB streaming read, for per-launch "
                         "latency percentiles (0 = skip)")
     p.add_argument("--copy-mib", type=int, default=0,
                    help="after timing, run 4 plain device copies of this many MiB (the "
@@ -161,16 +163,21 @@ def recorded_traffic(config: str, kernel: str = "gemv"):
     return float(t.group(1))
 
 
-def single_launch_percentiles(torch, stream, step, n):
+def single_launch_percentiles(torch, stream, step, n, evict=None):
     """p10/p50/p90 of single launches (HIP events on the launch stream around one
-    step), each after a 512 MiB write that evicts the operands from L2 and the
-    Infinity Cache, so each launch starts cold and alone."""
+    step).  Before each launch `evict(i)` runs on the same stream; by default it
+    writes 512 MiB.  The GEMV bench passes a 512 MiB streaming read instead, which
+    evicts the operands from L2 and the Infinity Cache without leaving dirty
+    lines there, so each launch starts cold and alone."""
     if n <= 0:
         return None
-    scratch = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    scratch = None
+    if evict is None:
+        scratch = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+        evict = lambda i: scratch.fill_(i & 0xFF)
     times = []
     for i in range(n):
-        scratch.fill_(i & 0xFF)
+        evict(i)
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record(stream)
@@ -489,9 +496,15 @@ def bench_gemv(args, torch, np, pd, workloads, name=None, shared=None):
         warm_gbs = nbytes / (warm_ms / nw * 1e-3) / 1e9
         print(f"[bench] cache-resident (same buffers every step): {warm_gbs:.1f} GB/s", flush=True)
 
-        single = single_launch_percentiles(torch, stream, step, args.single_launches)
+        ebytes = 512 << 20
+        ebuf = torch.ones(ebytes, dtype=torch.uint8, device="cuda")
+        esink = torch.empty(4096, dtype=torch.int32, device="cuda")
+        single = single_launch_percentiles(
+            torch, stream, step, args.single_launches,
+            evict=lambda i: pd.nvfp4_hbm_read_probe(ebuf, ebytes, esink, state["stream"]))
+        del ebuf
         if single:
-            print(f"[bench] single launches after a 512 MiB scratch write: p10 {single['p10']} us, "
+            print(f"[bench] single launches after a 512 MiB streaming read: p10 {single['p10']} us, "
                   f"p50 {single['p50']} us, p90 {single['p90']} us", flush=True)
         if not args.no_probe:
             probe_gbs = flat_probe_gbs(torch, pd, timer, state["stream"], shared)
@@ -557,6 +570,18 @@ def bench_gemv(args, torch, np, pd, workloads, name=None, shared=None):
     if cpu is not None:
         out["parity"] = cpu["parity"]
     return out
+
+
+def mma_kernel_name(pd, plan, packed):
+    """The kernel a small-N or grouped plan runs, by its committed-profile
+    name: matrix cores on packed weights, or by the variant's form."""
+    if packed:
+        return "mma_stream_packed"
+    if plan.path != pd.NVFP4_GEMV_PATH_FAST:
+        return "mma_generic"
+    form = pd.nvfp4_mma_variant_form(plan.variant)
+    return {pd.NVFP4_MMA_FORM_VALU_TILES: "vec_tile",
+            pd.NVFP4_MMA_FORM_LDS_STAGED: "mma_lds"}.get(form, "mma_stream")
 
 
 def plan_kernel_name(pd, plan):
@@ -752,11 +777,8 @@ def bench_smalln(args, torch, np, pd, workloads):
                                 else "row-major"}
     if args.packed:
         del out["config"]["plan"]
-    # the plan's kernel: matrix cores (mma_stream) or VALU row tiles (vec_tile)
-    valu = not args.packed and plan.path == pd.NVFP4_GEMV_PATH_FAST and \
-        pd.nvfp4_mma_variant_form(plan.variant) == pd.NVFP4_MMA_FORM_VALU_TILES
-    kernel = "mma_stream_packed" if args.packed else "vec_tile" if valu else "mma_stream"
-    extra = {} if valu else {"mfma_tflops": flops / (ms_step * 1e-3) / 1e12}
+    kernel = mma_kernel_name(pd, plan, args.packed)
+    extra = {} if kernel == "vec_tile" else {"mfma_tflops": flops / (ms_step * 1e-3) / 1e12}
     out["roofline"] = roofline(gbs, recorded_traffic(cfg.name, kernel), kernel=kernel, **extra)
     out["cpu_baseline"] = with_speedup(cpu, gbs)
     return out
@@ -824,8 +846,12 @@ def bench_grouped(args, torch, np, pd, workloads):
                      "replicas": reps, "operands": "HBM (rotated over >= 1 GB of copies)",
                      "weights": "packed once by nvfp4_mma_pack_weight (not timed)" if args.packed
                                 else "row-major"}
-    out["roofline"] = roofline(gbs, recorded_traffic(
-        cfg.name, "mma_stream_packed" if args.packed else "mma_stream"))
+    plan = pd.nvfp4_grouped_gemv_plan(E, n, k, packed=args.packed,
+                                      tuning={"variant": args.variant} if args.variant else None)
+    kernel = mma_kernel_name(pd, plan, args.packed)
+    out["config"]["plan"] = {"path": plan.path, "variant": plan.variant,
+                             "rows_per_block": plan.rows_per_block}
+    out["roofline"] = roofline(gbs, recorded_traffic(cfg.name, kernel), kernel=kernel)
     out["cpu_baseline"] = with_speedup(cpu, gbs)
     return out
 

@@ -99,6 +99,7 @@ int nvfp4_gemm_smalln_launch(const uint8_t *A_packed, const uint8_t *sfA,
 
 #define NVFP4_MMA_FORM_MATRIX_CORES 0
 #define NVFP4_MMA_FORM_VALU_TILES 1
+#define NVFP4_MMA_FORM_LDS_STAGED 2
 
 /*
  * Number of fast small-N / grouped kernel variants, and the shape of variant
@@ -113,7 +114,15 @@ int nvfp4_gemm_smalln_launch(const uint8_t *A_packed, const uint8_t *sfA,
  *    K slice of 2048 elements, 1 KiB of every row per load).  The products
  *    run on the VALU; more vectors than one pass holds mean another pass over
  *    the tile's rows.  These variants never split K: an explicit ksplit above
- *    1 or rows_per_block above the tile's rows is BAD_TUNING.
+ *    1 or rows_per_block above the tile's rows is BAD_TUNING;
+ *  - NVFP4_MMA_FORM_LDS_STAGED: the matrix-core products with every operand
+ *    (weight and vector codes per window, block scales per 4 windows) copied
+ *    into LDS by whole-line direct-to-LDS loads and read back in the
+ *    matrix-core lane order; the numbers are row tiles per wave, windows in
+ *    flight and waves (each wave takes a contiguous run of the workgroup's
+ *    windows, so on inexact data the fp32 sums may round differently from a
+ *    MATRIX_CORES variant).  Row-major weights only: with packed weights
+ *    these variants are BAD_TUNING.
  * Each returns a status (BAD_TUNING for v outside 1 .. num_variants,
  * NULL_POINTER for a NULL output).
  */
@@ -143,6 +152,19 @@ int nvfp4_gemm_smalln_launch_tuned(const uint8_t *A_packed, const uint8_t *sfA,
                                    int64_t l, int64_t m, int64_t n, int64_t k,
                                    int32_t out_type, const nvfp4_mma_tuning_t *tuning,
                                    void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * The grouped plan the library would use (path, variant, K split (always 1),
+ * rows per workgroup; the last three 0 for the generic kernel) for `experts`
+ * weight matrices of n x k, as nvfp4_gemm_smalln_plan does for the small-N
+ * GEMM; `in` may be NULL.  `packed` != 0 asks for the plan of the packed-weight
+ * launch (then `aligned` is ignored: packed operands are aligned by
+ * definition), else `aligned` says whether the pointers meet the fast
+ * kernels' alignment rules.  Returns a status (BAD_SHAPE as the matching
+ * launch would, BAD_TUNING, NULL_POINTER for a NULL out).
+ */
+int nvfp4_grouped_gemv_plan(int64_t experts, int64_t n, int64_t k, int aligned, int packed,
+                            const nvfp4_mma_tuning_t *in, nvfp4_mma_tuning_t *out);
 
 /*
  * The grouped (MoE) GEMV above.  Never splits K and needs no workspace.

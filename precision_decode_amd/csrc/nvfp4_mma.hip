@@ -33,11 +33,13 @@
 //    balanced by splitting K across workgroups (small-N GEMM only), with fp32
 //    partials added in split order by a second kernel.
 //
-// Two other forms sit beside it: weights packed once into the order the
-// lanes read them (mma_pack_weight; every load instruction then reads 1 KiB
-// contiguously instead of 16 rows x 64 bytes), and, for one or two vectors,
-// VALU row tiles that read the row-major weights row-contiguously and take
-// the few dot products themselves (vec_tile).
+// Three other forms sit beside it: the same products fed through LDS by
+// whole-line direct-to-LDS copies (mma_lds, the default for row-major
+// weights), weights packed once into the order the lanes read them
+// (mma_pack_weight; every load instruction then reads 1 KiB contiguously
+// instead of 16 rows x 64 bytes), and, for one or two vectors, VALU row tiles
+// that read the row-major weights row-contiguously and take the few dot
+// products themselves (vec_tile).
 //
 // Every accumulator starts at +0.0, so an exactly-zero result is +0.  With
 // integer-coded inputs (E2M1 values times scales 0, 1, 2) every partial sum is
@@ -47,6 +49,7 @@
 #include <climits>
 #include <cstddef>
 #include <cstdint>
+#include <type_traits>
 
 #include "device_common.h"
 #include "nvfp4_gemv.h"
@@ -296,6 +299,366 @@ __global__ void __launch_bounds__(W * kWave) mma_stream(const MmaArgs a) {
         }
 
         // Tiles of waves 1..W-1 through LDS, added to wave 0's in wave order.
+        if (W > 1) {
+            if (wave > 0) {
+#pragma unroll
+                for (int r = 0; r < R; ++r) red[((wave - 1) * R + r) * kWave + lane] = acc[r];
+            }
+            __syncthreads();
+        }
+        if (wave == 0) {
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                f32x4 s = acc[r];
+                for (int w = 1; w < W; ++w) s += red[((w - 1) * R + r) * kWave + lane];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    if (GROUPED) {
+                        const int64_t t = vp + kq * 4 + e;
+                        const int rr = r * kTile + li;
+                        if (t < v1 && rr < nrows)
+                            a.c[t * a.rows + row0 + rr] = round_out(al, s[e], a.out_bf16);
+                    } else {
+                        const int rr = r * kTile + kq * 4 + e;
+                        const int64_t col = vp - v0 + li;
+                        if (rr < nrows && col < a.nvec) {
+                            const int64_t o = (grp * a.rows + row0 + rr) * a.nvec + col;
+                            if (a.part != nullptr)
+                                a.part[split * a.groups * a.rows * a.nvec + o] = s[e];
+                            else
+                                a.c[o] = round_out(al, s[e], a.out_bf16);
+                        }
+                    }
+                }
+            }
+        }
+        if (W > 1 && vp + kTile < v1) __syncthreads();   // before the next pass reuses `red`
+    }
+}
+
+// ---------------------------------------------------------------- LDS-staged operands
+// vmcnt wait with lgkmcnt and expcnt left at their maximum (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+__device__ __forceinline__ uint32_t lds_address(const uint8_t *p) {
+    return static_cast<uint32_t>(
+        reinterpret_cast<size_t>((__attribute__((address_space(3))) const uint8_t *)(p)));
+}
+
+constexpr int kGroupWins = 4;   // windows per staged scale group (64 scale bytes per row)
+
+// Loads issued after the last load of window j + 1, once window j + NS has
+// been issued, where j sits at position u of its group: windows j + 2 ..
+// j + NS, each with WL copies, plus SL scale copies where one starts a group.
+template <int NS, int WL, int SL>
+constexpr int loads_after_next(int u) {
+    int n = 0;
+    for (int t = 2; t <= NS; ++t) n += WL + ((u + t) % kGroupWins == 0 ? SL : 0);
+    return n;
+}
+
+// Position of 16-byte chunk c (0..7) of staged row rho in its 128-byte LDS
+// row.  The 16 rows that one quarter of a wave reads at the same chunk land
+// on 16 distinct positions, and so do the two halves of 8 rows.
+__device__ __forceinline__ int chunk_pos(int rho, int c) { return c ^ ((rho & 7) ^ ((rho >> 3) & 1)); }
+// Position of 4-byte scale word w (0..15: window w / 4 of the group, lane
+// piece w % 4) in the 64-byte scale row of staged row rho.  The 16 rows that
+// one quarter reads at the same word land in 16 distinct banks, and a whole
+// wave's read in 64.
+__device__ __forceinline__ int scale_pos(int rho, int w) { return w ^ (4 * ((rho >> 2) & 3)); }
+
+// One window's operands from LDS, in one asm block that waits for its own
+// reads (the outputs are early-clobber: a read that returns while later ones
+// are still being issued must not land in a register that holds one of their
+// addresses): the weight codes of row li of the R tiles and of vector li
+// (chunks 2kq and 2kq + 1, at addresses aw0, aw1 for tile 0; the next tile
+// and the vectors 2 KiB apart) and the matching scale words (address as,
+// tiles and vectors 1 KiB apart).  The compiler does not relate these reads to the
+// direct-to-LDS loads (the kernel orders them with explicit vmcnt waits);
+// with plain C++ reads it placed a full vmcnt(0) drain at the loop head.
+template <int R>
+__device__ __forceinline__ void lds_read_window(uint32_t aw0, uint32_t aw1, uint32_t as,
+                                                u32x4 (&wq)[R][2], u32x4 (&vq)[2],
+                                                uint32_t (&ws)[R], uint32_t &vs) {
+    static_assert(R == 1 || R == 2, "one or two row tiles per wave");
+    if constexpr (R == 2) {
+        asm volatile(
+            "ds_read_b128 %0, %9\n\t"
+            "ds_read_b128 %1, %10\n\t"
+            "ds_read_b128 %2, %9 offset:2048\n\t"
+            "ds_read_b128 %3, %10 offset:2048\n\t"
+            "ds_read_b128 %4, %9 offset:4096\n\t"
+            "ds_read_b128 %5, %10 offset:4096\n\t"
+            "ds_read_b32 %6, %11\n\t"
+            "ds_read_b32 %7, %11 offset:1024\n\t"
+            "ds_read_b32 %8, %11 offset:2048\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(wq[0][0]), "=&v"(wq[0][1]), "=&v"(wq[1][0]), "=&v"(wq[1][1]), "=&v"(vq[0]),
+              "=&v"(vq[1]), "=&v"(ws[0]), "=&v"(ws[1]), "=&v"(vs)
+            : "v"(aw0), "v"(aw1), "v"(as)
+            : "memory");
+    } else {
+        asm volatile(
+            "ds_read_b128 %0, %6\n\t"
+            "ds_read_b128 %1, %7\n\t"
+            "ds_read_b128 %2, %6 offset:2048\n\t"
+            "ds_read_b128 %3, %7 offset:2048\n\t"
+            "ds_read_b32 %4, %8\n\t"
+            "ds_read_b32 %5, %8 offset:1024\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(wq[0][0]), "=&v"(wq[0][1]), "=&v"(vq[0]), "=&v"(vq[1]), "=&v"(ws[0]), "=&v"(vs)
+            : "v"(aw0), "v"(aw1), "v"(as)
+            : "memory");
+    }
+}
+
+// The same products as mma_stream on row-major weights, with every operand
+// brought in by 16-byte direct-to-LDS buffer loads of whole 128-byte lines.
+// In mma_stream each load instruction covers 16 rows x 64 bytes (the shape
+// the matrix-core lanes want), and its scale and vector loads 16 rows x 16 or
+// 64 bytes, so the address units handle many partial lines per byte.  Here:
+//  * each wave takes a contiguous run of the workgroup's windows;
+//  * per window, 8 rows x 128 bytes per instruction: the R*16 weight rows,
+//    then the 16 vectors (one window slot of a per-wave LDS ring, NS slots);
+//  * per group of 4 windows, the block scales of those rows and vectors, 64
+//    bytes per row, into one of two scale slots: 16 rows per 16-byte copy
+//    when every scale row and group starts 16-byte aligned (S16), else 4 rows
+//    per 4-byte copy (scale rows are only 4-byte aligned in general, and a
+//    16-byte copy from a 4-byte aligned address does not return the
+//    addressed bytes);
+//  * one asm block of LDS reads per window gives every lane the same 32 code
+//    bytes and scale words that mma_stream's lane holds, so the decode and
+//    the MFMAs are mma_stream's.
+// Staged rows are swizzled (chunk_pos at 16 bytes, scale_pos at 4 bytes) so
+// the reads hit distinct banks.  A window's loads always number the same
+// (out-of-range ones read nothing but still count), so explicit vmcnt waits
+// say exactly when a window has landed; the compiler's own tracking does not
+// cover direct-to-LDS loads.  Lane pieces past the wave's K range get zero
+// scales; rows and vectors past the block's read zeros or stale LDS, which
+// only reach outputs that are never written (an MFMA output row or column
+// depends on its own row and vector alone, and e2m1 codes are finite).
+template <int R, int NS, int W, bool GROUPED, bool S16>
+__global__ void __launch_bounds__(W * kWave) mma_lds(const MmaArgs a) {
+    static_assert(NS == 2 || NS == 4, "window slots must divide a scale group");
+    constexpr int kRows = (R + 1) * kTile;               // staged rows: weight tiles, then vectors
+    constexpr int kWinSlot = kRows * (kWinElems / 2);    // 128 bytes per row and window
+    constexpr int kScaleSlot = kRows * kGroupWins * 16;  // 64 bytes per row and group
+    constexpr int kWinLoads = kRows / 8;                 // 1 KiB copies per window
+    // scale copies per group: 16 rows x 64 bytes each when every scale row
+    // and group start is 16-byte aligned (S16), else 4 rows x 64 bytes
+    constexpr int kScaleLoads = S16 ? kRows / 16 : kRows / 4;
+    constexpr int kWaveBytes = NS * kWinSlot + 2 * kScaleSlot;
+    static_assert(NS * kWinLoads + kScaleLoads <= 63, "loads in flight must fit the 6-bit vmcnt");
+    __shared__ __attribute__((aligned(16))) uint8_t ring[W * kWaveBytes];
+    __shared__ f32x4 red[(W > 1 ? W - 1 : 1) * R * kWave];
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int li = lane & (kTile - 1);
+    const int kq = lane >> 4;
+
+    const uint32_t gi = blockIdx.x;
+    const uint32_t rbs = static_cast<uint32_t>(a.row_blocks), gs = static_cast<uint32_t>(a.groups);
+    const uint32_t q = gi / rbs;
+    const int64_t rb = gi - q * rbs;
+    const int64_t grp = q % gs;
+    const int64_t split = q / gs;
+
+    int64_t v0, v1;
+    vector_range<GROUPED>(a, grp, &v0, &v1);
+    if (v1 <= v0) return;   // workgroup-uniform: an expert without tokens
+
+    // K positions fit 32 bits (k <= 2^26).  The wave's windows: a contiguous
+    // run [wbeg, wend) of the workgroup's, elements [kwb, kwe).
+    const int64_t k = a.k;
+    const uint32_t half = static_cast<uint32_t>(k / 2);
+    const uint32_t sixteenth = static_cast<uint32_t>(k / 16);
+    const int kb0 = static_cast<int>(split * a.kchunk);
+    const int kend = static_cast<int>((k - kb0 < a.kchunk) ? k : kb0 + a.kchunk);
+    const int nwin = (kend - kb0 + kWinElems - 1) / kWinElems;
+    const int wbeg = wave * nwin / W, wend = (wave + 1) * nwin / W;
+    const int niter = wend - wbeg;
+    const int kwb = kb0 + wbeg * kWinElems;
+    const int kwe = (kb0 + wend * kWinElems < kend) ? kb0 + wend * kWinElems : kend;
+
+    const int64_t row0 = rb * a.rows_per_block;
+    const int nrows = static_cast<int>((a.rows - row0 < a.rows_per_block) ? a.rows - row0 : a.rows_per_block);
+    const __amdgpu_buffer_rsrc_t wdesc =
+        buffer_of(a.W + (grp * a.rows + row0) * (k / 2), nrows * static_cast<int>(half));
+    const __amdgpu_buffer_rsrc_t swdesc =
+        buffer_of(a.sW + (grp * a.rows + row0) * (k / 16), nrows * static_cast<int>(sixteenth));
+    const float al = group_alpha(a, grp, GROUPED);
+    uint8_t *wring = ring + wave * kWaveBytes;      // NS window slots
+    uint8_t *sring = wring + NS * kWinSlot;         // 2 scale slots
+
+    // Copy lanes, per instruction: window copy n covers staged rows 8n ..
+    // 8n+7 (lane l: row 8n + l/8, chunk at position l & 7); a 4-byte scale
+    // copy s covers rows 4s .. 4s+3 (lane l: row 4s + l/16, word at position
+    // l & 15), a 16-byte one rows 16s .. 16s+15 (lane l: row 16s + l/4, the
+    // 4 words at positions 4 (l & 3) .. +3, one window's: scale_pos keeps a
+    // window's 4 words together).
+    // wbase/sbase: byte offsets without the window's or group's (rows past
+    // the block out of range); wlo/slo: the element offset of the chunk in
+    // its window, or of the word's window in its group.  Vector rows past the
+    // pass read zeros through their descriptor.
+    uint32_t wbase[kWinLoads], sbase[kScaleLoads];
+    int wlo[kWinLoads], slo[kScaleLoads];
+#pragma unroll
+    for (int n = 0; n < kWinLoads; ++n) {
+        const int rho = 8 * n + (lane >> 3);
+        int c = 0;
+        for (int t = 0; t < 8; ++t) if (chunk_pos(rho, t) == (lane & 7)) c = t;
+        const bool vec = n >= 2 * R;
+        const int row = vec ? rho - R * kTile : rho;
+        wbase[n] = (vec || row < nrows) ? static_cast<uint32_t>(row) * half + 16u * c : kOutOfRange;
+        wlo[n] = 32 * c;
+    }
+#pragma unroll
+    for (int sI = 0; sI < kScaleLoads; ++sI) {
+        const int rho = S16 ? 16 * sI + (lane >> 2) : 4 * sI + (lane >> 4);
+        // the position map is its own inverse
+        const int w = S16 ? scale_pos(rho, 4 * (lane & 3)) : scale_pos(rho, lane & 15);
+        const bool vec = rho >= R * kTile;
+        const int row = vec ? rho - R * kTile : rho;
+        sbase[sI] = (vec || row < nrows) ? static_cast<uint32_t>(row) * sixteenth + 4u * w : kOutOfRange;
+        slo[sI] = kWinElems * (w >> 2);
+    }
+    // Read lanes: row li of tile 0, chunks 2kq and 2kq + 1; the scale word of
+    // row li for piece kq of window u of a group.
+    const uint32_t rw0 = 128u * li + 16u * chunk_pos(li, 2 * kq);
+    const uint32_t rw1 = 128u * li + 16u * chunk_pos(li, 2 * kq + 1);
+    uint32_t rs[kGroupWins];
+#pragma unroll
+    for (int u = 0; u < kGroupWins; ++u) rs[u] = 64u * li + 4u * scale_pos(li, 4 * u + kq);
+    const int lpiece = kLaneElems * kq;
+
+    for (int64_t vp = v0; vp < v1; vp += kTile) {
+        const int64_t nv = (v1 - vp < kTile) ? v1 - vp : kTile;
+        const __amdgpu_buffer_rsrc_t vdesc =
+            buffer_of(a.V + vp * (k / 2), static_cast<int>(nv * (k / 2)));
+        const __amdgpu_buffer_rsrc_t svdesc =
+            buffer_of(a.sV + vp * (k / 16), static_cast<int>(nv * (k / 16)));
+
+        // Window j of the wave (and, when j starts a group, the group's
+        // scales).  Offsets carry the out-of-range bit or-ed in: every
+        // in-range offset is below 2^31, and adding a window offset to
+        // kOutOfRange stays above it.
+        auto issue = [&](auto starts_group, int j, int slot) {
+            const int kw = kwb + j * kWinElems;   // past kwe for spare windows
+            if constexpr (decltype(starts_group)::value) {
+                const int sl = kwe - kw;          // elements of the group in range
+                uint8_t *dst = sring + ((j / kGroupWins) & 1) * kScaleSlot;
+#pragma unroll
+                for (int sI = 0; sI < kScaleLoads; ++sI) {
+                    const uint32_t o = (sbase[sI] + static_cast<uint32_t>(kw) / 16) |
+                                       (slo[sI] < sl ? 0u : kOutOfRange);
+                    const bool vrows = (S16 ? 16 : 4) * sI >= R * kTile;
+                    if constexpr (S16)
+                        __builtin_amdgcn_raw_ptr_buffer_load_lds(vrows ? svdesc : swdesc,
+                                                                 (lds_void_t *)(dst + 1024 * sI), 16, o,
+                                                                 0, 0, 0);
+                    else
+                        __builtin_amdgcn_raw_ptr_buffer_load_lds(vrows ? svdesc : swdesc,
+                                                                 (lds_void_t *)(dst + 256 * sI), 4, o,
+                                                                 0, 0, 0);
+                }
+            }
+            const int lim = kwe - kw;             // elements of this window in range
+            uint8_t *dst = wring + slot * kWinSlot;
+#pragma unroll
+            for (int n = 0; n < kWinLoads; ++n) {
+                const uint32_t o = (wbase[n] + static_cast<uint32_t>(kw) / 2) |
+                                   (wlo[n] < lim ? 0u : kOutOfRange);
+                if (n < 2 * R)
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(wdesc, (lds_void_t *)(dst + 1024 * n), 16,
+                                                             o, 0, 0, kNonTemporal);
+                else
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(vdesc, (lds_void_t *)(dst + 1024 * n), 16,
+                                                             o, 0, 0, 0);
+            }
+        };
+        f32x4 acc[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) acc[r] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+        auto consume = [&](int j, int slot, int u) {
+            const uint8_t *win = wring + slot * kWinSlot;
+            const uint8_t *sc = sring + ((j / kGroupWins) & 1) * kScaleSlot;
+            u32x4 wq[R][2], vq[2];
+            uint32_t ws[R], vs;
+            lds_read_window<R>(lds_address(win + rw0), lds_address(win + rw1), lds_address(sc + rs[u]),
+                               wq, vq, ws, vs);
+            // a lane piece past the wave's K range: zero scales (its codes are
+            // zeros or stale)
+            const uint32_t keep = lpiece < kwe - (kwb + j * kWinElems) ? ~0u : 0u;
+            vs &= keep;
+#pragma unroll
+            for (int r = 0; r < R; ++r) ws[r] &= keep;
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                f16x8 vo[4];
+                decode32(vq[h], vs >> (16 * h), vo);
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    f16x8 wo[4];
+                    decode32(wq[r][h], ws[r] >> (16 * h), wo);
+#pragma unroll
+                    for (int s4 = 0; s4 < 4; ++s4) {
+                        if (GROUPED)
+                            acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vo[s4], wo[s4], acc[r], 0,
+                                                                            0, 0);
+                        else
+                            acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wo[s4], vo[s4], acc[r], 0,
+                                                                            0, 0);
+                    }
+                }
+            }
+        };
+
+        // One step at position u of group g: consume window j, refill its
+        // slot with window j + NS (spare windows past the run read nothing),
+        // wait until window j + 1 has landed.
+        auto step = [&](int g, auto pos) {
+            constexpr int u = decltype(pos)::value;
+            const int j = g * kGroupWins + u;
+            if (j < niter) consume(j, u % NS, u);   // wave-uniform
+            phase_fence();
+            issue(std::integral_constant<bool, (u + NS) % kGroupWins == 0>{}, j + NS, u % NS);
+            phase_fence();
+            wait_vmcnt<loads_after_next<NS, kWinLoads, kScaleLoads>(u)>();
+            phase_fence();
+        };
+        if (niter > 0) {   // wave-uniform
+            phase_fence();
+            issue(std::true_type{}, 0, 0);
+            phase_fence();
+            if constexpr (NS == 4) {
+                issue(std::false_type{}, 1, 1);
+                phase_fence();
+                issue(std::false_type{}, 2, 2);
+                phase_fence();
+                issue(std::false_type{}, 3, 3);
+            } else {
+                issue(std::false_type{}, 1, 1);
+            }
+            phase_fence();
+            wait_vmcnt<(NS - 1) * kWinLoads>();   // window 0 landed
+            phase_fence();
+            for (int g = 0; g * kGroupWins < niter; ++g) {
+                step(g, std::integral_constant<int, 0>{});
+                step(g, std::integral_constant<int, 1>{});
+                step(g, std::integral_constant<int, 2>{});
+                step(g, std::integral_constant<int, 3>{});
+            }
+            wait_vmcnt<0>();
+            phase_fence();
+        }
+
         if (W > 1) {
             if (wave > 0) {
 #pragma unroll
@@ -622,36 +985,49 @@ mma_splitk_reduce(const float *__restrict__ part, const float *__restrict__ alph
 }
 
 // ---------------------------------------------------------------- host side
-enum Form { kMatrixCores = 0, kValuTiles = 1 };
+enum Form { kMatrixCores = 0, kValuTiles = 1, kLdsStaged = 2 };
 struct Variant {
     int R, U, W;
     int form;
 };
-// Matrix cores (mma_stream): {row tiles of 16 per wave, windows in flight,
-// waves per workgroup}.  VALU row tiles (vec_tile): {rows per tile, vectors
-// per pass, waves per workgroup}.
+// Matrix cores (mma_stream) and matrix cores fed through LDS (mma_lds): {row
+// tiles of 16 per wave, windows in flight, waves per workgroup}.  VALU row
+// tiles (vec_tile): {rows per tile, vectors per pass, waves per workgroup}.
 constexpr Variant kVariants[] = {
     {1, 2, 4, kMatrixCores}, {1, 2, 8, kMatrixCores}, {2, 2, 4, kMatrixCores},
     {2, 1, 8, kMatrixCores}, {1, 3, 4, kMatrixCores}, {2, 2, 8, kMatrixCores},
     {4, 2, 4, kValuTiles},   {8, 2, 4, kValuTiles},   {4, 4, 4, kValuTiles},
-    {8, 4, 4, kValuTiles},
+    {8, 4, 4, kValuTiles},   {2, 2, 4, kLdsStaged},   {2, 4, 4, kLdsStaged},
+    {1, 2, 4, kLdsStaged},   {2, 2, 6, kLdsStaged},   {2, 2, 8, kLdsStaged},
 };
 constexpr int kNumVariants = static_cast<int>(sizeof(kVariants) / sizeof(kVariants[0]));
-// Defaults from MI355X sweeps of every variant: {2, 2, 4} on the decode-style
-// small-N workloads (one 7168 x 16384 weight against 3 to 16 vectors), the
-// VALU tiles {4, 2, 4} against 1 or 2 vectors (12.9 and 13.8 us against 17.8
-// and 18.0 on the matrix cores, which pad the vectors to 16), {2, 1, 8} on the
-// grouped decode workload (64 experts of 2048 x 7168, 128 tokens; the VALU
-// tiles were no faster there, with up to 6 tokens per expert).  The VALU tiles
+// Defaults from MI355X sweeps of every variant.  Row-major weights: the
+// LDS-staged {2, 4, 4} on the decode-style small-N workloads (one 7168 x 16384
+// weight against 3 to 16 vectors: 16.0 and 15.5 us for 16 and 4 vectors,
+// against 21.5 and 18.2 for the register-fed {2, 2, 4}), the VALU tiles {4, 2,
+// 4} against 1 or 2 vectors (12.9 and 13.8 us against 17.8 and 18.0 on the
+// matrix cores, which pad the vectors to 16), the LDS-staged {2, 2, 4} on the
+// grouped decode workload (64 experts of 2048 x 7168, 128 tokens: 89 us
+// against 109 for the register-fed {2, 1, 8}; its 78 KiB of LDS let two
+// workgroups share a compute unit).  Packed weights already load 1 KiB per
+// instruction: {2, 2, 4} and {2, 1, 8} on the matrix cores.  The VALU tiles
 // never split K, so they are the default only while their tiles fill the GPU.
-constexpr int kDefaultSmallN = 2;
+constexpr int kDefaultSmallN = 11;
+constexpr int kDefaultSmallNPacked = 2;
 constexpr int kDefaultSmallNFew = 6;
 constexpr int64_t kFewVectors = 2;
-constexpr int kDefaultGrouped = 3;
+constexpr int kDefaultGrouped = 10;
+constexpr int kDefaultGroupedPacked = 3;
+static_assert(kVariants[kDefaultSmallN].form == kLdsStaged && kVariants[kDefaultSmallN].U == 4 &&
+                  kVariants[kDefaultGrouped].form == kLdsStaged && kVariants[kDefaultGrouped].U == 2 &&
+                  kVariants[kDefaultSmallNPacked].form == kMatrixCores &&
+                  kVariants[kDefaultGroupedPacked].form == kMatrixCores &&
+                  kVariants[kDefaultSmallNFew].form == kValuTiles,
+              "the defaults name the variants measured above");
 
 typedef void (*MmaKernel)(const MmaArgs);
 
-template <bool G, bool P>
+template <bool G, bool P, bool S16 = false>
 MmaKernel fast_kernel(int v) {
     switch (v) {
     case 0: return mma_stream<1, 2, 4, G, P>;
@@ -664,6 +1040,11 @@ MmaKernel fast_kernel(int v) {
     case 7: return P ? nullptr : vec_tile<8, 2, 4, G>;
     case 8: return P ? nullptr : vec_tile<4, 4, 4, G>;
     case 9: return P ? nullptr : vec_tile<8, 4, 4, G>;
+    case 10: return P ? nullptr : mma_lds<2, 2, 4, G, S16>;
+    case 11: return P ? nullptr : mma_lds<2, 4, 4, G, S16>;
+    case 12: return P ? nullptr : mma_lds<1, 2, 4, G, S16>;
+    case 13: return P ? nullptr : mma_lds<2, 2, 6, G, S16>;
+    case 14: return P ? nullptr : mma_lds<2, 2, 8, G, S16>;
     default: return nullptr;
     }
 }
@@ -732,9 +1113,9 @@ int make_plan(int64_t groups, int64_t rows, int64_t nvec_per_group, int64_t k, b
         if (tun.variant > 0) {
             p->variant = tun.variant - 1;
         } else if (grouped) {
-            p->variant = kDefaultGrouped;
+            p->variant = packed ? kDefaultGroupedPacked : kDefaultGrouped;
         } else if (packed) {
-            p->variant = kDefaultSmallN;
+            p->variant = kDefaultSmallNPacked;
         } else {
             const int64_t tiles = groups * ceil_div(rows, int64_t(kVariants[kDefaultSmallNFew].R));
             p->variant = (nvec_per_group <= kFewVectors && tiles >= 4 * kComputeUnits)
@@ -809,12 +1190,20 @@ int launch(const Plan &p, bool grouped, MmaArgs a, hipStream_t stream, bool pack
     a.kchunk = p.kchunk;
     a.row_blocks = p.row_blocks;
     a.rows_per_block = p.rows_per_block;
+    // LDS-staged variants copy block scales 16 bytes at a time when every
+    // scale row, workgroup K range and window group starts 16-byte aligned
+    const bool s16 = a.k % 256 == 0 && a.kchunk % 256 == 0 &&
+                     reinterpret_cast<uintptr_t>(a.sW) % 16 == 0 &&
+                     reinterpret_cast<uintptr_t>(a.sV) % 16 == 0;
     const void *fn;
     if (p.path == NVFP4_GEMV_PATH_FAST)
         fn = reinterpret_cast<const void *>(
-            grouped ? (packed ? fast_kernel<true, true>(p.variant) : fast_kernel<true, false>(p.variant))
+            grouped ? (packed ? fast_kernel<true, true>(p.variant)
+                              : s16 ? fast_kernel<true, false, true>(p.variant)
+                                    : fast_kernel<true, false>(p.variant))
                     : (packed ? fast_kernel<false, true>(p.variant)
-                              : fast_kernel<false, false>(p.variant)));
+                              : s16 ? fast_kernel<false, false, true>(p.variant)
+                                    : fast_kernel<false, false>(p.variant)));
     else
         fn = reinterpret_cast<const void *>(grouped ? mma_generic<true> : mma_generic<false>);
     void *args[] = {&a};
@@ -970,6 +1359,22 @@ int nvfp4_gemm_smalln_plan(int64_t l, int64_t m, int64_t n, int64_t k, int align
     out->ksplit = static_cast<int32_t>(p.ksplit);
     out->rows_per_block = p.path == NVFP4_GEMV_PATH_FAST ? static_cast<int32_t>(p.rows_per_block) : 0;
     *workspace_bytes = p.ws_bytes;
+    return NVFP4_GEMV_OK;
+}
+
+int nvfp4_grouped_gemv_plan(int64_t experts, int64_t n, int64_t k, int aligned, int packed,
+                            const nvfp4_mma_tuning_t *in, nvfp4_mma_tuning_t *out) {
+    if (!out) return NVFP4_GEMV_ERR_NULL_POINTER;
+    int s = check_dims(experts, n, 0, k, true);
+    if (s != NVFP4_GEMV_OK) return s;
+    if (packed && (k % 64 != 0 || k > kMaxFastK)) return NVFP4_GEMV_ERR_BAD_SHAPE;
+    Plan p;
+    s = make_plan(experts, n, 0, k, packed != 0 || aligned != 0, true, in, &p, packed != 0);
+    if (s != NVFP4_GEMV_OK) return s;
+    out->path = p.path;
+    out->variant = p.path == NVFP4_GEMV_PATH_FAST ? p.variant + 1 : 0;
+    out->ksplit = static_cast<int32_t>(p.ksplit);
+    out->rows_per_block = p.path == NVFP4_GEMV_PATH_FAST ? static_cast<int32_t>(p.rows_per_block) : 0;
     return NVFP4_GEMV_OK;
 }
 

@@ -147,3 +147,26 @@ def test_parity_summary_counts_ulps():
     r = bench.parity_summary(np, got, want)
     assert r == {"outputs": 4, "bit_identical": 1, "max_ulp": 2}
     assert bench.parity_summary(np, want, want)["bit_identical"] == 4
+
+
+def test_mma_kernel_name_follows_the_plan_form():
+    class Plan:
+        def __init__(self, path, variant):
+            self.path, self.variant = path, variant
+
+    class FakePd:
+        NVFP4_GEMV_PATH_FAST = 1
+        NVFP4_MMA_FORM_VALU_TILES = 1
+        NVFP4_MMA_FORM_LDS_STAGED = 2
+
+        @staticmethod
+        def nvfp4_mma_variant_form(v):
+            return {3: 0, 7: 1, 11: 2}[v]
+
+    assert bench.mma_kernel_name(FakePd, Plan(1, 3), False) == "mma_stream"
+    assert bench.mma_kernel_name(FakePd, Plan(1, 7), False) == "vec_tile"
+    assert bench.mma_kernel_name(FakePd, Plan(1, 11), False) == "mma_lds"
+    assert bench.mma_kernel_name(FakePd, Plan(2, 0), False) == "mma_generic"
+    assert bench.mma_kernel_name(FakePd, Plan(1, 3), True) == "mma_stream_packed"
+    for name in ("mma_stream", "vec_tile", "mma_lds", "mma_generic", "mma_stream_packed"):
+        assert name in bench.KERNEL_SOURCES

@@ -79,7 +79,7 @@ def test_smalln_default_plan_shapes(l, m, n, k):
     assert_bits_equal(run_smalln(ops, l, m, n, k), oracle_smalln(ops, l, m, n, k), f"{(l, m, n, k)}")
 
 
-NUM_MMA_VARIANTS = 10
+NUM_MMA_VARIANTS = 15
 
 
 def valu_tiles(v):
@@ -157,6 +157,47 @@ def gaussian_smalln_ops(l, m, n, k, seed):
         ops["B"][b], ops["sfB"][b], gb = oq.quantize_nvfp4(rawB[b])
         ops["alpha"][b] = np.float32(ga * gb)
     return ops
+
+
+@pytest.mark.parametrize("ksplit", [1, 2])
+def test_lds_staged_gaussian_within_tolerance(ksplit):
+    """Gaussian data (inexact sums) through every LDS-staged variant: ragged
+    rows, a K tail of one lane piece, waves whose K runs end mid-group, and
+    rows per block below the tiles, against the oracle within tolerance."""
+    l, m, n, k = 2, 203, 13, 4160
+    ops = gaussian_smalln_ops(l, m, n, k, seed=90 + ksplit)
+    dev = to_device(ops)
+    want = oracle_smalln(ops, l, m, n, k)
+    staged = [v for v in range(1, NUM_MMA_VARIANTS + 1)
+              if pd.nvfp4_mma_variant_form(v) == pd.NVFP4_MMA_FORM_LDS_STAGED]
+    assert staged
+    for v in staged:
+        for rpb in (0, 13):
+            tun = {"variant": v, "ksplit": ksplit, "rows_per_block": rpb}
+            got = run_smalln(ops, l, m, n, k, tuning=tun, dev=dev)
+            assert_within_tolerance(got, want, what=f"staged variant {v} rpb {rpb} ks {ksplit}")
+
+
+def test_lds_staged_scales_at_4_byte_alignment():
+    """Scale rows that start 4 bytes past a 16-byte boundary (k a multiple of
+    256): the LDS-staged variants then copy block scales 4 bytes at a time
+    instead of 16, bit for bit the same results."""
+    l, m, n, k = 2, 70, 16, 4096
+    ops = smalln_ops(l, m, n, k, seed=123)
+    want = oracle_smalln(ops, l, m, n, k)
+    dev = to_device(ops)
+    for key in ("sfA", "sfB"):
+        t = dev[key]
+        buf = torch.zeros(t.numel() + 16, dtype=torch.uint8, device="cuda")
+        buf[4:4 + t.numel()].copy_(t.reshape(-1))
+        dev[key] = buf[4:4 + t.numel()].view(t.shape)
+        assert dev[key].data_ptr() % 16 == 4
+    staged = [v for v in range(1, NUM_MMA_VARIANTS + 1)
+              if pd.nvfp4_mma_variant_form(v) == pd.NVFP4_MMA_FORM_LDS_STAGED]
+    for v in staged:
+        for ks in (1, 2):
+            got = run_smalln(ops, l, m, n, k, tuning={"variant": v, "ksplit": ks}, dev=dev)
+            assert_bits_equal(got, want, f"variant {v} ks {ks}, 4-byte aligned scales")
 
 
 @pytest.mark.parametrize("n", [1, 2])
