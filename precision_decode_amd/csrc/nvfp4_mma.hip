@@ -999,6 +999,7 @@ constexpr Variant kVariants[] = {
     {4, 2, 4, kValuTiles},   {8, 2, 4, kValuTiles},   {4, 4, 4, kValuTiles},
     {8, 4, 4, kValuTiles},   {2, 2, 4, kLdsStaged},   {2, 4, 4, kLdsStaged},
     {1, 2, 4, kLdsStaged},   {2, 2, 6, kLdsStaged},   {2, 2, 8, kLdsStaged},
+    {2, 2, 2, kLdsStaged},   {2, 4, 2, kLdsStaged},
 };
 constexpr int kNumVariants = static_cast<int>(sizeof(kVariants) / sizeof(kVariants[0]));
 // Defaults from MI355X sweeps of every variant.  Row-major weights: the
@@ -1006,20 +1007,21 @@ constexpr int kNumVariants = static_cast<int>(sizeof(kVariants) / sizeof(kVarian
 // weight against 3 to 16 vectors: 16.0 and 15.5 us for 16 and 4 vectors,
 // against 21.5 and 18.2 for the register-fed {2, 2, 4}), the VALU tiles {4, 2,
 // 4} against 1 or 2 vectors (12.9 and 13.8 us against 17.8 and 18.0 on the
-// matrix cores, which pad the vectors to 16), the LDS-staged {2, 2, 4} on the
-// grouped decode workload (64 experts of 2048 x 7168, 128 tokens: 89 us
-// against 109 for the register-fed {2, 1, 8}; its 78 KiB of LDS let two
-// workgroups share a compute unit).  Packed weights already load 1 KiB per
+// matrix cores, which pad the vectors to 16), the LDS-staged {2, 2, 2} on the
+// grouped decode workload (64 experts of 2048 x 7168, 128 tokens: 82 us
+// against 87-92 for {2, 2, 4} and 109 for the register-fed {2, 1, 8}; its
+// 38 KiB of LDS let four workgroups share a compute unit, and each wave
+// spreads its start over twice the windows).  Packed weights already load 1 KiB per
 // instruction: {2, 2, 4} and {2, 1, 8} on the matrix cores.  The VALU tiles
 // never split K, so they are the default only while their tiles fill the GPU.
 constexpr int kDefaultSmallN = 11;
 constexpr int kDefaultSmallNPacked = 2;
 constexpr int kDefaultSmallNFew = 6;
 constexpr int64_t kFewVectors = 2;
-constexpr int kDefaultGrouped = 10;
+constexpr int kDefaultGrouped = 15;
 constexpr int kDefaultGroupedPacked = 3;
 static_assert(kVariants[kDefaultSmallN].form == kLdsStaged && kVariants[kDefaultSmallN].U == 4 &&
-                  kVariants[kDefaultGrouped].form == kLdsStaged && kVariants[kDefaultGrouped].U == 2 &&
+                  kVariants[kDefaultGrouped].form == kLdsStaged && kVariants[kDefaultGrouped].W == 2 &&
                   kVariants[kDefaultSmallNPacked].form == kMatrixCores &&
                   kVariants[kDefaultGroupedPacked].form == kMatrixCores &&
                   kVariants[kDefaultSmallNFew].form == kValuTiles,
@@ -1045,6 +1047,8 @@ MmaKernel fast_kernel(int v) {
     case 12: return P ? nullptr : mma_lds<1, 2, 4, G, S16>;
     case 13: return P ? nullptr : mma_lds<2, 2, 6, G, S16>;
     case 14: return P ? nullptr : mma_lds<2, 2, 8, G, S16>;
+    case 15: return P ? nullptr : mma_lds<2, 2, 2, G, S16>;
+    case 16: return P ? nullptr : mma_lds<2, 4, 2, G, S16>;
     default: return nullptr;
     }
 }

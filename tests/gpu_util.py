@@ -8,7 +8,8 @@ import workloads
 
 
 def to_device(ops):
-    return {k: torch.from_numpy(np.ascontiguousarray(v)).cuda() for k, v in ops.items()}
+    # np.array copies: some fixtures are read-only arrays, which torch will not wrap
+    return {k: torch.from_numpy(np.array(v, order="C")).cuda() for k, v in ops.items()}
 
 
 def run_gpu(dops, l, m, k, tuning=None, use_alpha=True, mode="launch", stream=None):

@@ -433,7 +433,7 @@ def test_grouped_plan(lib):
     t = pd.nvfp4_grouped_gemv_plan(64, 2048, 7168)
     assert t.path == pd.NVFP4_GEMV_PATH_FAST and t.ksplit == 1
     assert pd.nvfp4_mma_variant_form(t.variant) == pd.NVFP4_MMA_FORM_LDS_STAGED
-    assert pd.nvfp4_mma_variant_info(t.variant) == (2, 2, 4)
+    assert pd.nvfp4_mma_variant_info(t.variant) == (2, 2, 2)
     t = pd.nvfp4_grouped_gemv_plan(64, 2048, 7168, packed=True)
     assert pd.nvfp4_mma_variant_form(t.variant) == pd.NVFP4_MMA_FORM_MATRIX_CORES
     assert pd.nvfp4_mma_variant_info(t.variant) == (2, 1, 8)
