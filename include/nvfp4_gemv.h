@@ -205,9 +205,12 @@ int nvfp4_gemv_launch_tuned(const uint8_t *A_packed, const uint8_t *sfA,
 
 /*
  * Streams `bytes` bytes (a multiple of 16, 16-byte aligned device buffer)
- * through the same non-temporal 16-byte loads the GEMV uses and writes one
- * word per workgroup into `sink` (device, at least 4096 uint32).  Its run time
- * gives the achievable HBM read bandwidth beside the GEMV's.  Returns a status.
+ * through the same non-temporal 16-byte loads the GEMV uses, in the fastest
+ * plain read order measured on MI355X (contiguous 16 KiB chunks, one per
+ * 4-wave workgroup at a time, every load of a chunk in flight together), and
+ * writes one word per workgroup into `sink` (device, at least 4096 uint32).
+ * Its run time gives the achievable HBM read bandwidth beside the GEMV's.
+ * Returns a status.
  */
 int nvfp4_hbm_read_probe(const void *buffer, size_t bytes, uint32_t *sink, void *stream);
 

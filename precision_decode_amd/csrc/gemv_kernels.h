@@ -34,8 +34,9 @@
 // a multiple of 1/4 below 2^22 and therefore exact in fp32, whatever the
 // summation order.
 //
-// This header holds the device code (kernels and their helpers); the host
-// side (plans, entry points, workspaces) is nvfp4_gemv.hip, its only includer.
+// This header holds the GEMV's device code (kernels and their helpers); the
+// read probes are in probe_kernels.h, and the host side (plans, entry points,
+// workspaces) is nvfp4_gemv.hip, the only includer of both.
 #ifndef NVFP4_GEMV_KERNELS_H
 #define NVFP4_GEMV_KERNELS_H
 
@@ -51,9 +52,6 @@ namespace {
 
 using namespace nvfp4dev;
 using namespace nvfp4plan;
-
-constexpr int kProbeThreads = 256;
-constexpr int kProbeMaxGroups = 4096;
 
 // ---------------------------------------------------------------- decode
 // acc + sum over the 8 codes of `a` of e2m1(code) * x~ (8 fp16 in xq).
@@ -740,126 +738,6 @@ gemv_splitk_reduce(const float *__restrict__ part, const float *__restrict__ alp
     for (int64_t j = 0; j < ksplit; ++j) s += part[j * n + i];
     const float al = alpha ? alpha[i / m] : 1.0f;
     c[i] = f16_of_product(al, s);
-}
-
-// ---------------------------------------------------------------- read probe
-// Reads n16 16-byte units once, in rounds of 8 loads per thread that are all
-// in flight together: in round r, thread t of the grid loads units
-// r * 8S + t + jS (j < 8, S = the grid's thread count), so every wave
-// instruction reads 1 KiB contiguously.  Each round's loads go through a
-// descriptor over that round's units, so loads past the end read zeros and
-// need no branch or serial tail; round offsets stay below 2^31 bytes.
-constexpr int kProbeLoads = 8;
-
-__global__ void __launch_bounds__(kProbeThreads)
-hbm_read_probe(const uint8_t *__restrict__ buf, int64_t n16, uint32_t *__restrict__ sink) {
-    const int64_t stride = static_cast<int64_t>(gridDim.x) * kProbeThreads;
-    const int64_t round = kProbeLoads * stride;
-    const uint32_t t = blockIdx.x * kProbeThreads + threadIdx.x;
-    u32x4 acc = {0u, 0u, 0u, 0u};
-    for (int64_t base = 0; base < n16; base += round) {
-        const int64_t len = (n16 - base < round) ? n16 - base : round;
-        const __amdgpu_buffer_rsrc_t rs = buffer_of(buf + base * 16, static_cast<int>(len * 16));
-        u32x4 v[kProbeLoads];
-#pragma unroll
-        for (int j = 0; j < kProbeLoads; ++j)
-            v[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                 rs, (t + j * static_cast<uint32_t>(stride)) * 16u, 0,
-                                                 kNonTemporal));
-#pragma unroll
-        for (int j = 0; j < kProbeLoads; ++j) acc ^= v[j];
-    }
-    uint32_t w = acc.x ^ acc.y ^ acc.z ^ acc.w;
-    for (int o = kWave / 2; o >= 1; o >>= 1) w ^= __shfl_xor(w, o, kWave);
-    __shared__ uint32_t per_wave[kProbeThreads / kWave];
-    if ((threadIdx.x & (kWave - 1)) == 0) per_wave[threadIdx.x / kWave] = w;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        uint32_t all = 0u;
-        for (int i = 0; i < kProbeThreads / kWave; ++i) all ^= per_wave[i];
-        sink[blockIdx.x] = all;
-    }
-}
-
-// ---------------------------------------------------------------- row read probe
-// Reads `rows` rows of codes (k/2 bytes each) and of scales (k/16 bytes each)
-// with the load pattern of gemv_fast<2, 4, 7>, the GEMV's kernel for long
-// rows, and no arithmetic: a workgroup of 7 waves owns 14 consecutive rows,
-// each wave streams 2 rows with 4 iterations of 1 KiB per row in flight,
-// 16-byte non-temporal loads of the codes and 2-byte loads of the scales,
-// one buffer descriptor per row (loads past a row's end, and rows past the
-// last, read zeros without touching memory).  Its time is the read ceiling of
-// that pattern for a matrix of this shape.  Each workgroup stores the XOR of
-// everything it read in sink[blockIdx.x].
-constexpr int kRowProbeR = 2, kRowProbeU = 4, kRowProbeW = 7;
-
-__global__ void __launch_bounds__(kRowProbeW * kWave)
-hbm_read_rows(const uint8_t *__restrict__ A, const uint8_t *__restrict__ sfA, int64_t rows,
-              int64_t k, uint32_t *__restrict__ sink) {
-    constexpr int R = kRowProbeR, U = kRowProbeU, W = kRowProbeW;
-    const int lane = threadIdx.x & (kWave - 1);
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    const int64_t row0 = (static_cast<int64_t>(blockIdx.x) * W + wave) * R;
-    const int nit = static_cast<int>((k + kIterElems - 1) / kIterElems);
-    const int nstage = (nit + U - 1) / U;
-
-    __amdgpu_buffer_rsrc_t ad[R], sd[R];
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-        const bool in = row0 + r < rows;
-        const int64_t row = in ? row0 + r : 0;
-        ad[r] = buffer_of(A + row * (k / 2), in ? static_cast<int>(k / 2) : 0);
-        sd[r] = buffer_of(sfA + row * (k / 16), in ? static_cast<int>(k / 16) : 0);
-    }
-    u32x4 v[U][R];
-    uint16_t sv[U][R];
-    auto issue = [&](int it, int u) {
-        const int off = it * static_cast<int>(kIterElems / 2) + lane * 16;
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-            v[u][r] = __builtin_bit_cast(
-                u32x4, __builtin_amdgcn_raw_buffer_load_b128(ad[r], off, 0, kNonTemporal));
-            sv[u][r] = __builtin_amdgcn_raw_buffer_load_b16(sd[r], off / 8, 0, kNonTemporal);
-        }
-    };
-    u32x4 acc = {0u, 0u, 0u, 0u};
-    uint32_t sacc = 0u;
-    phase_fence();
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-        issue(u, u);
-        phase_fence();
-    }
-    for (int st = 0; st + 1 < nstage; ++st) {
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-#pragma unroll
-            for (int r = 0; r < R; ++r) {
-                acc ^= v[u][r];
-                sacc ^= sv[u][r];
-            }
-            issue((st + 1) * U + u, u);   // past the last iteration: zeros, no traffic
-            phase_fence();
-        }
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-            acc ^= v[u][r];
-            sacc ^= sv[u][r];
-        }
-    }
-    uint32_t w = acc.x ^ acc.y ^ acc.z ^ acc.w ^ sacc;
-    for (int o = kWave / 2; o >= 1; o >>= 1) w ^= __shfl_xor(w, o, kWave);
-    __shared__ uint32_t per_wave[W];
-    if (lane == 0) per_wave[wave] = w;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        uint32_t all = 0u;
-        for (int i = 0; i < W; ++i) all ^= per_wave[i];
-        sink[blockIdx.x] = all;
-    }
 }
 
 }  // namespace

@@ -59,7 +59,8 @@ constexpr Variant kVariants[] = {
     {2, 4, 7, kXGlobal},  {2, 2, 7, kXGlobal},  {4, 2, 7, kXGlobal},  {2, 4, 4, kXGlobal},
     {1, 8, 7, kXGlobal},  {4, 1, 8, kXGlobal},  {16, 1, 8, kXTile},   {16, 1, 4, kXTile},
     {16, 1, 2, kXTile},   {16, 1, 1, kXTile},   {8, 1, 1, kXTile},    {8, 1, 2, kXTile},
-    {4, 1, 1, kXTile},    {4, 1, 2, kXTile},
+    {4, 1, 1, kXTile},    {4, 1, 2, kXTile},    {4, 1, 8, kXTile},    {4, 1, 4, kXTile},
+    {8, 1, 4, kXTile},
 };
 constexpr int kNumVariants = static_cast<int>(sizeof(kVariants) / sizeof(kVariants[0]));
 
@@ -67,18 +68,29 @@ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Default fast variant (0-based) by the number of 1 KiB K-iterations per row
 // of one workgroup's K-range, from MI355X measurements on the decode, batched,
-// Gaussian and short-K workloads: long rows want more rows in flight per
-// workgroup; with 3 to 5 iterations per row x read next to A beats staging it;
-// rows of one or two iterations are best read as row tiles, whose loads are
-// all in flight at once: rows of one iteration as 4-row tiles of one wave
-// (many small waves, little arithmetic left in each when its last load lands),
-// rows of two as 16-row tiles of two waves.
-inline int default_variant(int64_t k) {
+// Gaussian and short-K workloads.  Rows of 6 to 8 iterations (the decode
+// weight's 8) are best read as 4-row tiles of 8 waves: each wave then holds
+// one 1 KiB slice of 4 rows, all of it in flight at once, and a workgroup
+// reads 16-32 KiB of A, the shape in which a plain read of such a weight is
+// fastest (11.84 us against 12.23 for the staged {2, 4, 7} in an alternating
+// A/B on one box), as long as those tiles alone fill the GPU (at least 4
+// per compute unit; a tile's 8 waves cannot split K any further).  Longer
+// rows, and fewer rows, keep the staged {2, 4, 7}, which keeps every wave's
+// rows in flight over any number of iterations and splits K across
+// workgroups when its groups are few; with 3 to 5
+// iterations x read next to A beats staging it; rows of one or two
+// iterations are best read as row tiles, whose loads are all in flight at
+// once: rows of one iteration as 4-row tiles of one wave (many small waves,
+// little arithmetic left in each when its last load lands), rows of two as
+// 16-row tiles of two waves.
+inline int default_variant(int64_t l, int64_t m, int64_t k) {
     const int64_t nit = ceil_div(k < kMaxChunk ? k : kMaxChunk, kIterElems);
-    if (nit >= 6) return 0;    // {2, 4, 7}
-    if (nit >= 3) return 19;   // {2, 4, 4} x read next to A
-    if (nit == 2) return 24;   // 16-row tile, 2 waves
-    return 28;                 // 4-row tile, 1 wave
+    const int64_t nit_all = ceil_div(k, kIterElems);
+    if (nit_all > 8) return 0;   // {2, 4, 7} staged
+    if (nit >= 6) return l * ceil_div(m, int64_t(4)) >= 4 * kComputeUnits ? 30 : 0;   // 4-row tile, 8 waves
+    if (nit >= 3) return 19;     // {2, 4, 4} x read next to A
+    if (nit == 2) return 24;     // 16-row tile, 2 waves
+    return 28;                   // 4-row tile, 1 wave
 }
 
 struct Plan {
@@ -133,7 +145,7 @@ inline int make_plan(int64_t l, int64_t m, int64_t k, bool aligned, const nvfp4_
     if (tun.variant > kNumVariants) return NVFP4_GEMV_ERR_BAD_TUNING;
     p->path = (tun.path == NVFP4_GEMV_PATH_GENERIC || !fast_ok) ? NVFP4_GEMV_PATH_GENERIC
                                                                   : NVFP4_GEMV_PATH_FAST;
-    p->variant = tun.variant > 0 ? tun.variant - 1 : default_variant(k);
+    p->variant = tun.variant > 0 ? tun.variant - 1 : default_variant(l, m, k);
 
     int64_t rows_per_group;
     if (p->path == NVFP4_GEMV_PATH_FAST) {

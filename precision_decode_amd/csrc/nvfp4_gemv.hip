@@ -23,6 +23,7 @@
 #include "gemv_kernels.h"
 #include "gemv_plan.h"
 #include "nvfp4_gemv.h"
+#include "probe_kernels.h"
 
 namespace {
 
@@ -66,11 +67,14 @@ FastKernel fast_kernel(int v) {
     case 27: return gemv_tile<2, 8>;
     case 28: return gemv_tile<1, 4>;
     case 29: return gemv_tile<2, 4>;
+    case 30: return gemv_tile<8, 4>;
+    case 31: return gemv_tile<4, 4>;
+    case 32: return gemv_tile<4, 8>;
     default: return nullptr;
     }
 }
 
-static_assert(kNumVariants == 30, "fast_kernel() covers every entry of kVariants");
+static_assert(kNumVariants == 33, "fast_kernel() covers every entry of kVariants");
 
 // Enqueues the plan's kernels: the GEMV (or its partial sums) and, with a K
 // split, the second pass.
@@ -310,12 +314,12 @@ int nvfp4_hbm_read_probe(const void *buffer, size_t bytes, uint32_t *sink, void 
         return NVFP4_GEMV_ERR_BAD_SHAPE;
     if (reinterpret_cast<uintptr_t>(buffer) % 16 != 0 || reinterpret_cast<uintptr_t>(sink) % 4 != 0)
         return NVFP4_GEMV_ERR_ALIGNMENT;
-    const int64_t n16 = static_cast<int64_t>(bytes / 16);
-    // enough groups for one round of 8 loads per thread, up to kProbeMaxGroups
-    int64_t groups = ceil_div(n16, int64_t(kProbeThreads) * kProbeLoads);
+    const int64_t nbytes = static_cast<int64_t>(bytes);
+    // a workgroup per 16 KiB chunk, up to kProbeMaxGroups (each then takes several)
+    int64_t groups = ceil_div(nbytes, kProbeChunk);
     if (groups > kProbeMaxGroups) groups = kProbeMaxGroups;
     const uint8_t *buf = static_cast<const uint8_t *>(buffer);
-    void *args[] = {&buf, const_cast<int64_t *>(&n16), &sink};
+    void *args[] = {&buf, const_cast<int64_t *>(&nbytes), &sink};
     hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(hbm_read_probe),
                                    dim3(static_cast<uint32_t>(groups)), dim3(kProbeThreads), args,
                                    0, static_cast<hipStream_t>(stream));

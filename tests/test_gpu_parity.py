@@ -128,7 +128,7 @@ def test_generic_kernel(l, m, k, ksplit):
     assert_bits_equal(run_gpu(to_device(ops), l, m, k, tuning=tun), want, "generic")
 
 
-NUM_VARIANTS = 30
+NUM_VARIANTS = 33
 
 
 def test_variant_count():
@@ -261,10 +261,12 @@ def test_nan_and_negative_scales_and_overflow():
     assert_bits_equal(run_gpu(to_device(big), 1, 16, 4096), want, "overflow")
 
 
-@pytest.mark.parametrize("n", [64 << 20, (64 << 20) + 48, 300 << 20, 16])
+@pytest.mark.parametrize("n", [64 << 20, (64 << 20) + 48, 300 << 20, 16, (16 << 10) + 16])
 def test_hbm_read_probe_reads_every_byte_once(n):
-    """One round of 8 loads per thread, a ragged round, three rounds with a
-    partial last one (the group count capped), and a single unit."""
+    """16 KiB chunks, one per workgroup: exactly the group cap (4096 chunks),
+    a ragged chunk past the cap (one group takes two), several chunks per
+    group with a partial last round, a single 16-byte unit, and two chunks
+    of which the second holds one unit."""
     data = torch.randint(0, 2 ** 31 - 1, (n // 4,), dtype=torch.int32, device="cuda")
     sink = torch.zeros(4096, dtype=torch.int32, device="cuda")
     print(f"probe over {n} bytes", flush=True)
