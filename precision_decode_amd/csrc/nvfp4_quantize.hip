@@ -104,9 +104,18 @@ __device__ __forceinline__ float quot_short(float a, float b, float y) {
 //    so the argmin is the nearest value with ties down, and 6 beyond the grid;
 //  * half-step (the page's table on rint(2 min(|v|, 6))): below 2 the table is
 //    nearest-even on the grid; from 2 its cut points 2.75, 3.75 and 5.25 sit
-//    0.25 above the grid midpoints 2.5, 3.5 and 5, so |v| - 0.25 (exact there)
-//    is rounded instead, clamped below at 2 (med3), and the one cut whose tie
-//    goes the other way, |v| = 2.75, maps to 3.
+//    0.25 above the grid midpoints 2.5, 3.5 and 5, whose ties go to the even
+//    codes (2, 4 and 4).  The table sends 3.75 up and 5.25 down, as those ties
+//    do, but 2.75 up, against its tie.  So f(a) = RN(a (1 - 2^-24) - 0.25 +
+//    5 2^-24), one fma, is rounded instead, clamped below at 2 (med3):
+//    f(a) = a - 0.25 + (5 - a) 2^-24 before rounding, so f(2.75) lands
+//    2.25 2^-24 above 2.5 and rounds to the float above it (half an ulp there
+//    is 2 2^-24), f(3.75) and f(5.25) round onto 3.5 and 5 exactly, and every
+//    float next to a cut rounds to the side it belongs to.  Checked against
+//    the table for every finite fp32 |v| on the CPU.
+constexpr float kHalfStepScale = 0x1.fffffep-1f;            // 1 - 2^-24
+constexpr float kHalfStepShift = -0.25f + 5.0f * 0x1p-24f;  // exact in fp32
+
 template <int RULE>
 __device__ __forceinline__ u32x2 block_codes(const float (&v)[16]) {
     float t[16];
@@ -117,8 +126,8 @@ __device__ __forceinline__ u32x2 block_codes(const float (&v)[16]) {
             t[i] = __uint_as_float(b - ((b & 0x005FFFFFu) == 0x00400000u ? 1u : 0u));
         } else if constexpr (RULE == NVFP4_ROUND_HALF_STEP) {
             const float a = __builtin_fabsf(v[i]);
-            float m = __builtin_amdgcn_fmed3f(a - 0.25f, a, 2.0f);
-            m = a == 2.75f ? 3.0f : m;
+            const float m = __builtin_amdgcn_fmed3f(
+                __builtin_fmaf(a, kHalfStepScale, kHalfStepShift), a, 2.0f);
             t[i] = __builtin_copysignf(m, v[i]);
         } else {
             t[i] = v[i];
