@@ -38,7 +38,10 @@ Each JSON line:
                workload on this host's cores, with the parity of the last
                timed call against it
 
-Other paths (--path), each printing its own JSON line of the same form:
+Other paths (--path), each printing its own JSON line of the same form (their
+steps are launched one by one; --launch graph adds the replay of a HIP graph
+holding the same K steps and makes it the reported figure, which keeps the
+stream busy under a kernel tracer that slows the host's launches):
   quantize     the BF16 -> NVFP4 activation quantiser on a bf16 activation
                batch (--act-config tokens | decode_x)
   gemv_bf16x   the GEMV fed by a bf16 activation: quantiser + GEMV per step
@@ -105,7 +108,7 @@ def parse_args(argv=None):
                         "gaussian: bf16 draws quantised by the library's device quantiser, untimed), "
                         "or all: each in turn, one JSON line each, batched last")
     p.add_argument("--launch", default="stream", choices=["graph", "stream"],
-                   help="GEMV: time the K steps as one replay of a HIP graph that holds them, or "
+                   help="time the K steps as one replay of a HIP graph that holds them, or "
                         "launched one by one on the stream")
     p.add_argument("--trace-cold", action="store_true",
                    help="GEMV: only the warm-up and the timed steps (no cache-resident loop, "
@@ -313,17 +316,39 @@ def common_fields(args, gbs, ms_step, dtype):
             "scaling": "weak", "vs_baseline": None, "dtype": dtype, "data": "synthetic"}
 
 
-def timed_steps(args, timer, step, nbytes, label):
+def timed_steps(args, timer, step, nbytes, label, state, capture_stream):
+    """Warm-up, then the K steps launched one by one on the stream; with
+    --launch graph, the same K steps are also captured into one HIP graph on
+    `capture_stream` and its replay gives the step time.  `step` launches on
+    state["stream"].  Returns (ms per step, GB/s, the timings in us)."""
     for i in range(args.warmup):
         step(i)
     timer.torch.cuda.synchronize()
     ms_total, wall = timer(args.steps, step)
     ms_step = ms_total / args.steps
     gbs = nbytes / (ms_step * 1e-3) / 1e9
+    enqueue_us = timer.enqueue_s / args.steps * 1e6
     print(f"[bench] {label}: {args.steps} steps: {ms_step * 1e3:.2f} us/step, {gbs:.1f} GB/s "
           f"({100 * gbs / HBM_PEAK_GBS:.1f}% of peak), host wall {wall:.3f}s, host enqueue "
-          f"{timer.enqueue_s / args.steps * 1e6:.2f} us/step", flush=True)
-    return ms_step, gbs
+          f"{enqueue_us:.2f} us/step", flush=True)
+    timing = {"graph_replay": None, "stream_launches": round(ms_step * 1e3, 3),
+              "host_enqueue_per_launch": round(enqueue_us, 3)}
+    if args.launch == "graph":
+        g = capture_steps(timer.torch, args.steps, step, state, capture_stream)
+        g.replay()                                   # untimed: uploads the graph
+        timer.torch.cuda.synchronize()
+        ms_total, _ = timer(1, lambda i: g.replay())
+        ms_step = ms_total / args.steps
+        gbs = nbytes / (ms_step * 1e-3) / 1e9
+        timing["graph_replay"] = round(ms_step * 1e3, 3)
+        print(f"[bench] {label}, one graph replay of {args.steps} steps: {ms_step * 1e3:.2f} us/step, "
+              f"{gbs:.1f} GB/s ({100 * gbs / HBM_PEAK_GBS:.1f}% of peak)", flush=True)
+    return ms_step, gbs, timing
+
+
+def launch_label(args):
+    return ("one HIP graph replay of the K steps" if args.launch == "graph"
+            else "K launches on the stream")
 
 
 def cpu_time(fn, runs=3):
@@ -610,16 +635,17 @@ def bench_quantize(args, torch, np, pd, workloads):
             "sf": torch.empty((rows, d // 16), dtype=torch.uint8, device="cuda")}
     replicas, reps = replicate(torch, base, nbytes, args.replicas)
     stream = torch.cuda.current_stream()
-    sptr = stream.cuda_stream
+    state = {"stream": stream.cuda_stream}
+    capture_stream = torch.cuda.Stream()
     timer = Timer(torch, stream)
 
     def step(i):
         r = replicas[i % reps]
         pd.nvfp4_quantize_activation(r["x"], r["gs"], 1 if rows > 1 else 0, r["q"], r["sf"], rows, d,
-                                     args.rule, sptr)
+                                     args.rule, state["stream"])
 
     print(f"[bench] {reps} replicas ({reps * nbytes / 1e9:.2f} GB)", flush=True)
-    ms_step, gbs = timed_steps(args, timer, step, nbytes, "quantize")
+    ms_step, gbs, timing = timed_steps(args, timer, step, nbytes, "quantize", state, capture_stream)
     run_copies(torch, args.copy_mib)
 
     cpu = None
@@ -642,6 +668,8 @@ def bench_quantize(args, torch, np, pd, workloads):
                      "rows": rows, "d": d, "rule": args.rule, "bytes_per_step": nbytes,
                      "replicas": reps, "operands": "HBM (rotated over >= 1 GB of copies)"}
     out["roofline"] = roofline(gbs, recorded_traffic(cfg.name, "quantize_blocks"))
+    out["config"]["launch"] = launch_label(args)
+    out["timing_us"] = timing
     out["cpu_baseline"] = with_speedup(cpu, gbs)
     return out
 
@@ -669,16 +697,22 @@ def bench_bf16x(args, torch, np, pd, workloads):
     replicas, reps = replicate(torch, base, nbytes, args.replicas)
     c = torch.empty((l, m), dtype=torch.int16, device="cuda")
     stream = torch.cuda.current_stream()
-    sptr = stream.cuda_stream
+    state = {"stream": stream.cuda_stream}
+    capture_stream = torch.cuda.Stream()
     timer = Timer(torch, stream)
+    _, ws_bytes = pd.nvfp4_gemv_plan(l, m, k, aligned=True)
+    if ws_bytes:
+        # the GEMV's split-K workspace, sized before any capture on both streams
+        pd.nvfp4_workspace_reserve(ws_bytes, stream)
+        pd.nvfp4_workspace_reserve(ws_bytes, capture_stream)
 
     def step(i):
         r = replicas[i % reps]
         pd.nvfp4_gemv_bf16x_launch(r["A"], r["sfA"], None, r["x"], r["xs"], args.rule, r["xq"],
-                                   r["sfx"], r["alpha"], c, l, m, k, sptr)
+                                   r["sfx"], r["alpha"], c, l, m, k, state["stream"])
 
     print(f"[bench] {reps} replicas ({reps * nbytes / 1e9:.2f} GB)", flush=True)
-    ms_step, gbs = timed_steps(args, timer, step, nbytes, "gemv_bf16x")
+    ms_step, gbs, timing = timed_steps(args, timer, step, nbytes, "gemv_bf16x", state, capture_stream)
     run_copies(torch, args.copy_mib)
 
     cpu = None
@@ -704,6 +738,8 @@ def bench_bf16x(args, torch, np, pd, workloads):
                      "l": l, "m": m, "k": k, "rule": args.rule, "bytes_per_step": nbytes,
                      "replicas": reps, "operands": "HBM (rotated over >= 1 GB of copies)"}
     out["roofline"] = roofline(gbs, None)
+    out["config"]["launch"] = launch_label(args)
+    out["timing_us"] = timing
     out["cpu_baseline"] = with_speedup(cpu, gbs)
     return out
 
@@ -721,12 +757,17 @@ def bench_smalln(args, torch, np, pd, workloads):
     replicas, reps = replicate(torch, base, nbytes, args.replicas)
     c = torch.empty((l, m, n), dtype=torch.int16, device="cuda")
     stream = torch.cuda.current_stream()
-    sptr = stream.cuda_stream
+    state = {"stream": stream.cuda_stream}
+    capture_stream = torch.cuda.Stream()
     timer = Timer(torch, stream)
     tuned = args.variant or args.ksplit
     tuning = {"variant": args.variant, "ksplit": args.ksplit}
     plan, ws_bytes = pd.nvfp4_gemm_smalln_plan(l, m, n, k, tuning=tuning if tuned else None)
     ws = torch.empty(max(ws_bytes, 4), dtype=torch.uint8, device="cuda")
+    if not tuned and ws_bytes:
+        # the library's split-K workspace, sized before any capture on both streams
+        pd.nvfp4_workspace_reserve(ws_bytes, stream)
+        pd.nvfp4_workspace_reserve(ws_bytes, capture_stream)
     if args.packed:
         pack_replicas(torch, pd, replicas, "A", "sfA", l, m, k)
 
@@ -735,18 +776,18 @@ def bench_smalln(args, torch, np, pd, workloads):
         if args.packed:
             pd.nvfp4_gemm_smalln_launch_packed(r["A_packed"], r["sfA_packed"], r["B"], r["sfB"],
                                                r["alpha"], c, l, m, n, k, out_type,
-                                               tuning if tuned else None, sptr)
+                                               tuning if tuned else None, state["stream"])
         elif tuned:
             pd.nvfp4_gemm_smalln_launch_tuned(r["A"], r["sfA"], r["B"], r["sfB"], r["alpha"], c, l, m,
-                                              n, k, out_type, tuning, ws, ws_bytes, sptr)
+                                              n, k, out_type, tuning, ws, ws_bytes, state["stream"])
         else:
             pd.nvfp4_gemm_smalln_launch(r["A"], r["sfA"], r["B"], r["sfB"], r["alpha"], c, l, m, n, k,
-                                        out_type, sptr)
+                                        out_type, state["stream"])
 
     print(f"[bench] plan path={plan.path} variant={plan.variant} ksplit={plan.ksplit}"
           f"{' (row-major plan; packed weights)' if args.packed else ''}; "
           f"{reps} replicas ({reps * nbytes / 1e9:.2f} GB)", flush=True)
-    ms_step, gbs = timed_steps(args, timer, step, nbytes, "smalln")
+    ms_step, gbs, timing = timed_steps(args, timer, step, nbytes, "smalln", state, capture_stream)
     run_copies(torch, args.copy_mib)
 
     cpu = None
@@ -780,6 +821,8 @@ def bench_smalln(args, torch, np, pd, workloads):
     kernel = mma_kernel_name(pd, plan, args.packed)
     extra = {} if kernel == "vec_tile" else {"mfma_tflops": flops / (ms_step * 1e-3) / 1e12}
     out["roofline"] = roofline(gbs, recorded_traffic(cfg.name, kernel), kernel=kernel, **extra)
+    out["config"]["launch"] = launch_label(args)
+    out["timing_us"] = timing
     out["cpu_baseline"] = with_speedup(cpu, gbs)
     return out
 
@@ -798,7 +841,8 @@ def bench_grouped(args, torch, np, pd, workloads):
     replicas, reps = replicate(torch, base, nbytes, args.replicas)
     c = torch.empty((T, n), dtype=torch.int16, device="cuda")
     stream = torch.cuda.current_stream()
-    sptr = stream.cuda_stream
+    state = {"stream": stream.cuda_stream}
+    capture_stream = torch.cuda.Stream()
     timer = Timer(torch, stream)
     tuning = {"variant": args.variant}
     if args.packed:
@@ -809,15 +853,15 @@ def bench_grouped(args, torch, np, pd, workloads):
         if args.packed:
             pd.nvfp4_grouped_gemv_launch_packed(r["X"], r["sfX"], r["W_packed"], r["sfW_packed"],
                                                 r["offsets"], r["gs_x"], r["gs_w"], c, T, E, n, k,
-                                                out_type, tuning, sptr)
+                                                out_type, tuning, state["stream"])
         else:
             pd.nvfp4_grouped_gemv_launch_tuned(r["X"], r["sfX"], r["W"], r["sfW"], r["offsets"],
                                                r["gs_x"], r["gs_w"], c, T, E, n, k, out_type, tuning,
-                                               sptr)
+                                               state["stream"])
 
     print(f"[bench] variant={args.variant or 'default'}; {reps} replicas "
           f"({reps * nbytes / 1e9:.2f} GB)", flush=True)
-    ms_step, gbs = timed_steps(args, timer, step, nbytes, "grouped")
+    ms_step, gbs, timing = timed_steps(args, timer, step, nbytes, "grouped", state, capture_stream)
     run_copies(torch, args.copy_mib)
 
     cpu = None
@@ -852,6 +896,8 @@ def bench_grouped(args, torch, np, pd, workloads):
     out["config"]["plan"] = {"path": plan.path, "variant": plan.variant,
                              "rows_per_block": plan.rows_per_block}
     out["roofline"] = roofline(gbs, recorded_traffic(cfg.name, kernel), kernel=kernel)
+    out["config"]["launch"] = launch_label(args)
+    out["timing_us"] = timing
     out["cpu_baseline"] = with_speedup(cpu, gbs)
     return out
 

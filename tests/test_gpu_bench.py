@@ -39,3 +39,25 @@ def test_bench_line_on_the_tiny_workload(capsys, launch):
     assert d["value"] == pytest.approx(18832 / (d["ms_per_step"] * 1e-3) / 1e9, rel=1e-3)
     assert d["parity"] == {"outputs": 128, "bit_identical": 128, "max_ulp": 0}
     assert d["cpu_baseline"]["kind"] == "oracle" and d["cpu_baseline"]["cores"] >= 1
+
+
+@pytest.mark.parametrize("path_args", [
+    ["--path", "quantize", "--act-config", "decode_x"],
+    ["--path", "gemv_bf16x", "--config", "tiny"],
+    ["--path", "smalln", "--smalln-config", "tiny_n3"],
+    ["--path", "grouped", "--moe-config", "moe_tiny"],
+], ids=["quantize", "bf16x", "smalln", "grouped"])
+@pytest.mark.parametrize("launch", ["stream", "graph"])
+def test_path_lines_time_stream_launches_or_one_graph_replay(capsys, path_args, launch):
+    assert bench.main(path_args + ["--steps", "5", "--warmup", "2", "--launch", launch,
+                                   "--no-cpu-baseline"]) == 0
+    lines = [l for l in capsys.readouterr().out.splitlines() if l.startswith("{")]
+    assert len(lines) == 1
+    d = json.loads(lines[0])
+    t = d["timing_us"]
+    assert (t["graph_replay"] is None) == (launch == "stream")
+    headline = t["graph_replay"] if launch == "graph" else t["stream_launches"]
+    assert abs(headline - d["ms_per_step"] * 1e3) < 1e-2
+    assert d["config"]["launch"] == bench.launch_label(bench.parse_args(["--launch", launch]))
+    assert d["value"] == pytest.approx(d["config"]["bytes_per_step"] / (d["ms_per_step"] * 1e-3) / 1e9,
+                                       rel=1e-3, abs=0.01)
