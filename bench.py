@@ -22,26 +22,30 @@ Timing: W warm-up steps, then a synchronisation, then exactly K steps between
 two HIP events on the launch stream, then a synchronisation.  A GPU-side
 delay kernel (about 0.8 ms) runs before the start event, so the stream is not
 idle while the host enqueues the first steps and the clocks have left their
-idle state.  With --launch stream (the default) the K steps are launched one
-by one from Python; the same K steps are also captured once into a HIP graph,
-replayed once untimed and timed as one replay, and both figures are
-reported (--launch graph makes the replay the headline figure).
+idle state.  The K steps are launched one by one from Python, and the same
+K steps are also captured once into a HIP graph, replayed once untimed and
+timed as one replay; both figures are reported.  With --launch graph (the
+default) the replay is the headline figure, as in a decode loop captured in
+a graph; --launch stream makes the one-by-one launches the headline.
 
 Each JSON line:
   value        algorithmic bytes per step (A + sfA + x + sfx + c) / time, GB/s
   roofline     the same rate against the 8 TB/s HBM peak, the kernel's HBM
                traffic from rocprofv3 counters when they were taken on this
-               kernel source, and the read rates of two streaming-read probes
-               measured in the same run (a flat 1 GiB read, and a read of the
-               workload's own A and sfA with the GEMV's load pattern)
+               kernel source, and the read rates of streaming-read probes
+               measured in the same run, each the faster of stream launches
+               and a graph replay (a flat 1 GiB read; the workload's own A and
+               sfA read with the long-row GEMV's load pattern; a flat read of
+               the same size)
   cpu_baseline the CPU oracle (plain C, fp64, OpenMP over rows) on the same
                workload on this host's cores, with the parity of the last
                timed call against it
 
 Other paths (--path), each printing its own JSON line of the same form (their
-steps are launched one by one; --launch graph adds the replay of a HIP graph
-holding the same K steps and makes it the reported figure, which keeps the
-stream busy under a kernel tracer that slows the host's launches):
+steps are launched one by one; with --launch graph, the default, the replay of
+a HIP graph holding the same K steps is added and is the reported figure,
+which also keeps the stream busy under a kernel tracer that slows the host's
+launches):
   quantize     the BF16 -> NVFP4 activation quantiser on a bf16 activation
                batch (--act-config tokens | decode_x)
   gemv_bf16x   the GEMV fed by a bf16 activation: quantiser + GEMV per step
@@ -83,6 +87,7 @@ GEMV_ORDER = ("tiny", "decode", "shortk", "gaussian", "batched")
 PREROLL_CYCLES = 2_000_000
 # at most this many input copies (the tiny workload would otherwise need 50000)
 MAX_REPLICAS = 64
+MAX_GRAPH_STEPS = 20000     # kernel nodes in one captured graph
 CSRC = os.path.join(ROOT, "precision_decode_amd", "csrc")
 PROFILES = os.path.join(ROOT, "profiles")
 # counter summaries under profiles/ are valid only for the source they were taken on
@@ -107,7 +112,7 @@ def parse_args(argv=None):
                    help="GEMV workload from workloads.CONFIGS (decode, batched, shortk, tiny, or "
                         "gaussian: bf16 draws quantised by the library's device quantiser, untimed), "
                         "or all: each in turn, one JSON line each, batched last")
-    p.add_argument("--launch", default="stream", choices=["graph", "stream"],
+    p.add_argument("--launch", default="graph", choices=["graph", "stream"],
                    help="time the K steps as one replay of a HIP graph that holds them, or "
                         "launched one by one on the stream")
     p.add_argument("--trace-cold", action="store_true",
@@ -141,7 +146,13 @@ def parse_args(argv=None):
     p.add_argument("--copy-mib", type=int, default=0,
                    help="after timing, run 4 plain device copies of this many MiB (the "
                         "known-size reference for HBM byte counters)")
-    return p.parse_args(argv)
+    args = p.parse_args(argv)
+    if args.steps < 1 or args.warmup < 0:
+        p.error("--steps must be at least 1 and --warmup at least 0")
+    if args.launch == "graph" and args.steps > MAX_GRAPH_STEPS:
+        p.error(f"--launch graph captures the K steps in one HIP graph: --steps at most "
+                f"{MAX_GRAPH_STEPS} (use --launch stream for more)")
+    return args
 
 
 def kernel_source_hash(kernel: str = "gemv") -> str:
@@ -384,7 +395,26 @@ def quantize_gaussian_on_device(torch, np, pd, raw, l, m, k):
     return out
 
 
-def flat_probe_gbs(torch, pd, timer, sptr, shared):
+def launch_timer(timer, state, capture_stream, modes):
+    """(n, call) -> ms for n calls of call(i), each launching on state["stream"]:
+    launched one by one ("stream") or as one replay of a HIP graph holding the
+    n calls ("graph"); with both modes, the faster of the two."""
+    def run(n, call):
+        best = None
+        for mode in modes:
+            if mode == "stream":
+                ms, _ = timer(n, call)
+            else:
+                g = capture_steps(timer.torch, n, call, state, capture_stream)
+                g.replay()                           # untimed: uploads the graph
+                timer.torch.cuda.synchronize()
+                ms, _ = timer(1, lambda i: g.replay())
+            best = ms if best is None else min(best, ms)
+        return best
+    return run
+
+
+def flat_probe_gbs(torch, pd, timed, state, shared):
     """The library's flat streaming-read probe over 1 GiB (measured once per run)."""
     if "flat_probe_gbs" not in shared:
         pbytes = 1 << 30
@@ -392,16 +422,16 @@ def flat_probe_gbs(torch, pd, timer, sptr, shared):
         pbuf.fill_(1)
         sink = torch.empty(4096, dtype=torch.int32, device="cuda")
         for _ in range(3):
-            pd.nvfp4_hbm_read_probe(pbuf, pbytes, sink, sptr)
+            pd.nvfp4_hbm_read_probe(pbuf, pbytes, sink, state["stream"])
         pn = 20
-        pms, _ = timer(pn, lambda i: pd.nvfp4_hbm_read_probe(pbuf, pbytes, sink, sptr))
+        pms = timed(pn, lambda i: pd.nvfp4_hbm_read_probe(pbuf, pbytes, sink, state["stream"]))
         shared["flat_probe_gbs"] = pbytes / (pms / pn * 1e-3) / 1e9
         del pbuf
         print(f"[bench] streaming-read probe (1 GiB): {shared['flat_probe_gbs']:.1f} GB/s", flush=True)
     return shared["flat_probe_gbs"]
 
 
-def row_probe_gbs(torch, pd, timer, sptr, replicas, l, m, k):
+def row_probe_gbs(torch, pd, timed, state, replicas, l, m, k):
     """The row-pattern read probe over every copy's A and sfA in turn: the read
     ceiling of the GEMV's load pattern for this weight, operands in HBM."""
     if k % 32 != 0:
@@ -411,29 +441,31 @@ def row_probe_gbs(torch, pd, timer, sptr, replicas, l, m, k):
     sink = torch.empty(-(-rows // 14), dtype=torch.int32, device="cuda")
     nbytes = rows * (k // 2 + k // 16)
     for i in range(min(reps, 4)):
-        pd.nvfp4_hbm_read_probe_rows(replicas[i]["A"], replicas[i]["sfA"], rows, k, sink, sptr)
+        pd.nvfp4_hbm_read_probe_rows(replicas[i]["A"], replicas[i]["sfA"], rows, k, sink,
+                                     state["stream"])
     pn = max(8, 4 * reps)
-    pms, _ = timer(pn, lambda i: pd.nvfp4_hbm_read_probe_rows(replicas[i % reps]["A"],
-                                                              replicas[i % reps]["sfA"], rows, k,
-                                                              sink, sptr))
+    pms = timed(pn, lambda i: pd.nvfp4_hbm_read_probe_rows(replicas[i % reps]["A"],
+                                                           replicas[i % reps]["sfA"], rows, k,
+                                                           sink, state["stream"]))
     gbs = nbytes / (pms / pn * 1e-3) / 1e9
     print(f"[bench] row-pattern read probe over A and sfA ({nbytes / 1e6:.1f} MB, rotated): "
           f"{gbs:.1f} GB/s ({pms / pn * 1e3:.2f} us per read)", flush=True)
     return gbs
 
 
-def flat_probe_same_size_gbs(torch, pd, timer, sptr, nbytes):
+def flat_probe_same_size_gbs(torch, pd, timed, state, nbytes):
     """The flat streaming-read probe over contiguous copies of `nbytes` (the
-    workload's A and sfA together), rotated over >= 1 GB: the read rate of a
-    plain sequential read of this size, operands in HBM."""
+    workload's A and sfA together), rotated over >= 1 GB (or over 64 copies,
+    for operands below 16 MB): the read rate of a plain sequential read of
+    this size, operands in HBM."""
     nb = -(-nbytes // 16) * 16
-    reps = max(2, -(-1_000_000_000 // nb))
+    reps = min(MAX_REPLICAS, max(2, -(-1_000_000_000 // nb)))   # at most 256 launches below
     bufs = [torch.ones(nb, dtype=torch.uint8, device="cuda") for _ in range(reps)]
     sink = torch.empty(4096, dtype=torch.int32, device="cuda")
     for i in range(reps):
-        pd.nvfp4_hbm_read_probe(bufs[i], nb, sink, sptr)
+        pd.nvfp4_hbm_read_probe(bufs[i], nb, sink, state["stream"])
     pn = max(8, 4 * reps)
-    pms, _ = timer(pn, lambda i: pd.nvfp4_hbm_read_probe(bufs[i % reps], nb, sink, sptr))
+    pms = timed(pn, lambda i: pd.nvfp4_hbm_read_probe(bufs[i % reps], nb, sink, state["stream"]))
     gbs = nb / (pms / pn * 1e-3) / 1e9
     del bufs
     print(f"[bench] flat read probe over {nb / 1e6:.1f} MB copies (rotated): {gbs:.1f} GB/s "
@@ -517,7 +549,9 @@ def bench_gemv(args, torch, np, pd, workloads, name=None, shared=None):
     warm_gbs = single = probe_gbs = probe_rows = probe_flat = None
     if not args.trace_cold:
         nw = min(args.steps, 500)
-        warm_ms, _ = timer(nw, lambda i: step(0))
+        warm_ms = launch_timer(timer, state, capture_stream, (args.launch,))(nw, lambda i: step(0))
+        # the read probes' ceiling: each timed both ways, the faster counts
+        timed = launch_timer(timer, state, capture_stream, ("stream", "graph"))
         warm_gbs = nbytes / (warm_ms / nw * 1e-3) / 1e9
         print(f"[bench] cache-resident (same buffers every step): {warm_gbs:.1f} GB/s", flush=True)
 
@@ -532,9 +566,9 @@ def bench_gemv(args, torch, np, pd, workloads, name=None, shared=None):
             print(f"[bench] single launches after a 512 MiB streaming read: p10 {single['p10']} us, "
                   f"p50 {single['p50']} us, p90 {single['p90']} us", flush=True)
         if not args.no_probe:
-            probe_gbs = flat_probe_gbs(torch, pd, timer, state["stream"], shared)
-            probe_rows = row_probe_gbs(torch, pd, timer, state["stream"], replicas, l, m, k)
-            probe_flat = flat_probe_same_size_gbs(torch, pd, timer, state["stream"],
+            probe_gbs = flat_probe_gbs(torch, pd, timed, state, shared)
+            probe_rows = row_probe_gbs(torch, pd, timed, state, replicas, l, m, k)
+            probe_flat = flat_probe_same_size_gbs(torch, pd, timed, state,
                                                   l * m * (k // 2 + k // 16))
     run_copies(torch, args.copy_mib)
 

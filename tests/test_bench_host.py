@@ -9,7 +9,7 @@ import bench
 
 def test_defaults_time_every_gemv_workload_batched_last():
     a = bench.parse_args([])
-    assert a.gpus == 1 and a.path == "gemv" and a.config == "all" and a.launch == "stream"
+    assert a.gpus == 1 and a.path == "gemv" and a.config == "all" and a.launch == "graph"
     assert a.steps > 0 and a.warmup > 0 and a.single_launches > 0 and not a.trace_cold
     import workloads
     assert set(bench.GEMV_ORDER) == set(workloads.CONFIGS)
@@ -170,3 +170,12 @@ def test_mma_kernel_name_follows_the_plan_form():
     assert bench.mma_kernel_name(FakePd, Plan(1, 3), True) == "mma_stream_packed"
     for name in ("mma_stream", "vec_tile", "mma_lds", "mma_generic", "mma_stream_packed"):
         assert name in bench.KERNEL_SOURCES
+
+
+def test_graph_launch_bounds_the_steps():
+    with pytest.raises(SystemExit):
+        bench.parse_args(["--steps", str(bench.MAX_GRAPH_STEPS + 1)])
+    assert bench.parse_args(["--steps", str(bench.MAX_GRAPH_STEPS + 1), "--launch", "stream"]).steps \
+        == bench.MAX_GRAPH_STEPS + 1
+    with pytest.raises(SystemExit):
+        bench.parse_args(["--steps", "0"])
