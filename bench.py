@@ -640,7 +640,8 @@ def mma_kernel_name(pd, plan, packed):
         return "mma_generic"
     form = pd.nvfp4_mma_variant_form(plan.variant)
     return {pd.NVFP4_MMA_FORM_VALU_TILES: "vec_tile",
-            pd.NVFP4_MMA_FORM_LDS_STAGED: "mma_lds"}.get(form, "mma_stream")
+            pd.NVFP4_MMA_FORM_LDS_STAGED: "mma_lds",
+            pd.NVFP4_MMA_FORM_LDS_VECTOR_REGS: "mma_lds"}.get(form, "mma_stream")
 
 
 def plan_kernel_name(pd, plan):
@@ -924,7 +925,7 @@ def bench_grouped(args, torch, np, pd, workloads):
                      "replicas": reps, "operands": "HBM (rotated over >= 1 GB of copies)",
                      "weights": "packed once by nvfp4_mma_pack_weight (not timed)" if args.packed
                                 else "row-major"}
-    plan = pd.nvfp4_grouped_gemv_plan(E, n, k, packed=args.packed,
+    plan = pd.nvfp4_grouped_gemv_plan(E, n, k, T, packed=args.packed,
                                       tuning={"variant": args.variant} if args.variant else None)
     kernel = mma_kernel_name(pd, plan, args.packed)
     out["config"]["plan"] = {"path": plan.path, "variant": plan.variant,

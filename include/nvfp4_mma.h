@@ -100,6 +100,7 @@ int nvfp4_gemm_smalln_launch(const uint8_t *A_packed, const uint8_t *sfA,
 #define NVFP4_MMA_FORM_MATRIX_CORES 0
 #define NVFP4_MMA_FORM_VALU_TILES 1
 #define NVFP4_MMA_FORM_LDS_STAGED 2
+#define NVFP4_MMA_FORM_LDS_VECTOR_REGS 3
 
 /*
  * Number of fast small-N / grouped kernel variants, and the shape of variant
@@ -122,7 +123,12 @@ int nvfp4_gemm_smalln_launch(const uint8_t *A_packed, const uint8_t *sfA,
  *    flight and waves (each wave takes a contiguous run of the workgroup's
  *    windows, so on inexact data the fp32 sums may round differently from a
  *    MATRIX_CORES variant).  Row-major weights only: with packed weights
- *    these variants are BAD_TUNING.
+ *    these variants are BAD_TUNING;
+ *  - NVFP4_MMA_FORM_LDS_VECTOR_REGS: as LDS_STAGED for the weight codes and
+ *    scales, while every lane loads its own vector codes and scale word from
+ *    L2 straight into registers (less LDS per workgroup, more workgroups per
+ *    compute unit; it pays while there are few vectors).  Row-major weights
+ *    only.
  * Each returns a status (BAD_TUNING for v outside 1 .. num_variants,
  * NULL_POINTER for a NULL output).
  */
@@ -156,15 +162,16 @@ int nvfp4_gemm_smalln_launch_tuned(const uint8_t *A_packed, const uint8_t *sfA,
 /*
  * The grouped plan the library would use (path, variant, K split (always 1),
  * rows per workgroup; the last three 0 for the generic kernel) for `experts`
- * weight matrices of n x k, as nvfp4_gemm_smalln_plan does for the small-N
- * GEMM; `in` may be NULL.  `packed` != 0 asks for the plan of the packed-weight
+ * weight matrices of n x k and `tokens` routed tokens (the launch's count:
+ * the default variant depends on the tokens per expert), as
+ * nvfp4_gemm_smalln_plan does for the small-N GEMM; `in` may be NULL.  `packed` != 0 asks for the plan of the packed-weight
  * launch (then `aligned` is ignored: packed operands are aligned by
  * definition), else `aligned` says whether the pointers meet the fast
  * kernels' alignment rules.  Returns a status (BAD_SHAPE as the matching
- * launch would, BAD_TUNING, NULL_POINTER for a NULL out).
+ * launch would, or for tokens < 0; BAD_TUNING; NULL_POINTER for a NULL out).
  */
-int nvfp4_grouped_gemv_plan(int64_t experts, int64_t n, int64_t k, int aligned, int packed,
-                            const nvfp4_mma_tuning_t *in, nvfp4_mma_tuning_t *out);
+int nvfp4_grouped_gemv_plan(int64_t experts, int64_t n, int64_t k, int64_t tokens, int aligned,
+                            int packed, const nvfp4_mma_tuning_t *in, nvfp4_mma_tuning_t *out);
 
 /*
  * The grouped (MoE) GEMV above.  Never splits K and needs no workspace.

@@ -36,6 +36,7 @@ NVFP4_OUT_BF16 = 1
 NVFP4_MMA_FORM_MATRIX_CORES = 0
 NVFP4_MMA_FORM_VALU_TILES = 1
 NVFP4_MMA_FORM_LDS_STAGED = 2
+NVFP4_MMA_FORM_LDS_VECTOR_REGS = 3
 
 NVFP4_GEMV_PATH_AUTO = 0
 NVFP4_GEMV_PATH_FAST = 1
@@ -158,7 +159,7 @@ def load():
     lib.nvfp4_mma_variant_form.restype = ctypes.c_int
     lib.nvfp4_mma_variant_form.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_int32)]
     lib.nvfp4_grouped_gemv_plan.restype = ctypes.c_int
-    lib.nvfp4_grouped_gemv_plan.argtypes = [_I64, _I64, _I64, ctypes.c_int, ctypes.c_int,
+    lib.nvfp4_grouped_gemv_plan.argtypes = [_I64, _I64, _I64, _I64, ctypes.c_int, ctypes.c_int,
                                             ctypes.POINTER(MmaTuning), ctypes.POINTER(MmaTuning)]
     lib.nvfp4_gemm_smalln_plan.restype = ctypes.c_int
     lib.nvfp4_gemm_smalln_plan.argtypes = [_I64, _I64, _I64, _I64, ctypes.c_int,
@@ -342,8 +343,8 @@ def nvfp4_mma_variant_info(v: int):
 
 
 def nvfp4_mma_variant_form(v: int) -> int:
-    """NVFP4_MMA_FORM_MATRIX_CORES (0), NVFP4_MMA_FORM_VALU_TILES (1) or
-    NVFP4_MMA_FORM_LDS_STAGED (2)."""
+    """NVFP4_MMA_FORM_MATRIX_CORES (0), NVFP4_MMA_FORM_VALU_TILES (1),
+    NVFP4_MMA_FORM_LDS_STAGED (2) or NVFP4_MMA_FORM_LDS_VECTOR_REGS (3)."""
     f = ctypes.c_int32()
     _check(load().nvfp4_mma_variant_form(v, ctypes.byref(f)), "nvfp4_mma_variant_form")
     return f.value
@@ -359,11 +360,11 @@ def nvfp4_gemm_smalln_plan(l, m, n, k, aligned=True, tuning=None):
     return out, int(ws.value)
 
 
-def nvfp4_grouped_gemv_plan(experts, n, k, aligned=True, packed=False, tuning=None):
-    """Returns the MmaTuning the grouped GEMV would use."""
+def nvfp4_grouped_gemv_plan(experts, n, k, tokens, aligned=True, packed=False, tuning=None):
+    """Returns the MmaTuning the grouped GEMV would use for `tokens` routed tokens."""
     out = MmaTuning()
-    _check(load().nvfp4_grouped_gemv_plan(experts, n, k, int(bool(aligned)), int(bool(packed)),
-                                          _mma_tuning(tuning), ctypes.byref(out)),
+    _check(load().nvfp4_grouped_gemv_plan(experts, n, k, tokens, int(bool(aligned)),
+                                          int(bool(packed)), _mma_tuning(tuning), ctypes.byref(out)),
            "nvfp4_grouped_gemv_plan")
     return out
 

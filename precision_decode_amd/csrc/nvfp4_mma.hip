@@ -35,7 +35,8 @@
 //
 // Three other forms sit beside it: the same products fed through LDS by
 // whole-line direct-to-LDS copies (mma_lds, the default for row-major
-// weights), weights packed once into the order the lanes read them
+// weights; with few vectors, only the weights, the vectors going straight to
+// registers), weights packed once into the order the lanes read them
 // (mma_pack_weight; every load instruction then reads 1 KiB contiguously
 // instead of 16 rows x 64 bytes), and, for one or two vectors, VALU row tiles
 // that read the row-major weights row-contiguously and take the few dot
@@ -355,7 +356,8 @@ constexpr int kGroupWins = 4;   // windows per staged scale group (64 scale byte
 
 // Loads issued after the last load of window j + 1, once window j + NS has
 // been issued, where j sits at position u of its group: windows j + 2 ..
-// j + NS, each with WL copies, plus SL scale copies where one starts a group.
+// j + NS, each with WL loads (its copies, and its vector loads into registers
+// when the vectors skip LDS), plus SL scale copies where one starts a group.
 template <int NS, int WL, int SL>
 constexpr int loads_after_next(int u) {
     int n = 0;
@@ -382,6 +384,23 @@ __device__ __forceinline__ int scale_pos(int rho, int w) { return w ^ (4 * ((rho
 // tiles and vectors 1 KiB apart).  The compiler does not relate these reads to the
 // direct-to-LDS loads (the kernel orders them with explicit vmcnt waits);
 // with plain C++ reads it placed a full vmcnt(0) drain at the loop head.
+template <int R>
+__device__ __forceinline__ void lds_read_weights(uint32_t aw0, uint32_t aw1, uint32_t as,
+                                                 u32x4 (&wq)[R][2], uint32_t (&ws)[R]) {
+    static_assert(R == 2, "two row tiles per wave");
+    asm volatile(
+        "ds_read_b128 %0, %6\n\t"
+        "ds_read_b128 %1, %7\n\t"
+        "ds_read_b128 %2, %6 offset:2048\n\t"
+        "ds_read_b128 %3, %7 offset:2048\n\t"
+        "ds_read_b32 %4, %8\n\t"
+        "ds_read_b32 %5, %8 offset:1024\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(wq[0][0]), "=&v"(wq[0][1]), "=&v"(wq[1][0]), "=&v"(wq[1][1]), "=&v"(ws[0]), "=&v"(ws[1])
+        : "v"(aw0), "v"(aw1), "v"(as)
+        : "memory");
+}
+
 template <int R>
 __device__ __forceinline__ void lds_read_window(uint32_t aw0, uint32_t aw1, uint32_t as,
                                                 u32x4 (&wq)[R][2], u32x4 (&vq)[2],
@@ -434,7 +453,14 @@ __device__ __forceinline__ void lds_read_window(uint32_t aw0, uint32_t aw1, uint
 //    addressed bytes);
 //  * one asm block of LDS reads per window gives every lane the same 32 code
 //    bytes and scale words that mma_stream's lane holds, so the decode and
-//    the MFMAs are mma_stream's.
+//    the MFMAs are mma_stream's;
+//  * with VR, only the weight rows and their scales go through LDS: every
+//    lane loads its own 32 vector code bytes and scale word of the window
+//    from L2 into registers (one ring of NS register slots), issued with the
+//    window just before its copies, so the same waits cover them.  The slot
+//    shrinks by the 16 vector rows, and more workgroups fit a compute unit;
+//    with many vectors, 16 rows x 32 bytes per lane cost more as register
+//    loads than as whole-line copies.
 // Staged rows are swizzled (chunk_pos at 16 bytes, scale_pos at 4 bytes) so
 // the reads hit distinct banks.  A window's loads always number the same
 // (out-of-range ones read nothing but still count), so explicit vmcnt waits
@@ -443,10 +469,12 @@ __device__ __forceinline__ void lds_read_window(uint32_t aw0, uint32_t aw1, uint
 // scales; rows and vectors past the block's read zeros or stale LDS, which
 // only reach outputs that are never written (an MFMA output row or column
 // depends on its own row and vector alone, and e2m1 codes are finite).
-template <int R, int NS, int W, bool GROUPED, bool S16>
+template <int R, int NS, int W, bool GROUPED, bool S16, bool VR = false>
 __global__ void __launch_bounds__(W * kWave) mma_lds(const MmaArgs a) {
     static_assert(NS == 2 || NS == 4, "window slots must divide a scale group");
-    constexpr int kRows = (R + 1) * kTile;               // staged rows: weight tiles, then vectors
+    static_assert(!VR || R == 2, "register-fed vectors: two row tiles");
+    constexpr int kRows = (R + (VR ? 0 : 1)) * kTile;    // staged rows: weight tiles, then vectors
+    constexpr int kVecLoads = VR ? 3 : 0;                // per window: 2 code loads, 1 scale load
     constexpr int kWinSlot = kRows * (kWinElems / 2);    // 128 bytes per row and window
     constexpr int kScaleSlot = kRows * kGroupWins * 16;  // 64 bytes per row and group
     constexpr int kWinLoads = kRows / 8;                 // 1 KiB copies per window
@@ -454,7 +482,7 @@ __global__ void __launch_bounds__(W * kWave) mma_lds(const MmaArgs a) {
     // and group start is 16-byte aligned (S16), else 4 rows x 64 bytes
     constexpr int kScaleLoads = S16 ? kRows / 16 : kRows / 4;
     constexpr int kWaveBytes = NS * kWinSlot + 2 * kScaleSlot;
-    static_assert(NS * kWinLoads + kScaleLoads <= 63, "loads in flight must fit the 6-bit vmcnt");
+    static_assert(NS * (kWinLoads + kVecLoads) + kScaleLoads <= 63, "loads in flight must fit the 6-bit vmcnt");
     __shared__ __attribute__((aligned(16))) uint8_t ring[W * kWaveBytes];
     __shared__ f32x4 red[(W > 1 ? W - 1 : 1) * R * kWave];
     const int lane = threadIdx.x & (kWave - 1);
@@ -548,8 +576,21 @@ __global__ void __launch_bounds__(W * kWave) mma_lds(const MmaArgs a) {
         // scales).  Offsets carry the out-of-range bit or-ed in: every
         // in-range offset is below 2^31, and adding a window offset to
         // kOutOfRange stays above it.
-        auto issue = [&](auto starts_group, int j, int slot) {
+        u32x4 vreg[NS][2];
+        uint32_t vsreg[NS];
+        auto issue = [&](auto starts_group, int j, auto slotc) {
+            constexpr int slot = decltype(slotc)::value;
             const int kw = kwb + j * kWinElems;   // past kwe for spare windows
+            if constexpr (VR) {
+                // this lane's 32 code bytes of vector li (bytes 32 kq .. +31 of
+                // the window) and its scale word, from L2 into registers
+                const uint32_t vo = static_cast<uint32_t>(li) * half + static_cast<uint32_t>(kw) / 2 +
+                                    32u * kq;
+                vreg[slot][0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vdesc, vo, 0, 0));
+                vreg[slot][1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vdesc, vo + 16, 0, 0));
+                vsreg[slot] = __builtin_amdgcn_raw_buffer_load_b32(
+                    svdesc, static_cast<uint32_t>(li) * sixteenth + static_cast<uint32_t>(kw) / 16 + 4u * kq, 0, 0);
+            }
             if constexpr (decltype(starts_group)::value) {
                 const int sl = kwe - kw;          // elements of the group in range
                 uint8_t *dst = sring + ((j / kGroupWins) & 1) * kScaleSlot;
@@ -586,13 +627,22 @@ __global__ void __launch_bounds__(W * kWave) mma_lds(const MmaArgs a) {
 #pragma unroll
         for (int r = 0; r < R; ++r) acc[r] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-        auto consume = [&](int j, int slot, int u) {
+        auto consume = [&](int j, auto slotc, int u) {
+            constexpr int slot = decltype(slotc)::value;
             const uint8_t *win = wring + slot * kWinSlot;
             const uint8_t *sc = sring + ((j / kGroupWins) & 1) * kScaleSlot;
             u32x4 wq[R][2], vq[2];
             uint32_t ws[R], vs;
-            lds_read_window<R>(lds_address(win + rw0), lds_address(win + rw1), lds_address(sc + rs[u]),
-                               wq, vq, ws, vs);
+            if constexpr (VR) {
+                lds_read_weights<R>(lds_address(win + rw0), lds_address(win + rw1), lds_address(sc + rs[u]),
+                                    wq, ws);
+                vq[0] = vreg[slot][0];
+                vq[1] = vreg[slot][1];
+                vs = vsreg[slot];
+            } else {
+                lds_read_window<R>(lds_address(win + rw0), lds_address(win + rw1), lds_address(sc + rs[u]),
+                                   wq, vq, ws, vs);
+            }
             // a lane piece past the wave's K range: zero scales (its codes are
             // zeros or stale)
             const uint32_t keep = lpiece < kwe - (kwb + j * kWinElems) ? ~0u : 0u;
@@ -626,28 +676,29 @@ __global__ void __launch_bounds__(W * kWave) mma_lds(const MmaArgs a) {
         auto step = [&](int g, auto pos) {
             constexpr int u = decltype(pos)::value;
             const int j = g * kGroupWins + u;
-            if (j < niter) consume(j, u % NS, u);   // wave-uniform
+            if (j < niter) consume(j, std::integral_constant<int, u % NS>{}, u);   // wave-uniform
             phase_fence();
-            issue(std::integral_constant<bool, (u + NS) % kGroupWins == 0>{}, j + NS, u % NS);
+            issue(std::integral_constant<bool, (u + NS) % kGroupWins == 0>{}, j + NS,
+                  std::integral_constant<int, u % NS>{});
             phase_fence();
-            wait_vmcnt<loads_after_next<NS, kWinLoads, kScaleLoads>(u)>();
+            wait_vmcnt<loads_after_next<NS, kWinLoads + kVecLoads, kScaleLoads>(u)>();
             phase_fence();
         };
         if (niter > 0) {   // wave-uniform
             phase_fence();
-            issue(std::true_type{}, 0, 0);
+            issue(std::true_type{}, 0, std::integral_constant<int, 0>{});
             phase_fence();
             if constexpr (NS == 4) {
-                issue(std::false_type{}, 1, 1);
+                issue(std::false_type{}, 1, std::integral_constant<int, 1>{});
                 phase_fence();
-                issue(std::false_type{}, 2, 2);
+                issue(std::false_type{}, 2, std::integral_constant<int, 2>{});
                 phase_fence();
-                issue(std::false_type{}, 3, 3);
+                issue(std::false_type{}, 3, std::integral_constant<int, 3>{});
             } else {
-                issue(std::false_type{}, 1, 1);
+                issue(std::false_type{}, 1, std::integral_constant<int, 1>{});
             }
             phase_fence();
-            wait_vmcnt<(NS - 1) * kWinLoads>();   // window 0 landed
+            wait_vmcnt<(NS - 1) * (kWinLoads + kVecLoads)>();   // window 0 landed
             phase_fence();
             for (int g = 0; g * kGroupWins < niter; ++g) {
                 step(g, std::integral_constant<int, 0>{});
@@ -985,7 +1036,7 @@ mma_splitk_reduce(const float *__restrict__ part, const float *__restrict__ alph
 }
 
 // ---------------------------------------------------------------- host side
-enum Form { kMatrixCores = 0, kValuTiles = 1, kLdsStaged = 2 };
+enum Form { kMatrixCores = 0, kValuTiles = 1, kLdsStaged = 2, kLdsVectorRegs = 3 };
 struct Variant {
     int R, U, W;
     int form;
@@ -999,29 +1050,42 @@ constexpr Variant kVariants[] = {
     {4, 2, 4, kValuTiles},   {8, 2, 4, kValuTiles},   {4, 4, 4, kValuTiles},
     {8, 4, 4, kValuTiles},   {2, 2, 4, kLdsStaged},   {2, 4, 4, kLdsStaged},
     {1, 2, 4, kLdsStaged},   {2, 2, 6, kLdsStaged},   {2, 2, 8, kLdsStaged},
-    {2, 2, 2, kLdsStaged},   {2, 4, 2, kLdsStaged},
+    {2, 2, 2, kLdsStaged},   {2, 4, 2, kLdsStaged},   {2, 2, 4, kLdsVectorRegs},
+    {2, 2, 2, kLdsVectorRegs},
 };
 constexpr int kNumVariants = static_cast<int>(sizeof(kVariants) / sizeof(kVariants[0]));
-// Defaults from MI355X sweeps of every variant.  Row-major weights: the
-// LDS-staged {2, 4, 4} on the decode-style small-N workloads (one 7168 x 16384
-// weight against 3 to 16 vectors: 16.0 and 15.5 us for 16 and 4 vectors,
-// against 21.5 and 18.2 for the register-fed {2, 2, 4}), the VALU tiles {4, 2,
-// 4} against 1 or 2 vectors (12.9 and 13.8 us against 17.8 and 18.0 on the
-// matrix cores, which pad the vectors to 16), the LDS-staged {2, 2, 2} on the
-// grouped decode workload (64 experts of 2048 x 7168, 128 tokens: 82 us
-// against 87-92 for {2, 2, 4} and 109 for the register-fed {2, 1, 8}; its
-// 38 KiB of LDS let four workgroups share a compute unit, and each wave
-// spreads its start over twice the windows).  Packed weights already load 1 KiB per
+// Defaults from MI355X sweeps of every variant (graph replays, rotated
+// operands).  Row-major weights, one 7168 x 16384 weight against n vectors:
+// the VALU tiles {4, 2, 4} for n <= 2 (12.9 and 13.8 us against 17.8 and 18.0
+// on the matrix cores, which pad the vectors to 16); the LDS-staged {2, 2, 4}
+// with the vectors in registers for 3 <= n <= 8 (15.0 / 15.0 / 15.2 / 15.6 us
+// at n = 3 / 4 / 6 / 8 against 15.6 / 15.6 / 15.7 / 15.8 for the all-LDS
+// {2, 4, 4}); the all-LDS {2, 4, 4} above 8 (16.0 and 16.3 us at 12 and 16
+// against 16.1-16.5 and 17.0-17.4 with the vectors in registers, whose 16
+// rows then cost more as register loads than as whole-line copies).  The
+// grouped GEMV (64 experts of 2048 x 7168, 128 tokens): the LDS-staged {2, 2,
+// 2} with the vectors in registers while the experts average at most 4
+// tokens (78.1 us against 80.1 for the all-LDS {2, 2, 2}, 83-92 for {2, 2, 4}
+// and 109 for the register-fed {2, 1, 8}); its 26 KiB of LDS let six
+// workgroups share a compute unit.  Packed weights already load 1 KiB per
 // instruction: {2, 2, 4} and {2, 1, 8} on the matrix cores.  The VALU tiles
 // never split K, so they are the default only while their tiles fill the GPU.
 constexpr int kDefaultSmallN = 11;
+constexpr int kDefaultSmallNMid = 17;
 constexpr int kDefaultSmallNPacked = 2;
 constexpr int kDefaultSmallNFew = 6;
 constexpr int64_t kFewVectors = 2;
+constexpr int64_t kMidVectors = 8;
 constexpr int kDefaultGrouped = 15;
+constexpr int kDefaultGroupedFew = 18;
+constexpr int64_t kFewTokensPerExpert = 4;
 constexpr int kDefaultGroupedPacked = 3;
 static_assert(kVariants[kDefaultSmallN].form == kLdsStaged && kVariants[kDefaultSmallN].U == 4 &&
+                  kVariants[kDefaultSmallNMid].form == kLdsVectorRegs &&
+                  kVariants[kDefaultSmallNMid].W == 4 &&
                   kVariants[kDefaultGrouped].form == kLdsStaged && kVariants[kDefaultGrouped].W == 2 &&
+                  kVariants[kDefaultGroupedFew].form == kLdsVectorRegs &&
+                  kVariants[kDefaultGroupedFew].W == 2 &&
                   kVariants[kDefaultSmallNPacked].form == kMatrixCores &&
                   kVariants[kDefaultGroupedPacked].form == kMatrixCores &&
                   kVariants[kDefaultSmallNFew].form == kValuTiles,
@@ -1049,6 +1113,8 @@ MmaKernel fast_kernel(int v) {
     case 14: return P ? nullptr : mma_lds<2, 2, 8, G, S16>;
     case 15: return P ? nullptr : mma_lds<2, 2, 2, G, S16>;
     case 16: return P ? nullptr : mma_lds<2, 4, 2, G, S16>;
+    case 17: return P ? nullptr : mma_lds<2, 2, 4, G, S16, true>;
+    case 18: return P ? nullptr : mma_lds<2, 2, 2, G, S16, true>;
     default: return nullptr;
     }
 }
@@ -1117,14 +1183,18 @@ int make_plan(int64_t groups, int64_t rows, int64_t nvec_per_group, int64_t k, b
         if (tun.variant > 0) {
             p->variant = tun.variant - 1;
         } else if (grouped) {
-            p->variant = packed ? kDefaultGroupedPacked : kDefaultGrouped;
+            // nvec_per_group: the tokens per expert on average, rounded up
+            p->variant = packed ? kDefaultGroupedPacked
+                                : nvec_per_group <= kFewTokensPerExpert ? kDefaultGroupedFew
+                                                                        : kDefaultGrouped;
         } else if (packed) {
             p->variant = kDefaultSmallNPacked;
         } else {
             const int64_t tiles = groups * ceil_div(rows, int64_t(kVariants[kDefaultSmallNFew].R));
             p->variant = (nvec_per_group <= kFewVectors && tiles >= 4 * kComputeUnits)
                              ? kDefaultSmallNFew
-                             : kDefaultSmallN;
+                         : nvec_per_group <= kMidVectors ? kDefaultSmallNMid
+                                                         : kDefaultSmallN;
         }
         const Variant &v = kVariants[p->variant];
         if (v.form == kValuTiles) {
@@ -1366,14 +1436,16 @@ int nvfp4_gemm_smalln_plan(int64_t l, int64_t m, int64_t n, int64_t k, int align
     return NVFP4_GEMV_OK;
 }
 
-int nvfp4_grouped_gemv_plan(int64_t experts, int64_t n, int64_t k, int aligned, int packed,
-                            const nvfp4_mma_tuning_t *in, nvfp4_mma_tuning_t *out) {
+int nvfp4_grouped_gemv_plan(int64_t experts, int64_t n, int64_t k, int64_t tokens, int aligned,
+                            int packed, const nvfp4_mma_tuning_t *in, nvfp4_mma_tuning_t *out) {
     if (!out) return NVFP4_GEMV_ERR_NULL_POINTER;
     int s = check_dims(experts, n, 0, k, true);
     if (s != NVFP4_GEMV_OK) return s;
+    if (tokens < 0) return NVFP4_GEMV_ERR_BAD_SHAPE;
     if (packed && (k % 64 != 0 || k > kMaxFastK)) return NVFP4_GEMV_ERR_BAD_SHAPE;
     Plan p;
-    s = make_plan(experts, n, 0, k, packed != 0 || aligned != 0, true, in, &p, packed != 0);
+    s = make_plan(experts, n, ceil_div(tokens, experts), k, packed != 0 || aligned != 0, true, in, &p,
+                  packed != 0);
     if (s != NVFP4_GEMV_OK) return s;
     out->path = p.path;
     out->variant = p.path == NVFP4_GEMV_PATH_FAST ? p.variant + 1 : 0;
@@ -1496,7 +1568,7 @@ int nvfp4_grouped_gemv_launch_packed(const uint8_t *X_packed, const uint8_t *sfX
                              experts, n, k, out_type, true);
     if (s != NVFP4_GEMV_OK) return s;
     Plan p;
-    s = make_plan(experts, n, 0, k, true, true, tuning, &p, true);
+    s = make_plan(experts, n, ceil_div(tokens, experts), k, true, true, tuning, &p, true);
     if (s != NVFP4_GEMV_OK) return s;
     if (tokens == 0) return NVFP4_GEMV_OK;
     MmaArgs a = {};
@@ -1526,7 +1598,8 @@ int nvfp4_grouped_gemv_launch_tuned(const uint8_t *X_packed, const uint8_t *sfX,
                              n, k, out_type);
     if (s != NVFP4_GEMV_OK) return s;
     Plan p;
-    s = make_plan(experts, n, 0, k, aligned_ptrs(W_packed, sfW, X_packed, sfX), true, tuning, &p);
+    s = make_plan(experts, n, ceil_div(tokens, experts), k, aligned_ptrs(W_packed, sfW, X_packed, sfX),
+                  true, tuning, &p);
     if (s != NVFP4_GEMV_OK) return s;
     if (tokens == 0) return NVFP4_GEMV_OK;
     MmaArgs a = {};

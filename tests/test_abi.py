@@ -324,7 +324,8 @@ def test_smalln_plans(lib):
         r, u, w = pd.nvfp4_mma_variant_info(v)
         form = pd.nvfp4_mma_variant_form(v)
         forms.add(form)
-        if form in (pd.NVFP4_MMA_FORM_MATRIX_CORES, pd.NVFP4_MMA_FORM_LDS_STAGED):
+        if form in (pd.NVFP4_MMA_FORM_MATRIX_CORES, pd.NVFP4_MMA_FORM_LDS_STAGED,
+                    pd.NVFP4_MMA_FORM_LDS_VECTOR_REGS):
             assert r in (1, 2) and u >= 1 and 1 <= w <= 16
             t, ws = pd.nvfp4_gemm_smalln_plan(3, 100, 5, 4096, tuning={"variant": v, "ksplit": 3})
             assert t.variant == v and t.ksplit == 3 and ws == 3 * 3 * 100 * 5 * 4
@@ -340,7 +341,7 @@ def test_smalln_plans(lib):
                 with pytest.raises(pd.Nvfp4GemvError):
                     pd.nvfp4_gemm_smalln_plan(3, 100, 5, 4096, tuning=bad)
     assert forms == {pd.NVFP4_MMA_FORM_MATRIX_CORES, pd.NVFP4_MMA_FORM_VALU_TILES,
-                     pd.NVFP4_MMA_FORM_LDS_STAGED}
+                     pd.NVFP4_MMA_FORM_LDS_STAGED, pd.NVFP4_MMA_FORM_LDS_VECTOR_REGS}
     for bad_v in (0, n + 1):
         with pytest.raises(pd.Nvfp4GemvError):
             pd.nvfp4_mma_variant_form(bad_v)
@@ -417,48 +418,62 @@ def test_default_plans_of_the_benchmark_workloads(lib, l, m, k, variant):
 
 def test_smalln_default_form_by_vector_count(lib):
     """One or two vectors against a weight that fills the GPU with 4-row tiles
-    go to the VALU tiles; more vectors, or too few tiles, to the matrix cores
-    fed through LDS (row-major weights) or read directly (packed weights)."""
+    go to the VALU tiles; 3 to 8 vectors (or one or two with too few tiles) to
+    the matrix cores with LDS-staged weights and the vectors in registers;
+    more vectors to the all-LDS form (row-major weights)."""
     for n in (1, 2):
         t, ws = pd.nvfp4_gemm_smalln_plan(1, 7168, n, 16384)
         assert pd.nvfp4_mma_variant_form(t.variant) == pd.NVFP4_MMA_FORM_VALU_TILES
         assert pd.nvfp4_mma_variant_info(t.variant) == (4, 2, 4)
         assert t.ksplit == 1 and ws == 0 and t.rows_per_block == 4
-    for l, m, n, k in ((1, 7168, 3, 16384), (1, 7168, 16, 16384), (1, 256, 2, 16384)):
+    for l, m, n, k in ((1, 7168, 3, 16384), (1, 7168, 8, 16384), (1, 256, 2, 16384)):
+        t, _ = pd.nvfp4_gemm_smalln_plan(l, m, n, k)
+        assert pd.nvfp4_mma_variant_form(t.variant) == pd.NVFP4_MMA_FORM_LDS_VECTOR_REGS, (l, m, n, k)
+        assert pd.nvfp4_mma_variant_info(t.variant) == (2, 2, 4)
+    for l, m, n, k in ((1, 7168, 9, 16384), (1, 7168, 16, 16384)):
         t, _ = pd.nvfp4_gemm_smalln_plan(l, m, n, k)
         assert pd.nvfp4_mma_variant_form(t.variant) == pd.NVFP4_MMA_FORM_LDS_STAGED, (l, m, n, k)
         assert pd.nvfp4_mma_variant_info(t.variant) == (2, 4, 4)
 
 
 def test_grouped_plan(lib):
-    """The grouped plan: LDS-staged matrix cores on row-major weights, the
+    """The grouped plan: LDS-staged matrix cores on row-major weights (with the
+    tokens in registers while the experts average at most 4 tokens), the
     register-fed ones on packed weights, the generic kernel off the fast
     shapes; never a K split."""
-    t = pd.nvfp4_grouped_gemv_plan(64, 2048, 7168)
-    assert t.path == pd.NVFP4_GEMV_PATH_FAST and t.ksplit == 1
+    for tokens in (0, 128, 256):
+        t = pd.nvfp4_grouped_gemv_plan(64, 2048, 7168, tokens)
+        assert t.path == pd.NVFP4_GEMV_PATH_FAST and t.ksplit == 1
+        assert pd.nvfp4_mma_variant_form(t.variant) == pd.NVFP4_MMA_FORM_LDS_VECTOR_REGS
+        assert pd.nvfp4_mma_variant_info(t.variant) == (2, 2, 2)
+    t = pd.nvfp4_grouped_gemv_plan(64, 2048, 7168, 257)
     assert pd.nvfp4_mma_variant_form(t.variant) == pd.NVFP4_MMA_FORM_LDS_STAGED
     assert pd.nvfp4_mma_variant_info(t.variant) == (2, 2, 2)
-    t = pd.nvfp4_grouped_gemv_plan(64, 2048, 7168, packed=True)
+    t = pd.nvfp4_grouped_gemv_plan(64, 2048, 7168, 128, packed=True)
     assert pd.nvfp4_mma_variant_form(t.variant) == pd.NVFP4_MMA_FORM_MATRIX_CORES
     assert pd.nvfp4_mma_variant_info(t.variant) == (2, 1, 8)
-    t = pd.nvfp4_grouped_gemv_plan(4, 96, 96)                   # k % 64 != 0
+    t = pd.nvfp4_grouped_gemv_plan(4, 96, 96, 20)               # k % 64 != 0
     assert t.path == pd.NVFP4_GEMV_PATH_GENERIC and t.variant == 0
-    t = pd.nvfp4_grouped_gemv_plan(4, 96, 128, aligned=False)
+    t = pd.nvfp4_grouped_gemv_plan(4, 96, 128, 20, aligned=False)
     assert t.path == pd.NVFP4_GEMV_PATH_GENERIC
     staged = [v for v in range(1, pd.nvfp4_mma_num_variants() + 1)
-              if pd.nvfp4_mma_variant_form(v) == pd.NVFP4_MMA_FORM_LDS_STAGED]
-    t = pd.nvfp4_grouped_gemv_plan(4, 96, 128, tuning={"variant": staged[-1], "rows_per_block": 20})
+              if pd.nvfp4_mma_variant_form(v) in (pd.NVFP4_MMA_FORM_LDS_STAGED,
+                                                  pd.NVFP4_MMA_FORM_LDS_VECTOR_REGS)]
+    t = pd.nvfp4_grouped_gemv_plan(4, 96, 128, 20, tuning={"variant": staged[-1], "rows_per_block": 20})
     assert t.variant == staged[-1] and t.rows_per_block == 20
-    for kw in ({"packed": True, "k": 96}, {"k": 0}, {"experts": 0}):
-        args = {"experts": 4, "n": 96, "k": 128}
+    for kw in ({"packed": True, "k": 96}, {"k": 0}, {"experts": 0}, {"tokens": -1}):
+        args = {"experts": 4, "n": 96, "k": 128, "tokens": 20}
         args.update(kw)
         packed = args.pop("packed", False)
         with pytest.raises(pd.Nvfp4GemvError):
-            pd.nvfp4_grouped_gemv_plan(args["experts"], args["n"], args["k"], packed=packed)
-    for kw in ({"tuning": {"ksplit": 2}}, {"packed": True, "tuning": {"variant": staged[0]}}):
-        with pytest.raises(pd.Nvfp4GemvError):
-            pd.nvfp4_grouped_gemv_plan(4, 96, 128, **kw)
-    assert lib.nvfp4_grouped_gemv_plan(4, 96, 128, 1, 0, None, None) == pd.NVFP4_GEMV_ERR_NULL_POINTER
+            pd.nvfp4_grouped_gemv_plan(args["experts"], args["n"], args["k"], args["tokens"],
+                                       packed=packed)
+    for v in (staged[0], staged[-1]):
+        for kw in ({"tuning": {"ksplit": 2}}, {"packed": True, "tuning": {"variant": v}}):
+            with pytest.raises(pd.Nvfp4GemvError):
+                pd.nvfp4_grouped_gemv_plan(4, 96, 128, 20, **kw)
+    assert lib.nvfp4_grouped_gemv_plan(4, 96, 128, 20, 1, 0, None, None) == \
+        pd.NVFP4_GEMV_ERR_NULL_POINTER
 
 
 # ---------------------------------------------------------------- packed weights
@@ -518,8 +533,10 @@ def test_packed_launch_validation(lib):
             if pd.nvfp4_mma_variant_form(v) == pd.NVFP4_MMA_FORM_VALU_TILES]
     staged = [v for v in range(1, pd.nvfp4_mma_num_variants() + 1)
               if pd.nvfp4_mma_variant_form(v) == pd.NVFP4_MMA_FORM_LDS_STAGED]
-    for bad in ((0, valu[0], 0, 0), (0, staged[0], 0, 0), (2, 0, 0, 0), (0, 1, 0, 8), (0, 3, 0, 24),
-                (0, 1, 0, 48)):
+    vregs = [v for v in range(1, pd.nvfp4_mma_num_variants() + 1)
+             if pd.nvfp4_mma_variant_form(v) == pd.NVFP4_MMA_FORM_LDS_VECTOR_REGS]
+    for bad in ((0, valu[0], 0, 0), (0, staged[0], 0, 0), (0, vregs[0], 0, 0), (2, 0, 0, 0),
+                (0, 1, 0, 8), (0, 3, 0, 24), (0, 1, 0, 48)):
         # VALU or LDS-staged variants, generic path, partial tiles
         assert s(tuning=bad) == pd.NVFP4_GEMV_ERR_BAD_TUNING, bad
         assert gr(tuning=bad) == pd.NVFP4_GEMV_ERR_BAD_TUNING, bad

@@ -158,14 +158,16 @@ def test_mma_kernel_name_follows_the_plan_form():
         NVFP4_GEMV_PATH_FAST = 1
         NVFP4_MMA_FORM_VALU_TILES = 1
         NVFP4_MMA_FORM_LDS_STAGED = 2
+        NVFP4_MMA_FORM_LDS_VECTOR_REGS = 3
 
         @staticmethod
         def nvfp4_mma_variant_form(v):
-            return {3: 0, 7: 1, 11: 2}[v]
+            return {3: 0, 7: 1, 11: 2, 18: 3}[v]
 
     assert bench.mma_kernel_name(FakePd, Plan(1, 3), False) == "mma_stream"
     assert bench.mma_kernel_name(FakePd, Plan(1, 7), False) == "vec_tile"
     assert bench.mma_kernel_name(FakePd, Plan(1, 11), False) == "mma_lds"
+    assert bench.mma_kernel_name(FakePd, Plan(1, 18), False) == "mma_lds"
     assert bench.mma_kernel_name(FakePd, Plan(2, 0), False) == "mma_generic"
     assert bench.mma_kernel_name(FakePd, Plan(1, 3), True) == "mma_stream_packed"
     for name in ("mma_stream", "vec_tile", "mma_lds", "mma_generic", "mma_stream_packed"):

@@ -79,7 +79,7 @@ def test_smalln_default_plan_shapes(l, m, n, k):
     assert_bits_equal(run_smalln(ops, l, m, n, k), oracle_smalln(ops, l, m, n, k), f"{(l, m, n, k)}")
 
 
-NUM_MMA_VARIANTS = 17
+NUM_MMA_VARIANTS = 19
 
 
 def valu_tiles(v):
@@ -169,7 +169,8 @@ def test_lds_staged_gaussian_within_tolerance(ksplit):
     dev = to_device(ops)
     want = oracle_smalln(ops, l, m, n, k)
     staged = [v for v in range(1, NUM_MMA_VARIANTS + 1)
-              if pd.nvfp4_mma_variant_form(v) == pd.NVFP4_MMA_FORM_LDS_STAGED]
+              if pd.nvfp4_mma_variant_form(v) in (pd.NVFP4_MMA_FORM_LDS_STAGED,
+                                                  pd.NVFP4_MMA_FORM_LDS_VECTOR_REGS)]
     assert staged
     for v in staged:
         for rpb in (0, 13):
@@ -193,7 +194,8 @@ def test_lds_staged_scales_at_4_byte_alignment():
         dev[key] = buf[4:4 + t.numel()].view(t.shape)
         assert dev[key].data_ptr() % 16 == 4
     staged = [v for v in range(1, NUM_MMA_VARIANTS + 1)
-              if pd.nvfp4_mma_variant_form(v) == pd.NVFP4_MMA_FORM_LDS_STAGED]
+              if pd.nvfp4_mma_variant_form(v) in (pd.NVFP4_MMA_FORM_LDS_STAGED,
+                                                  pd.NVFP4_MMA_FORM_LDS_VECTOR_REGS)]
     for v in staged:
         for ks in (1, 2):
             got = run_smalln(ops, l, m, n, k, tuning={"variant": v, "ksplit": ks}, dev=dev)
