@@ -141,7 +141,8 @@ int nvfp4_mma_variant_form(int v, int32_t *form);
  * The small-N plan the library would use (path, variant, K split, rows per
  * workgroup; the last three 0 for the generic kernel) and the workspace it
  * needs, as nvfp4_gemv_plan does for the GEMV; `in` may be NULL.  `aligned`
- * says whether the pointers meet the fast kernels' alignment rules.
+ * says whether the pointers meet the fast kernels' alignment rules.  Returns
+ * a status (BAD_SHAPE as the launch would, BAD_TUNING, NULL_POINTER).
  */
 int nvfp4_gemm_smalln_plan(int64_t l, int64_t m, int64_t n, int64_t k, int aligned,
                            const nvfp4_mma_tuning_t *in, nvfp4_mma_tuning_t *out,
@@ -168,7 +169,7 @@ int nvfp4_gemm_smalln_launch_tuned(const uint8_t *A_packed, const uint8_t *sfA,
  * launch (then `aligned` is ignored: packed operands are aligned by
  * definition), else `aligned` says whether the pointers meet the fast
  * kernels' alignment rules.  Returns a status (BAD_SHAPE as the matching
- * launch would, or for tokens < 0; BAD_TUNING; NULL_POINTER for a NULL out).
+ * launch would, BAD_TUNING, NULL_POINTER for a NULL out).
  */
 int nvfp4_grouped_gemv_plan(int64_t experts, int64_t n, int64_t k, int64_t tokens, int aligned,
                             int packed, const nvfp4_mma_tuning_t *in, nvfp4_mma_tuning_t *out);

@@ -53,20 +53,15 @@
 #include <type_traits>
 
 #include "device_common.h"
+#include "mma_plan.h"
 #include "nvfp4_gemv.h"
 #include "nvfp4_mma.h"
 
 namespace {
 
 using namespace nvfp4dev;
+using namespace nvfp4mmaplan;
 
-constexpr int kTile = 16;            // MFMA tile: 16 weight rows x 16 vectors
-constexpr int kWinElems = 256;       // K elements of one window: 128 bytes of every row
-constexpr int kLaneElems = 64;       // K elements of one window in one lane (32 code bytes)
-constexpr int64_t kMaxFastK = int64_t(1) << 26;   // keeps 32-row descriptors within 31 bits
-constexpr int64_t kComputeUnits = 256;            // CUs of an MI355X (8 XCDs x 32)
-constexpr int kReduceThreads = 256;
-constexpr int kGenericWaves = 4;
 constexpr int64_t kSliceElems = 2048;   // VALU tiles: K elements of one slice, 1 KiB of a row
 // Packed weights (nvfp4_mma_pack_weight): one window of one 16-row tile is
 // 2 KiB of codes (two 1 KiB halves, 16 bytes per lane) and 256 bytes of
@@ -1036,61 +1031,7 @@ mma_splitk_reduce(const float *__restrict__ part, const float *__restrict__ alph
 }
 
 // ---------------------------------------------------------------- host side
-enum Form { kMatrixCores = 0, kValuTiles = 1, kLdsStaged = 2, kLdsVectorRegs = 3 };
-struct Variant {
-    int R, U, W;
-    int form;
-};
-// Matrix cores (mma_stream) and matrix cores fed through LDS (mma_lds): {row
-// tiles of 16 per wave, windows in flight, waves per workgroup}.  VALU row
-// tiles (vec_tile): {rows per tile, vectors per pass, waves per workgroup}.
-constexpr Variant kVariants[] = {
-    {1, 2, 4, kMatrixCores}, {1, 2, 8, kMatrixCores}, {2, 2, 4, kMatrixCores},
-    {2, 1, 8, kMatrixCores}, {1, 3, 4, kMatrixCores}, {2, 2, 8, kMatrixCores},
-    {4, 2, 4, kValuTiles},   {8, 2, 4, kValuTiles},   {4, 4, 4, kValuTiles},
-    {8, 4, 4, kValuTiles},   {2, 2, 4, kLdsStaged},   {2, 4, 4, kLdsStaged},
-    {1, 2, 4, kLdsStaged},   {2, 2, 6, kLdsStaged},   {2, 2, 8, kLdsStaged},
-    {2, 2, 2, kLdsStaged},   {2, 4, 2, kLdsStaged},   {2, 2, 4, kLdsVectorRegs},
-    {2, 2, 2, kLdsVectorRegs},
-};
-constexpr int kNumVariants = static_cast<int>(sizeof(kVariants) / sizeof(kVariants[0]));
-// Defaults from MI355X sweeps of every variant (graph replays, rotated
-// operands).  Row-major weights, one 7168 x 16384 weight against n vectors:
-// the VALU tiles {4, 2, 4} for n <= 2 (12.9 and 13.8 us against 17.8 and 18.0
-// on the matrix cores, which pad the vectors to 16); the LDS-staged {2, 2, 4}
-// with the vectors in registers for 3 <= n <= 8 (15.0 / 15.0 / 15.2 / 15.6 us
-// at n = 3 / 4 / 6 / 8 against 15.6 / 15.6 / 15.7 / 15.8 for the all-LDS
-// {2, 4, 4}); the all-LDS {2, 4, 4} above 8 (16.0 and 16.3 us at 12 and 16
-// against 16.1-16.5 and 17.0-17.4 with the vectors in registers, whose 16
-// rows then cost more as register loads than as whole-line copies).  The
-// grouped GEMV (64 experts of 2048 x 7168, 128 tokens): the LDS-staged {2, 2,
-// 2} with the vectors in registers while the experts average at most 4
-// tokens (78.1 us against 80.1 for the all-LDS {2, 2, 2}, 83-92 for {2, 2, 4}
-// and 109 for the register-fed {2, 1, 8}); its 26 KiB of LDS let six
-// workgroups share a compute unit.  Packed weights already load 1 KiB per
-// instruction: {2, 2, 4} and {2, 1, 8} on the matrix cores.  The VALU tiles
-// never split K, so they are the default only while their tiles fill the GPU.
-constexpr int kDefaultSmallN = 11;
-constexpr int kDefaultSmallNMid = 17;
-constexpr int kDefaultSmallNPacked = 2;
-constexpr int kDefaultSmallNFew = 6;
-constexpr int64_t kFewVectors = 2;
-constexpr int64_t kMidVectors = 8;
-constexpr int kDefaultGrouped = 15;
-constexpr int kDefaultGroupedFew = 18;
-constexpr int64_t kFewTokensPerExpert = 4;
-constexpr int kDefaultGroupedPacked = 3;
-static_assert(kVariants[kDefaultSmallN].form == kLdsStaged && kVariants[kDefaultSmallN].U == 4 &&
-                  kVariants[kDefaultSmallNMid].form == kLdsVectorRegs &&
-                  kVariants[kDefaultSmallNMid].W == 4 &&
-                  kVariants[kDefaultGrouped].form == kLdsStaged && kVariants[kDefaultGrouped].W == 2 &&
-                  kVariants[kDefaultGroupedFew].form == kLdsVectorRegs &&
-                  kVariants[kDefaultGroupedFew].W == 2 &&
-                  kVariants[kDefaultSmallNPacked].form == kMatrixCores &&
-                  kVariants[kDefaultGroupedPacked].form == kMatrixCores &&
-                  kVariants[kDefaultSmallNFew].form == kValuTiles,
-              "the defaults name the variants measured above");
-
+// (shape rules, variants, defaults and the launch plan are in mma_plan.h)
 typedef void (*MmaKernel)(const MmaArgs);
 
 template <bool G, bool P, bool S16 = false>
@@ -1117,136 +1058,6 @@ MmaKernel fast_kernel(int v) {
     case 18: return P ? nullptr : mma_lds<2, 2, 2, G, S16, true>;
     default: return nullptr;
     }
-}
-
-int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
-
-struct Plan {
-    int path;
-    int variant;
-    int64_t ksplit, kchunk, row_blocks, rows_per_block, groups;
-    int threads;
-    size_t ws_bytes;
-};
-
-bool fits_int64_product(int64_t a, int64_t b) { return a == 0 || b <= INT64_MAX / a; }
-
-// groups x rows x (k/2) and the other byte counts within int64, outputs < 2^31.
-int check_dims(int64_t groups, int64_t rows, int64_t nvec, int64_t k, bool allow_zero_vec) {
-    if (groups < 1 || rows < 1 || nvec < (allow_zero_vec ? 0 : 1) || k < 16 || k % 16 != 0)
-        return NVFP4_GEMV_ERR_BAD_SHAPE;
-    if (k >= (int64_t(1) << 31)) return NVFP4_GEMV_ERR_BAD_SHAPE;
-    if (!fits_int64_product(groups, rows) || !fits_int64_product(groups * rows, k / 2))
-        return NVFP4_GEMV_ERR_BAD_SHAPE;
-    if (!fits_int64_product(nvec, k / 2)) return NVFP4_GEMV_ERR_BAD_SHAPE;
-    return NVFP4_GEMV_OK;
-}
-
-// Workgroups of the fast kernel: (split, group, row block).  Defaults:
-//  * the small-N GEMM splits K (powers of two, at least one window per wave
-//    and split) while there are fewer 16-row tiles than compute units;
-//  * while the workgroups are few (under 8 per compute unit), the rows per
-//    workgroup shrink so that the count becomes a multiple of the 256 compute
-//    units of an MI355X: a workgroup's time is set by its rows, so equal rows
-//    on every unit beat full tiles on some and idle units elsewhere.
-int make_plan(int64_t groups, int64_t rows, int64_t nvec_per_group, int64_t k, bool aligned,
-              bool grouped, const nvfp4_mma_tuning_t *t, Plan *p, bool packed = false) {
-    nvfp4_mma_tuning_t tun = {NVFP4_GEMV_PATH_AUTO, 0, 0, 0};
-    if (t) tun = *t;
-    if (tun.path < NVFP4_GEMV_PATH_AUTO || tun.path > NVFP4_GEMV_PATH_GENERIC || tun.variant < 0 ||
-        tun.variant > kNumVariants || tun.ksplit < 0 || tun.rows_per_block < 0)
-        return NVFP4_GEMV_ERR_BAD_TUNING;
-    const bool fast_ok = aligned && k % 64 == 0 && k <= kMaxFastK;
-    if (tun.path == NVFP4_GEMV_PATH_FAST && !fast_ok) return NVFP4_GEMV_ERR_BAD_TUNING;
-    if (tun.path == NVFP4_GEMV_PATH_GENERIC &&
-        (tun.variant != 0 || tun.ksplit > 1 || tun.rows_per_block != 0))
-        return NVFP4_GEMV_ERR_BAD_TUNING;
-    if (grouped && tun.ksplit > 1) return NVFP4_GEMV_ERR_BAD_TUNING;
-    // Packed weights: matrix-core variants only, whole tiles per workgroup,
-    // K splits on window boundaries.
-    if (packed && (!fast_ok || tun.path == NVFP4_GEMV_PATH_GENERIC ||
-                   (tun.variant > 0 && kVariants[tun.variant - 1].form != kMatrixCores) ||
-                   tun.rows_per_block % kTile != 0))
-        return NVFP4_GEMV_ERR_BAD_TUNING;
-    const bool fast = tun.path != NVFP4_GEMV_PATH_GENERIC && fast_ok;
-    p->path = fast ? NVFP4_GEMV_PATH_FAST : NVFP4_GEMV_PATH_GENERIC;
-    if (!fast) {
-        // (with NVFP4_GEMV_PATH_AUTO, fast-kernel settings are ignored where the
-        // shape or alignment rules the fast kernel out; an explicit K split is not)
-        if (tun.ksplit > 1) return NVFP4_GEMV_ERR_BAD_TUNING;
-        p->variant = 0;
-        p->ksplit = 1;
-        p->kchunk = k;
-        p->rows_per_block = kGenericWaves;
-        p->threads = kGenericWaves * kWave;
-    } else {
-        if (tun.variant > 0) {
-            p->variant = tun.variant - 1;
-        } else if (grouped) {
-            // nvec_per_group: the tokens per expert on average, rounded up
-            p->variant = packed ? kDefaultGroupedPacked
-                                : nvec_per_group <= kFewTokensPerExpert ? kDefaultGroupedFew
-                                                                        : kDefaultGrouped;
-        } else if (packed) {
-            p->variant = kDefaultSmallNPacked;
-        } else {
-            const int64_t tiles = groups * ceil_div(rows, int64_t(kVariants[kDefaultSmallNFew].R));
-            p->variant = (nvec_per_group <= kFewVectors && tiles >= 4 * kComputeUnits)
-                             ? kDefaultSmallNFew
-                         : nvec_per_group <= kMidVectors ? kDefaultSmallNMid
-                                                         : kDefaultSmallN;
-        }
-        const Variant &v = kVariants[p->variant];
-        if (v.form == kValuTiles) {
-            // a workgroup per tile of v.R rows (or fewer on request), no K split
-            if (tun.rows_per_block > v.R || tun.ksplit > 1) return NVFP4_GEMV_ERR_BAD_TUNING;
-            p->ksplit = 1;
-            p->kchunk = k;
-            p->rows_per_block = tun.rows_per_block > 0 ? tun.rows_per_block : v.R;
-            p->threads = v.W * kWave;
-            p->row_blocks = ceil_div(rows, p->rows_per_block);
-            p->groups = groups * p->row_blocks;
-            if (p->groups >= (int64_t(1) << 31)) return NVFP4_GEMV_ERR_BAD_SHAPE;
-            p->ws_bytes = 0;
-            return NVFP4_GEMV_OK;
-        }
-        const int64_t tile_rows = int64_t(v.R) * kTile;
-        if (tun.rows_per_block > tile_rows) return NVFP4_GEMV_ERR_BAD_TUNING;
-        int64_t ks = 1;
-        if (tun.ksplit > 0) {
-            ks = tun.ksplit;
-        } else if (!grouped) {
-            const int64_t wg1 = groups * ceil_div(rows, int64_t(kTile));
-            const int64_t most = k / (int64_t(v.W) * kWinElems);
-            while (wg1 * ks < kComputeUnits && ks * 2 <= most) ks *= 2;
-        }
-        const int64_t granule = packed ? kWinElems : kLaneElems;
-        if (ks > ceil_div(k, granule)) return NVFP4_GEMV_ERR_BAD_TUNING;
-        const int64_t kchunk = ceil_div(ceil_div(k, ks), granule) * granule;
-        p->ksplit = ceil_div(k, kchunk);
-        p->kchunk = kchunk;
-        int64_t rpb = tile_rows;
-        if (tun.rows_per_block > 0) {
-            rpb = tun.rows_per_block;
-        } else if (!packed) {
-            const int64_t wg = groups * ceil_div(rows, tile_rows) * p->ksplit;
-            if (wg < 8 * kComputeUnits) {
-                const int64_t target = ceil_div(wg, kComputeUnits) * kComputeUnits;
-                const int64_t blocks = ceil_div(target, groups * p->ksplit);   // per group
-                rpb = ceil_div(rows, blocks);
-                if (rpb > tile_rows) rpb = tile_rows;
-            }
-        }
-        p->rows_per_block = rpb;
-        p->threads = v.W * kWave;
-    }
-    p->row_blocks = ceil_div(rows, p->rows_per_block);
-    p->groups = groups * p->row_blocks * p->ksplit;
-    if (p->groups >= (int64_t(1) << 31)) return NVFP4_GEMV_ERR_BAD_SHAPE;
-    p->ws_bytes = p->ksplit > 1
-                      ? static_cast<size_t>(p->ksplit) * groups * rows * nvec_per_group * sizeof(float)
-                      : 0;
-    return NVFP4_GEMV_OK;
 }
 
 bool overlaps(const void *p, size_t pn, const void *q, size_t qn) {
@@ -1327,11 +1138,8 @@ int validate_smalln(const uint8_t *A, const uint8_t *sfA, const uint8_t *B, cons
                     int32_t out_type, bool packed = false) {
     if (!A || !sfA || !B || !sfB || !c) return NVFP4_GEMV_ERR_NULL_POINTER;
     if (out_type != NVFP4_OUT_F16 && out_type != NVFP4_OUT_BF16) return NVFP4_GEMV_ERR_BAD_ARGUMENT;
-    int s = check_dims(l, m, n, k, false);
+    int s = check_smalln_shape(l, m, n, k);
     if (s != NVFP4_GEMV_OK) return s;
-    if (!fits_int64_product(l, n) || !fits_int64_product(l * n, k / 2) ||
-        !fits_int64_product(l * m, n) || l * m * n >= (int64_t(1) << 31))
-        return NVFP4_GEMV_ERR_BAD_SHAPE;
     if (reinterpret_cast<uintptr_t>(c) % 2 != 0 || reinterpret_cast<uintptr_t>(alpha) % 4 != 0)
         return NVFP4_GEMV_ERR_ALIGNMENT;
     int64_t ab = l * m * (k / 2), sb = l * m * (k / 16);
@@ -1354,10 +1162,8 @@ int validate_grouped(const uint8_t *X, const uint8_t *sfX, const uint8_t *W, con
                      bool packed = false) {
     if (!X || !sfX || !W || !sfW || !offsets || !c) return NVFP4_GEMV_ERR_NULL_POINTER;
     if (out_type != NVFP4_OUT_F16 && out_type != NVFP4_OUT_BF16) return NVFP4_GEMV_ERR_BAD_ARGUMENT;
-    int s = check_dims(experts, n, tokens, k, true);
+    int s = check_grouped_shape(tokens, experts, n, k);
     if (s != NVFP4_GEMV_OK) return s;
-    if (!fits_int64_product(tokens, n) || tokens * n >= (int64_t(1) << 31))
-        return NVFP4_GEMV_ERR_BAD_SHAPE;
     auto mis = [](const void *p, uintptr_t a) { return reinterpret_cast<uintptr_t>(p) % a != 0; };
     if (mis(c, 2) || mis(offsets, 4) || mis(gs_x, 4) || mis(gs_w, 4)) return NVFP4_GEMV_ERR_ALIGNMENT;
     int64_t wb = experts * n * (k / 2), swb = experts * n * (k / 16);
@@ -1423,7 +1229,7 @@ int nvfp4_gemm_smalln_plan(int64_t l, int64_t m, int64_t n, int64_t k, int align
                            const nvfp4_mma_tuning_t *in, nvfp4_mma_tuning_t *out,
                            size_t *workspace_bytes) {
     if (!out || !workspace_bytes) return NVFP4_GEMV_ERR_NULL_POINTER;
-    int s = check_dims(l, m, n, k, false);
+    int s = check_smalln_shape(l, m, n, k);
     if (s != NVFP4_GEMV_OK) return s;
     Plan p;
     s = make_plan(l, m, n, k, aligned != 0, false, in, &p);
@@ -1439,9 +1245,8 @@ int nvfp4_gemm_smalln_plan(int64_t l, int64_t m, int64_t n, int64_t k, int align
 int nvfp4_grouped_gemv_plan(int64_t experts, int64_t n, int64_t k, int64_t tokens, int aligned,
                             int packed, const nvfp4_mma_tuning_t *in, nvfp4_mma_tuning_t *out) {
     if (!out) return NVFP4_GEMV_ERR_NULL_POINTER;
-    int s = check_dims(experts, n, 0, k, true);
+    int s = check_grouped_shape(tokens, experts, n, k);
     if (s != NVFP4_GEMV_OK) return s;
-    if (tokens < 0) return NVFP4_GEMV_ERR_BAD_SHAPE;
     if (packed && (k % 64 != 0 || k > kMaxFastK)) return NVFP4_GEMV_ERR_BAD_SHAPE;
     Plan p;
     s = make_plan(experts, n, ceil_div(tokens, experts), k, packed != 0 || aligned != 0, true, in, &p,

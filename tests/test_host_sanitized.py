@@ -6,6 +6,10 @@
   launches) with g++ and runs it against a mock backend that fails the device
   query, the workspace allocation and the launch on purpose: the statuses are
   DEVICE, WORKSPACE and LAUNCH, and invalid calls never reach the backend.
+* ``tests/host/mma_plan_check.cpp`` compiles the small-N GEMM and grouped
+  GEMV plan (``precision_decode_amd/csrc/mma_plan.h``: shape rules, variants,
+  defaults, launch plan) and checks 200000 random shapes and tunings against
+  what the kernels assume, and the default rules.
 * ``tests/host/oracle_check.c`` compiles the oracle's C sums
   (``oracle/nvfp4_ref.c``) with gcc and runs them on exact-size buffers.
 """
@@ -38,6 +42,16 @@ def test_plan_and_orchestration_under_sanitizers(tmp_path):
            os.path.join(HOST, "plan_check.cpp"), "-o", exe]
     run = build_and_run(cmd, exe)
     assert run.returncode == 0 and "plan_check ok" in run.stdout, run.stdout + run.stderr
+
+
+@pytest.mark.skipif(shutil.which("g++") is None, reason="needs g++")
+def test_mma_plan_under_sanitizers(tmp_path):
+    exe = str(tmp_path / "mma_plan_check")
+    cmd = ["g++", "-std=c++17", *SAN, "-I", os.path.join(ROOT, "include"),
+           "-I", os.path.join(ROOT, "precision_decode_amd", "csrc"),
+           os.path.join(HOST, "mma_plan_check.cpp"), "-o", exe]
+    run = build_and_run(cmd, exe)
+    assert run.returncode == 0 and "mma_plan_check ok" in run.stdout, run.stdout + run.stderr
 
 
 @pytest.mark.skipif(shutil.which("gcc") is None, reason="needs gcc")
