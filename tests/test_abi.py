@@ -318,6 +318,10 @@ def test_smalln_plans(lib):
     assert t.path == pd.NVFP4_GEMV_PATH_GENERIC and t.ksplit == 1 and ws == 0
     t, _ = pd.nvfp4_gemm_smalln_plan(2, 100, 3, 64, aligned=False)
     assert t.path == pd.NVFP4_GEMV_PATH_GENERIC
+    # the launches' shape rules: outputs below 2^31 elements
+    with pytest.raises(pd.Nvfp4GemvError):
+        pd.nvfp4_gemm_smalln_plan(1, 1 << 16, 1 << 15, 64)
+    t, _ = pd.nvfp4_gemm_smalln_plan(1, 1 << 16, (1 << 15) - 1, 64)
     n = pd.nvfp4_mma_num_variants()
     forms = set()
     for v in range(1, n + 1):
@@ -461,7 +465,8 @@ def test_grouped_plan(lib):
                                                   pd.NVFP4_MMA_FORM_LDS_VECTOR_REGS)]
     t = pd.nvfp4_grouped_gemv_plan(4, 96, 128, 20, tuning={"variant": staged[-1], "rows_per_block": 20})
     assert t.variant == staged[-1] and t.rows_per_block == 20
-    for kw in ({"packed": True, "k": 96}, {"k": 0}, {"experts": 0}, {"tokens": -1}):
+    for kw in ({"packed": True, "k": 96}, {"k": 0}, {"experts": 0}, {"tokens": -1},
+               {"tokens": 1 << 21, "n": 1 << 10}):
         args = {"experts": 4, "n": 96, "k": 128, "tokens": 20}
         args.update(kw)
         packed = args.pop("packed", False)
