@@ -94,11 +94,11 @@ PROFILES = os.path.join(ROOT, "profiles")
 # (the GEMV's device code is gemv_kernels.h with its helpers in device_common.h)
 KERNEL_SOURCES = {"gemv": ("gemv_kernels.h", "device_common.h"),
                   "quantize_blocks": ("nvfp4_quantize.hip", "device_common.h"),
-                  "mma_stream": ("nvfp4_mma.hip", "device_common.h"),
-                  "mma_lds": ("nvfp4_mma.hip", "device_common.h"),
-                  "mma_generic": ("nvfp4_mma.hip", "device_common.h"),
-                  "vec_tile": ("nvfp4_mma.hip", "device_common.h"),
-                  "mma_stream_packed": ("nvfp4_mma.hip", "device_common.h")}
+                  "mma_stream": ("mma_kernels.h", "device_common.h"),
+                  "mma_lds": ("mma_kernels.h", "device_common.h"),
+                  "mma_generic": ("mma_kernels.h", "device_common.h"),
+                  "vec_tile": ("mma_kernels.h", "device_common.h"),
+                  "mma_stream_packed": ("mma_kernels.h", "device_common.h")}
 
 
 def parse_args(argv=None):
