@@ -25,8 +25,8 @@
 // cover 1 KiB contiguously, and hands every lane its block through LDS.  The
 // divisions round exactly as IEEE division does without its cost: x / g as
 // an fp64 product with 1/g (the quotient of a bf16 by an fp32 never lies
-// within 2^-49 of an fp32 rounding midpoint, the fp64 product is within
-// 2^-52), x_n / s as one reciprocal and one fused residual correction (the
+// within 2^-49 of an fp32 rounding midpoint, the fp64 product with a
+// reciprocal within one ulp is within 2^-51), x_n / s as one reciprocal and one fused residual correction (the
 // block scale has 4 significant bits, so quotients stay 2^-29 away from
 // midpoints); blocks outside the range this holds for take IEEE divisions.
 // The E2M1 rounding of every rule runs on gfx950's FP4 conversion.
@@ -71,11 +71,24 @@ __device__ __forceinline__ float e4m3_value_pos(uint32_t s) {
     return __uint_as_float((((s >> 3) + 120u) << 23) | ((s & 7u) << 20));
 }
 
-// RN32(a / b) from y = RN64(1/b) as RN32(RN64(a * y)): exact whenever a/b,
-// if not representable, lies more than 2^-51 (relative) from every fp32
-// rounding midpoint and is not a subnormal fp32 number.
+// RN32(a / b) from y within one fp64 ulp of 1/b as RN32(RN64(a * y)): the
+// fp64 product is within 2^-51 (relative) of a/b, so this is exact whenever
+// a/b, if not representable, lies farther than that from every fp32 rounding
+// midpoint and is not a subnormal fp32 number.
 __device__ __forceinline__ float quot_f64(float a, double y) {
     return static_cast<float>(static_cast<double>(a) * y);
+}
+
+// 1/d within one fp64 ulp for a normal d far from the exponent range's ends:
+// two Newton steps from the hardware reciprocal (relative error below 2^-22),
+// each step squaring the error; the fused residual 1 - d y is exact to well
+// under an ulp of itself, so the last step's rounding is the only one left.
+__device__ __forceinline__ double recip_f64(double d) {
+    double y = __builtin_amdgcn_rcp(d);
+    double e = __builtin_fma(-d, y, 1.0);
+    y = __builtin_fma(y, e, y);
+    e = __builtin_fma(-d, y, 1.0);
+    return __builtin_fma(y, e, y);
 }
 
 // RN32(a / b) for b with at most 4 significant bits, from y within 2^-22 of
@@ -175,7 +188,7 @@ __device__ __forceinline__ void quantize_one(u32x4 w0, u32x4 w1, float g, u32x2 
     float xn[16];
     float am;
     if (fast) {
-        const double yg = 1.0 / static_cast<double>(g);
+        const double yg = recip_f64(static_cast<double>(g));
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             xn[2 * i] = quot_f64(bf16_to_f32(w[i] & 0xFFFFu), yg);
@@ -235,9 +248,19 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_blocks(
     const int64_t b0 = static_cast<int64_t>(blockIdx.x) * kQuantThreads + wave * kWave;   // the wave's first block
     if (b0 >= nblocks) return;                     // wave-uniform
     const int nvalid = static_cast<int>(nblocks - b0 < kWave ? nblocks - b0 : kWave);
-    // block numbers stay below 2^31 (checked on the host): a 32-bit division
-    const int64_t bb = b < nblocks ? b : nblocks - 1;
-    const uint32_t row = static_cast<uint32_t>(bb) / static_cast<uint32_t>(bpr);
+    // The lane's row, for a scale per row: the wave's first row and offset in
+    // it once per wave (block numbers stay below 2^31, checked on the host),
+    // then, when a row holds a wave's 64 blocks or more, at most one row
+    // boundary inside the wave.  Lanes past the last block take the last row.
+    uint32_t row = 0;
+    if (gs_stride != 0) {
+        const uint32_t ub0 = static_cast<uint32_t>(b0), ubpr = static_cast<uint32_t>(bpr);
+        const uint32_t r0 = ub0 / ubpr;
+        const uint32_t off = ub0 - r0 * ubpr + static_cast<uint32_t>(lane);
+        row = r0 + (ubpr >= static_cast<uint32_t>(kWave) ? (off >= ubpr ? 1u : 0u) : off / ubpr);
+        const uint32_t last = static_cast<uint32_t>(rows - 1);
+        row = row < last ? row : last;
+    }
     // the wave's blocks (loads past the last block read zeros), then the
     // block's global scale, all in flight together
     const __amdgpu_buffer_rsrc_t xr = nvfp4dev::buffer_of(

@@ -72,7 +72,7 @@ def test_hand_derived_examples(ex):
 
 @pytest.mark.parametrize("rule", RULES)
 @pytest.mark.parametrize("rows,d", [(1, 16), (1, 16384), (3, 4144), (8, 7168), (64, 2048),
-                                    (1000, 48), (5, 16)])
+                                    (1000, 48), (5, 16), (9, 1008), (7, 1024), (11, 1040)])
 def test_gaussian_rows_per_row_scale(rule, rows, d):
     raw = workloads.gaussian_bf16(1, rows, d, seed=rows * 31 + d)["A"][0]
     amax = np.abs(raw).max(axis=1).astype(np.float32)
