@@ -421,7 +421,7 @@ __device__ __forceinline__ void lds_read_window(uint32_t aw0, uint32_t aw1, uint
 // scales; rows and vectors past the block's read zeros or stale LDS, which
 // only reach outputs that are never written (an MFMA output row or column
 // depends on its own row and vector alone, and e2m1 codes are finite).
-template <int R, int NS, int W, bool GROUPED, bool S16, bool VR = false>
+template <int R, int NS, int W, bool GROUPED, bool S16, bool VR = false, bool EARLY = false>
 __global__ void __launch_bounds__(W * kWave) mma_lds(const MmaArgs a) {
     static_assert(NS == 2 || NS == 4, "window slots must divide a scale group");
     static_assert(!VR || R == 2, "register-fed vectors: two row tiles");
@@ -579,12 +579,13 @@ __global__ void __launch_bounds__(W * kWave) mma_lds(const MmaArgs a) {
 #pragma unroll
         for (int r = 0; r < R; ++r) acc[r] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-        auto consume = [&](int j, auto slotc, int u) {
+        // Window j's operands, out of its slot (and register slot) into wq,
+        // vq, ws, vs: the slot can be refilled once this returns.
+        auto fetch = [&](int j, auto slotc, int u, u32x4 (&wq)[R][2], u32x4 (&vq)[2], uint32_t (&ws)[R],
+                         uint32_t &vs) {
             constexpr int slot = decltype(slotc)::value;
             const uint8_t *win = wring + slot * kWinSlot;
             const uint8_t *sc = sring + ((j / kGroupWins) & 1) * kScaleSlot;
-            u32x4 wq[R][2], vq[2];
-            uint32_t ws[R], vs;
             if constexpr (VR) {
                 lds_read_weights<R>(lds_address(win + rw0), lds_address(win + rw1), lds_address(sc + rs[u]),
                                     wq, ws);
@@ -601,6 +602,10 @@ __global__ void __launch_bounds__(W * kWave) mma_lds(const MmaArgs a) {
             vs &= keep;
 #pragma unroll
             for (int r = 0; r < R; ++r) ws[r] &= keep;
+        };
+        // The window's decode and products.
+        auto compute = [&](const u32x4 (&wq)[R][2], const u32x4 (&vq)[2], const uint32_t (&ws)[R],
+                           uint32_t vs) {
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
                 f16x8 vo[4];
@@ -622,17 +627,33 @@ __global__ void __launch_bounds__(W * kWave) mma_lds(const MmaArgs a) {
             }
         };
 
-        // One step at position u of group g: consume window j, refill its
-        // slot with window j + NS (spare windows past the run read nothing),
-        // wait until window j + 1 has landed.
+        // One step at position u of group g: take window j out of its slot,
+        // decode and multiply it, refill the slot with window j + NS (spare
+        // windows past the run read nothing), wait until window j + 1 has
+        // landed.  EARLY refills the slot as soon as the window's operands
+        // are in registers, so the refill flies while they are decoded and
+        // multiplied.  With two windows in flight and four waves that pays
+        // (on a 7168 x 16384 weight: 4 vectors in registers 15.5 -> 14.6 us,
+        // 16 vectors all in LDS 16.8 -> 15.5); with four windows in flight,
+        // eight waves, or several workgroups per compute unit it was slower.
         auto step = [&](int g, auto pos) {
             constexpr int u = decltype(pos)::value;
             const int j = g * kGroupWins + u;
-            if (j < niter) consume(j, std::integral_constant<int, u % NS>{}, u);   // wave-uniform
+            constexpr auto slot = std::integral_constant<int, u % NS>{};
+            constexpr auto starts = std::integral_constant<bool, (u + NS) % kGroupWins == 0>{};
+            u32x4 wq[R][2], vq[2];
+            uint32_t ws[R], vs;
+            if (j < niter) {   // wave-uniform
+                fetch(j, slot, u, wq, vq, ws, vs);
+                if constexpr (!EARLY) compute(wq, vq, ws, vs);
+            }
             phase_fence();
-            issue(std::integral_constant<bool, (u + NS) % kGroupWins == 0>{}, j + NS,
-                  std::integral_constant<int, u % NS>{});
+            issue(starts, j + NS, slot);
             phase_fence();
+            if constexpr (EARLY) {
+                if (j < niter) compute(wq, vq, ws, vs);
+                phase_fence();
+            }
             wait_vmcnt<loads_after_next<NS, kWinLoads + kVecLoads, kScaleLoads>(u)>();
             phase_fence();
         };

@@ -52,29 +52,32 @@ constexpr int kNumVariants = static_cast<int>(sizeof(kVariants) / sizeof(kVarian
 // operands).  Row-major weights, one 7168 x 16384 weight against n vectors:
 // the VALU tiles {4, 2, 4} for n <= 2 (12.9 and 13.8 us against 17.8 and 18.0
 // on the matrix cores, which pad the vectors to 16); the LDS-staged {2, 2, 4}
-// with the vectors in registers for 3 <= n <= 8 (15.0 / 15.0 / 15.2 / 15.6 us
-// at n = 3 / 4 / 6 / 8 against 15.6 / 15.6 / 15.7 / 15.8 for the all-LDS
-// {2, 4, 4}); the all-LDS {2, 4, 4} above 8 (16.0 and 16.3 us at 12 and 16
-// against 16.1-16.5 and 17.0-17.4 with the vectors in registers, whose 16
-// rows then cost more as register loads than as whole-line copies).  The
-// grouped GEMV (64 experts of 2048 x 7168, 128 tokens): the LDS-staged {2, 2,
+// with the vectors in registers for 3 <= n <= 13 (14.6 / 14.7 / 15.2 / 15.4
+// us at n = 4 / 8 / 12 / 13 against 15.3 / 15.3 / 15.4 / 15.4 for the all-LDS
+// {2, 2, 4} and 15.3 / 15.4 / 15.6 / 15.6 for the all-LDS {2, 4, 4}); the
+// all-LDS {2, 2, 4} above 13 (15.4 / 15.5 us at 14 / 16 against 15.6 / 16.1
+// with the vectors in registers, whose 16 rows then cost more as register
+// loads than as whole-line copies, and 15.7 / 15.8 for {2, 4, 4}).  Both
+// {2, 2, 4} forms refill a window's slot before its decode and products.
+// The grouped GEMV (64 experts of 2048 x 7168, 128 tokens): the LDS-staged {2, 2,
 // 2} with the vectors in registers while the experts average at most 4
 // tokens (78.1 us against 80.1 for the all-LDS {2, 2, 2}, 83-92 for {2, 2, 4}
 // and 109 for the register-fed {2, 1, 8}); its 26 KiB of LDS let six
 // workgroups share a compute unit.  Packed weights already load 1 KiB per
 // instruction: {2, 2, 4} and {2, 1, 8} on the matrix cores.  The VALU tiles
 // never split K, so they are the default only while their tiles fill the GPU.
-constexpr int kDefaultSmallN = 11;
+constexpr int kDefaultSmallN = 10;
 constexpr int kDefaultSmallNMid = 17;
 constexpr int kDefaultSmallNPacked = 2;
 constexpr int kDefaultSmallNFew = 6;
 constexpr int64_t kFewVectors = 2;
-constexpr int64_t kMidVectors = 8;
+constexpr int64_t kMidVectors = 13;
 constexpr int kDefaultGrouped = 15;
 constexpr int kDefaultGroupedFew = 18;
 constexpr int64_t kFewTokensPerExpert = 4;
 constexpr int kDefaultGroupedPacked = 3;
-static_assert(kVariants[kDefaultSmallN].form == kLdsStaged && kVariants[kDefaultSmallN].U == 4 &&
+static_assert(kVariants[kDefaultSmallN].form == kLdsStaged && kVariants[kDefaultSmallN].U == 2 &&
+                  kVariants[kDefaultSmallN].W == 4 &&
                   kVariants[kDefaultSmallNMid].form == kLdsVectorRegs &&
                   kVariants[kDefaultSmallNMid].W == 4 &&
                   kVariants[kDefaultGrouped].form == kLdsStaged && kVariants[kDefaultGrouped].W == 2 &&

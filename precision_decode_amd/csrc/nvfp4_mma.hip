@@ -82,14 +82,14 @@ MmaKernel fast_kernel(int v) {
     case 7: return P ? nullptr : vec_tile<8, 2, 4, G>;
     case 8: return P ? nullptr : vec_tile<4, 4, 4, G>;
     case 9: return P ? nullptr : vec_tile<8, 4, 4, G>;
-    case 10: return P ? nullptr : mma_lds<2, 2, 4, G, S16>;
+    case 10: return P ? nullptr : mma_lds<2, 2, 4, G, S16, false, true>;
     case 11: return P ? nullptr : mma_lds<2, 4, 4, G, S16>;
     case 12: return P ? nullptr : mma_lds<1, 2, 4, G, S16>;
     case 13: return P ? nullptr : mma_lds<2, 2, 6, G, S16>;
     case 14: return P ? nullptr : mma_lds<2, 2, 8, G, S16>;
     case 15: return P ? nullptr : mma_lds<2, 2, 2, G, S16>;
     case 16: return P ? nullptr : mma_lds<2, 4, 2, G, S16>;
-    case 17: return P ? nullptr : mma_lds<2, 2, 4, G, S16, true>;
+    case 17: return P ? nullptr : mma_lds<2, 2, 4, G, S16, true, true>;
     case 18: return P ? nullptr : mma_lds<2, 2, 2, G, S16, true>;
     default: return nullptr;
     }

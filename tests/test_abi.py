@@ -422,22 +422,23 @@ def test_default_plans_of_the_benchmark_workloads(lib, l, m, k, variant):
 
 def test_smalln_default_form_by_vector_count(lib):
     """One or two vectors against a weight that fills the GPU with 4-row tiles
-    go to the VALU tiles; 3 to 8 vectors (or one or two with too few tiles) to
-    the matrix cores with LDS-staged weights and the vectors in registers;
+    go to the VALU tiles; 3 to 13 vectors (or one or two with too few tiles)
+    to the matrix cores with LDS-staged weights and the vectors in registers;
     more vectors to the all-LDS form (row-major weights)."""
     for n in (1, 2):
         t, ws = pd.nvfp4_gemm_smalln_plan(1, 7168, n, 16384)
         assert pd.nvfp4_mma_variant_form(t.variant) == pd.NVFP4_MMA_FORM_VALU_TILES
         assert pd.nvfp4_mma_variant_info(t.variant) == (4, 2, 4)
         assert t.ksplit == 1 and ws == 0 and t.rows_per_block == 4
-    for l, m, n, k in ((1, 7168, 3, 16384), (1, 7168, 8, 16384), (1, 256, 2, 16384)):
+    for l, m, n, k in ((1, 7168, 3, 16384), (1, 7168, 8, 16384), (1, 7168, 13, 16384),
+                       (1, 256, 2, 16384)):
         t, _ = pd.nvfp4_gemm_smalln_plan(l, m, n, k)
         assert pd.nvfp4_mma_variant_form(t.variant) == pd.NVFP4_MMA_FORM_LDS_VECTOR_REGS, (l, m, n, k)
         assert pd.nvfp4_mma_variant_info(t.variant) == (2, 2, 4)
-    for l, m, n, k in ((1, 7168, 9, 16384), (1, 7168, 16, 16384)):
+    for l, m, n, k in ((1, 7168, 14, 16384), (1, 7168, 16, 16384)):
         t, _ = pd.nvfp4_gemm_smalln_plan(l, m, n, k)
         assert pd.nvfp4_mma_variant_form(t.variant) == pd.NVFP4_MMA_FORM_LDS_STAGED, (l, m, n, k)
-        assert pd.nvfp4_mma_variant_info(t.variant) == (2, 4, 4)
+        assert pd.nvfp4_mma_variant_info(t.variant) == (2, 2, 4)
 
 
 def test_grouped_plan(lib):
