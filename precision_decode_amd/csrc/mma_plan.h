@@ -45,13 +45,14 @@ constexpr Variant kVariants[] = {
     {8, 4, 4, kValuTiles},   {2, 2, 4, kLdsStaged},   {2, 4, 4, kLdsStaged},
     {1, 2, 4, kLdsStaged},   {2, 2, 6, kLdsStaged},   {2, 2, 8, kLdsStaged},
     {2, 2, 2, kLdsStaged},   {2, 4, 2, kLdsStaged},   {2, 2, 4, kLdsVectorRegs},
-    {2, 2, 2, kLdsVectorRegs},
+    {2, 2, 2, kLdsVectorRegs}, {4, 1, 4, kValuTiles},
 };
 constexpr int kNumVariants = static_cast<int>(sizeof(kVariants) / sizeof(kVariants[0]));
 // Defaults from MI355X sweeps of every variant (graph replays, rotated
 // operands).  Row-major weights, one 7168 x 16384 weight against n vectors:
-// the VALU tiles {4, 2, 4} for n <= 2 (12.9 and 13.8 us against 17.8 and 18.0
-// on the matrix cores, which pad the vectors to 16); the LDS-staged {2, 2, 4}
+// the VALU tiles {4, 1, 4} for n = 1 and {4, 2, 4} for n = 2 (11.8 and 14.0
+// us; 12.7 for {4, 2, 4} with one vector, 17.8 and 18.0 on the matrix cores,
+// which pad the vectors to 16); the LDS-staged {2, 2, 4}
 // with the vectors in registers for 3 <= n <= 13 (14.6 / 14.7 / 15.2 / 15.4
 // us at n = 4 / 8 / 12 / 13 against 15.3 / 15.3 / 15.4 / 15.4 for the all-LDS
 // {2, 2, 4} and 15.3 / 15.4 / 15.6 / 15.6 for the all-LDS {2, 4, 4}); the
@@ -70,6 +71,7 @@ constexpr int kDefaultSmallN = 10;
 constexpr int kDefaultSmallNMid = 17;
 constexpr int kDefaultSmallNPacked = 2;
 constexpr int kDefaultSmallNFew = 6;
+constexpr int kDefaultSmallNOne = 19;
 constexpr int64_t kFewVectors = 2;
 constexpr int64_t kMidVectors = 13;
 constexpr int kDefaultGrouped = 15;
@@ -85,7 +87,8 @@ static_assert(kVariants[kDefaultSmallN].form == kLdsStaged && kVariants[kDefault
                   kVariants[kDefaultGroupedFew].W == 2 &&
                   kVariants[kDefaultSmallNPacked].form == kMatrixCores &&
                   kVariants[kDefaultGroupedPacked].form == kMatrixCores &&
-                  kVariants[kDefaultSmallNFew].form == kValuTiles,
+                  kVariants[kDefaultSmallNFew].form == kValuTiles &&
+                  kVariants[kDefaultSmallNOne].form == kValuTiles && kVariants[kDefaultSmallNOne].U == 1,
               "the defaults name the variants measured above");
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -182,7 +185,7 @@ inline int make_plan(int64_t groups, int64_t rows, int64_t nvec_per_group, int64
         } else {
             const int64_t tiles = groups * ceil_div(rows, int64_t(kVariants[kDefaultSmallNFew].R));
             p->variant = (nvec_per_group <= kFewVectors && tiles >= 4 * kComputeUnits)
-                             ? kDefaultSmallNFew
+                             ? (nvec_per_group == 1 ? kDefaultSmallNOne : kDefaultSmallNFew)
                          : nvec_per_group <= kMidVectors ? kDefaultSmallNMid
                                                          : kDefaultSmallN;
         }

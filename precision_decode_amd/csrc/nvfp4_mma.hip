@@ -91,6 +91,7 @@ MmaKernel fast_kernel(int v) {
     case 16: return P ? nullptr : mma_lds<2, 4, 2, G, S16>;
     case 17: return P ? nullptr : mma_lds<2, 2, 4, G, S16, true, true>;
     case 18: return P ? nullptr : mma_lds<2, 2, 2, G, S16, true>;
+    case 19: return P ? nullptr : vec_tile<4, 1, 4, G>;
     default: return nullptr;
     }
 }

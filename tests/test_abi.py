@@ -336,7 +336,7 @@ def test_smalln_plans(lib):
         else:
             # VALU row tiles: r rows per workgroup, u vectors per pass, never a K split
             assert form == pd.NVFP4_MMA_FORM_VALU_TILES
-            assert r in (4, 8) and u in (2, 4) and 1 <= w <= 16
+            assert r in (4, 8) and u in (1, 2, 4) and 1 <= w <= 16
             t, ws = pd.nvfp4_gemm_smalln_plan(3, 100, 5, 4096, tuning={"variant": v})
             assert t.variant == v and t.ksplit == 1 and ws == 0 and t.rows_per_block == r
             t, _ = pd.nvfp4_gemm_smalln_plan(3, 100, 5, 4096, tuning={"variant": v, "rows_per_block": 3})
@@ -428,7 +428,7 @@ def test_smalln_default_form_by_vector_count(lib):
     for n in (1, 2):
         t, ws = pd.nvfp4_gemm_smalln_plan(1, 7168, n, 16384)
         assert pd.nvfp4_mma_variant_form(t.variant) == pd.NVFP4_MMA_FORM_VALU_TILES
-        assert pd.nvfp4_mma_variant_info(t.variant) == (4, 2, 4)
+        assert pd.nvfp4_mma_variant_info(t.variant) == (4, n, 4)   # one vector slot per vector
         assert t.ksplit == 1 and ws == 0 and t.rows_per_block == 4
     for l, m, n, k in ((1, 7168, 3, 16384), (1, 7168, 8, 16384), (1, 7168, 13, 16384),
                        (1, 256, 2, 16384)):

@@ -79,7 +79,7 @@ def test_smalln_default_plan_shapes(l, m, n, k):
     assert_bits_equal(run_smalln(ops, l, m, n, k), oracle_smalln(ops, l, m, n, k), f"{(l, m, n, k)}")
 
 
-NUM_MMA_VARIANTS = 19
+NUM_MMA_VARIANTS = 20
 
 
 def valu_tiles(v):
