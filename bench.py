@@ -223,7 +223,7 @@ class Timer:
             try:
                 sleep(PREROLL_CYCLES)
             except RuntimeError:
-                self.torch.cuda._sleep = None     # not available on this build: no delay
+                self.torch.cuda._sleep = None     # not available in this torch: no delay
 
     def __call__(self, n, fn):
         torch = self.torch
@@ -941,8 +941,8 @@ def main(argv=None) -> int:
     args = parse_args(argv)
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU only: the NVFP4 GEMV runs on a single MI355X and this "
-              "build has no multi-GPU path (the design notes describe sharding along M). "
+        print("bench.py measures one GPU only: the NVFP4 GEMV runs on a single MI355X and the "
+              "library has no multi-GPU path (the design notes describe sharding along M). "
               "Run with --gpus 1.", file=sys.stderr)
         return 2
 

@@ -9,7 +9,7 @@ GPU library and its Python binding never do, and they share no code with it.
 * ``quantize``   - the BF16 -> NVFP4 quantisers: with a global scale from the
   tensor's amax (the Gaussian workload's bytes, the weight quantiser) or given
   by the caller (the graph-safe activation quantiser), under the three E2M1
-  rounding rules the pages use or this build reads; and the GEMV fed by a
+  rounding rules the pages use or the library's readings of them; and the GEMV fed by a
   quantised activation;
 * ``build``      - compiles ``nvfp4_ref.c`` with gcc.
 
