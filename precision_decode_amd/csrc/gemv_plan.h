@@ -73,7 +73,7 @@ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // one 1 KiB slice of 4 rows, all of it in flight at once, and a workgroup
 // reads 16-32 KiB of A, the shape in which a plain read of such a weight is
 // fastest (11.84 us against 12.23 for the staged {2, 4, 7} in an alternating
-// A/B on one box), as long as those tiles alone fill the GPU (at least 4
+// A/B on one MI355X), as long as those tiles alone fill the GPU (at least 4
 // per compute unit; a tile's 8 waves cannot split K any further).  Longer
 // rows, and fewer rows, keep the staged {2, 4, 7}, which keeps every wave's
 // rows in flight over any number of iterations and splits K across

@@ -1,6 +1,6 @@
 // Read probes of the NVFP4 GEMV library (gfx950): plain streaming reads, no
 // arithmetic, whose run times are the read ceilings the GEMV is measured
-// against on the same box in the same run.  Device code only; the entry
+// against on the same GPU in the same run.  Device code only; the entry
 // points are nvfp4_hbm_read_probe and nvfp4_hbm_read_probe_rows in
 // nvfp4_gemv.hip, this header's only includer.
 #ifndef NVFP4_PROBE_KERNELS_H
