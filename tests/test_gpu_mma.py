@@ -70,6 +70,9 @@ def test_smalln_configs_bit_exact(name, out_type):
 SMALLN_SHAPES = [
     (1, 1, 1, 32), (2, 80, 3, 256), (1, 17, 16, 2080), (3, 33, 5, 4096), (1, 100, 17, 1024),
     (2, 48, 2, 160), (1, 7, 40, 512), (1, 300, 16, 16384), (2, 31, 9, 320), (1, 64, 4, 64),
+    # the defaults by vector count on weights that fill the GPU: one-vector VALU tiles,
+    # vectors in registers up to 13, all in LDS from 14
+    (1, 7168, 1, 16384), (2, 4100, 1, 2048), (1, 4096, 13, 2048), (1, 4096, 14, 2048),
 ]
 
 
