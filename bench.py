@@ -93,7 +93,7 @@ PROFILES = os.path.join(ROOT, "profiles")
 # counter summaries under profiles/ are valid only for the source they were taken on
 # (the GEMV's device code is gemv_kernels.h with its helpers in device_common.h)
 KERNEL_SOURCES = {"gemv": ("gemv_kernels.h", "device_common.h"),
-                  "quantize_blocks": ("nvfp4_quantize.hip", "device_common.h"),
+                  "quantize_blocks": ("nvfp4_quantize.hip", "quant_arith.h", "device_common.h"),
                   "mma_stream": ("mma_kernels.h", "device_common.h"),
                   "mma_lds": ("mma_kernels.h", "device_common.h"),
                   "mma_generic": ("mma_kernels.h", "device_common.h"),
