@@ -199,10 +199,14 @@ class SmallNConfig:
 
 SMALLN_CONFIGS = {
     "tiny_n3": SmallNConfig("tiny_n3", 2, 80, 3, 256, note="tiny, ragged rows"),
+    "decode_n1": SmallNConfig("decode_n1", 1, 7168, 1, 16384,
+                              note="the decode weight against 1 vector (the GEMV through the GEMM call)"),
     "decode_n2": SmallNConfig("decode_n2", 1, 7168, 2, 16384,
                               note="the decode weight against 2 vectors (one speculative token)"),
     "decode_n4": SmallNConfig("decode_n4", 1, 7168, 4, 16384,
                               note="the decode weight against 4 vectors (speculative tokens)"),
+    "decode_n8": SmallNConfig("decode_n8", 1, 7168, 8, 16384,
+                              note="the decode weight against 8 vectors"),
     "decode_n16": SmallNConfig("decode_n16", 1, 7168, 16, 16384,
                                note="the decode weight against 16 vectors (a decode batch)"),
 }
